@@ -1,0 +1,214 @@
+"""Throughput of the tiled GEMM on one MI355X; prints one JSON line.
+
+A step is one GEMM over the 8192 x 8192 x 8192 bf16 workload (row-major A
+and B drawn from N(0,1)/sqrt(K), fp32 accumulation, bf16 output) with the
+inputs already resident in device memory.  The timed region is exactly
+`--steps` back-to-back calls through the C ABI, bracketed by
+torch.cuda.synchronize(); each call is also bracketed by HIP events on the
+launch stream, whose mean is the kernel time used for the roofline.
+
+Beside the main figure the line carries:
+  roofline      the GEMM kernel against the dense bf16 MFMA peak;
+  cpu_baseline  the CPU oracle timed on this host on a bounded sample of the
+                same workload (whole output rows), scaled to TFLOP/s;
+  also          the same measurement for the 1024x1024x2048 fp16 GEMM, its
+                fused bias+ReLU form and the grouped MoE GEMM.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--no-also]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GEMM TFLOP/s and % of MI355X fp16 MFMA peak (1024x1024x2048 and 8192^3)"
+PEAK_MFMA_TFLOPS = 2516.6   # dense fp16/bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_HBM_GBS = 8000.0       # HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gemm_8192_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-also", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the CPU-baseline sample")
+    return ap.parse_args()
+
+
+def upload(bits, dt):
+    import numpy as np
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda()
+    return t.view(torch.float16 if dt == 0 else torch.bfloat16)
+
+
+def time_calls(fn, steps: int, warmup: int):
+    """Warm up, then time exactly `steps` calls: wall clock over the whole
+    region (synchronised on both sides) and HIP events around each call."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record()
+        fn()
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    return wall, sum(per) / len(per), per[len(per) // 2]
+
+
+def dense_setup(name, variant="float"):
+    import torch
+
+    import tiled_matrix_multiplication_gemm_amd as mg
+    from tiled_matrix_multiplication_gemm_amd import inputs
+
+    c = inputs.dense_workload(name, variant)
+    A, B = upload(c.A, c.dtype), upload(c.B, c.dtype)
+    C = torch.empty((c.M, c.N), dtype=A.dtype, device="cuda")
+    if c.bias is not None:
+        bias = upload(c.bias, c.dtype)
+        fn = lambda: mg.mg_gemm_bias_relu(A, B, bias, out=C)
+    else:
+        fn = lambda: mg.mg_gemm(A, B, out=C)
+    return c, fn
+
+
+def measure_dense(name, steps, warmup):
+    import tiled_matrix_multiplication_gemm_amd as mg
+
+    c, fn = dense_setup(name)
+    wall, mean_ms, med_ms = time_calls(fn, steps, warmup)
+    flops = 2.0 * c.M * c.N * c.K
+    cfg = mg.mg_config_info(mg.mg_last_config())["name"]
+    hbm_bytes = 2.0 * (c.M * c.K + c.K * c.N + c.M * c.N) + (2.0 * c.N if c.bias is not None else 0.0)
+    return dict(case=c, flops=flops, wall=wall, kernel_ms=mean_ms, kernel_ms_median=med_ms, tile_config=cfg,
+                compulsory_bytes=hbm_bytes)
+
+
+def measure_grouped(name, steps, warmup):
+    import numpy as np
+    import torch
+
+    import tiled_matrix_multiplication_gemm_amd as mg
+    from tiled_matrix_multiplication_gemm_amd import inputs
+
+    c = inputs.grouped_workload(name, "float")
+    X, W = upload(c.X, c.dtype), upload(c.W, c.dtype)
+    off = torch.from_numpy(c.offsets.astype(np.int32)).cuda()
+    Y = torch.empty((c.T, c.N), dtype=X.dtype, device="cuda")
+    fn = lambda: mg.mg_grouped_gemm(X, W, off, out=Y)
+    wall, mean_ms, med_ms = time_calls(fn, steps, warmup)
+    flops = 2.0 * c.T * c.K * c.N
+    hbm_bytes = 2.0 * (c.T * c.K + c.E * c.K * c.N + c.T * c.N) + 4.0 * (c.E + 1)
+    cfg = mg.mg_config_info(mg.mg_last_config())["name"]
+    return dict(case=c, flops=flops, wall=wall, kernel_ms=mean_ms, kernel_ms_median=med_ms, tile_config=cfg,
+                compulsory_bytes=hbm_bytes)
+
+
+def cpu_baseline(case, target_s: float):
+    """The oracle, as it is, on whole output rows of the same workload."""
+    import numpy as np
+
+    import oracle
+
+    threads = min(16, oracle.default_threads())
+    rows = 8
+    while True:
+        t0 = time.perf_counter()
+        oracle.gemm(case.A[:rows], case.B, case.dtype, bias=case.bias, relu=case.relu, nthreads=threads)
+        dt = time.perf_counter() - t0
+        if dt >= target_s or rows >= case.M:
+            break
+        # grow the sample towards the target length
+        rows = int(min(case.M, max(rows * 2, rows * target_s / max(dt, 1e-3) * 0.9)))
+    flops = 2.0 * rows * case.N * case.K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d output rows (%dx%dx%d), %.1f s, fp64 accumulation" % (rows, case.M, rows, case.N,
+                                                                                       case.K, dt)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import tiled_matrix_multiplication_gemm_amd as mg
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    mg.lib()
+
+    main_res = measure_dense(args.workload, args.steps, args.warmup)
+    c = main_res["case"]
+    value = main_res["flops"] * args.steps / main_res["wall"] / 1e12
+    achieved = main_res["flops"] / (main_res["kernel_ms"] * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_res["wall"] / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if c.dtype == 1 else "f16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "M": c.M, "N": c.N, "K": c.K,
+                   "layout": "row-major A[M,K], B[K,N]", "accumulate": "fp32",
+                   "tile_config": main_res["tile_config"]},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_MFMA_TFLOPS, 4), "traffic": None,
+                     "kernel_ms_mean": round(main_res["kernel_ms"], 4),
+                     "kernel_ms_median": round(main_res["kernel_ms_median"], 4),
+                     "kernel": "gemm_tile_kernel (%s)" % main_res["tile_config"]},
+    }
+    sys.stdout.flush()
+    if not args.no_also:
+        also = {}
+        for name in ("gemm_1024x1024x2048_f16", "gemm_bias_relu_1024x1024x2048_f16"):
+            r = measure_dense(name, max(args.steps, 50), max(args.warmup, 10))
+            ach = r["flops"] / (r["kernel_ms"] * 1e-3) / 1e12
+            also[name] = {"tflops": round(r["flops"] * max(args.steps, 50) / r["wall"] / 1e12, 2),
+                          "kernel_tflops": round(ach, 2), "frac_mfma_peak": round(ach / PEAK_MFMA_TFLOPS, 4),
+                          "kernel_ms_mean": round(r["kernel_ms"], 5), "tile_config": r["tile_config"]}
+        gname = "grouped_moe_e32_t8192_k1024_n4096_f16"
+        r = measure_grouped(gname, args.steps, args.warmup)
+        ach = r["flops"] / (r["kernel_ms"] * 1e-3) / 1e12
+        gbs = r["compulsory_bytes"] / (r["kernel_ms"] * 1e-3) / 1e9
+        also[gname] = {"tflops": round(r["flops"] * args.steps / r["wall"] / 1e12, 2),
+                       "kernel_tflops": round(ach, 2), "frac_mfma_peak": round(ach / PEAK_MFMA_TFLOPS, 4),
+                       "hbm_gbs_compulsory": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                       "kernel_ms_mean": round(r["kernel_ms"], 5), "tile_config": r["tile_config"]}
+        line["also"] = also
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(c, args.cpu_seconds)
+    print(json.dumps(line))
+    sys.stdout.flush()
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,162 @@
+/*
+ * mi355gemm -- tiled dense GEMM for one AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libmi355gemm.so.  Every entry point takes plain device pointers,
+ * sizes in elements and a HIP stream; it validates its arguments on the host
+ * (before any HIP call), enqueues its kernels on `stream` and returns without
+ * synchronising.  The library allocates no memory and keeps no state besides
+ * a read-only configuration table and the process-wide override set by
+ * mg_set_config().
+ *
+ * Common rules
+ *  - Element types: fp16 or bf16 in, the same type out.  Products are exact
+ *    and are accumulated in fp32 ("Triton study notes", section 2.1: always
+ *    accumulate in fp32); the fp32 result is rounded once, to nearest even,
+ *    to the output type.
+ *  - Layout: row-major matrices with a unit inner stride.  Leading strides
+ *    are in elements, must be >= the row length and a multiple of 8 (so
+ *    every row starts on a 16-byte boundary); base pointers must be 16-byte
+ *    aligned.  Transposed operands (inner stride != 1) are rejected.
+ *  - Ownership: the caller owns every buffer.  Outputs must not overlap
+ *    inputs.  Buffers must stay valid until the enqueued work has finished.
+ *  - Errors: a non-MG_OK status means nothing was enqueued, except
+ *    MG_ERR_HIP, which reports a failed launch (hipGetLastError).
+ *  - Sizes: M == 0 or N == 0 is a no-op returning MG_OK; K == 0 yields the
+ *    empty sum (zeros, or ReLU(bias) for the fused epilogue).
+ *  - Concurrency: calls are independent and may be issued from several host
+ *    threads; mg_set_config() is process-wide and meant for benchmarking.
+ */
+#ifndef MI355GEMM_H
+#define MI355GEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MG_OK = 0,
+    MG_ERR_INVALID_ARG = 1,        /* null pointer with a nonzero extent, negative size, bad count */
+    MG_ERR_UNSUPPORTED_DTYPE = 2,  /* dtype not fp16/bf16, or input and output types differ        */
+    MG_ERR_UNSUPPORTED_LAYOUT = 3, /* inner stride != 1, or leading stride shorter than a row       */
+    MG_ERR_MISALIGNED = 4,         /* base pointer not 16-byte aligned or leading stride % 8 != 0   */
+    MG_ERR_HIP = 5,                /* the HIP runtime reported an error when launching               */
+    MG_ERR_BAD_CONFIG = 6          /* unknown configuration id, or a BK the configuration cannot use */
+} mg_status;
+
+typedef enum { MG_F16 = 0, MG_BF16 = 1 } mg_dtype;
+
+/* Human-readable name of a status code (static storage). */
+const char* mg_status_string(mg_status status);
+
+/*
+ * C[M,N] = A[M,K] * B[K,N].
+ *
+ * The tiled product of the pages' minimal kernel ("Using Triton to optimise
+ * GEMM across chips", section 2.1; Gluon matmul example): the output is cut
+ * into BM x BN tiles, each tile accumulates BK-wide slices of A and B.
+ * A: M x K, row stride stride_am, inner stride stride_ak (must be 1).
+ * B: K x N, row stride stride_bk, inner stride stride_bn (must be 1).
+ * C: M x N, row stride stride_cm, inner stride stride_cn (must be 1).
+ */
+mg_status mg_gemm(const void* A, const void* B, void* C,
+                  int64_t M, int64_t N, int64_t K,
+                  int64_t stride_am, int64_t stride_ak,
+                  int64_t stride_bk, int64_t stride_bn,
+                  int64_t stride_cm, int64_t stride_cn,
+                  mg_dtype in_dtype, mg_dtype out_dtype, hipStream_t stream);
+
+/*
+ * C[M,N] = ReLU(A[M,K] * B[K,N] + bias[N]) in one kernel.
+ *
+ * The fused epilogue of "Using Triton to optimise GEMM across chips",
+ * section 3.4: bias and activation are applied to the fp32 accumulator in
+ * registers before the single rounding, so the product never makes an extra
+ * trip through memory.  bias: N contiguous elements of out_dtype.  ReLU of a
+ * non-positive value is +0.0.  Other arguments as mg_gemm.
+ */
+mg_status mg_gemm_bias_relu(const void* A, const void* B, const void* bias, void* C,
+                            int64_t M, int64_t N, int64_t K,
+                            int64_t stride_am, int64_t stride_ak,
+                            int64_t stride_bk, int64_t stride_bn,
+                            int64_t stride_cm, int64_t stride_cn,
+                            mg_dtype in_dtype, mg_dtype out_dtype, hipStream_t stream);
+
+/*
+ * Grouped GEMM for the expert layer of a mixture-of-experts model, in one
+ * launch: for every expert e,
+ *     Y[o_e : o_{e+1}, :] = X[o_e : o_{e+1}, :] * W[e]
+ * with o = expert_offsets (the yfxerp page, section 2.3, on the dozens of
+ * GEMMs one MoE layer chains).
+ * X: T x K token rows sorted by expert, row stride stride_xm.
+ * W: E matrices K x N; W[e] starts stride_we elements after W[e-1]; row
+ *    stride stride_wk.  stride_we must be a multiple of 8.
+ * Y: T x N, row stride stride_ym.
+ * expert_offsets: DEVICE array of E+1 int32 with o_0 = 0, o_E = T and
+ *    o_e <= o_{e+1}.  It is read by the kernel and is NOT validated (a
+ *    violation is undefined behaviour).  Experts with no rows write nothing.
+ * dtype is both the input and the output type.
+ */
+mg_status mg_grouped_gemm(const void* X, const void* W, void* Y, const int32_t* expert_offsets,
+                          int64_t E, int64_t T, int64_t N, int64_t K,
+                          int64_t stride_xm, int64_t stride_we, int64_t stride_wk, int64_t stride_ym,
+                          mg_dtype dtype, hipStream_t stream);
+
+/*
+ * Blocked re-layout of A ("layout planner", "Using Triton to optimise GEMM
+ * across chips", section 3.2): A[M,K] -> Ap[ceil(K/BK), M, BK], i.e. element
+ * (m, k) moves to ((k / BK) * M + m) * BK + k % BK, and the last K block is
+ * zero-padded.  Each BM x BK tile of A then is one contiguous run.
+ * Ap must hold mg_prepacked_bytes(M, K, BK, dtype) bytes, 16-byte aligned.
+ * BK must be a BK of some configuration (see mg_config_bk).
+ */
+size_t mg_prepacked_bytes(int64_t M, int64_t K, int64_t BK, mg_dtype dtype);
+mg_status mg_prepack_a(const void* A, void* Ap, int64_t M, int64_t K, int64_t stride_am, int64_t BK,
+                       mg_dtype dtype, hipStream_t stream);
+
+/* The BK that mg_gemm_prepacked will use for this problem (the selected
+ * configuration's K step); pack A with exactly this BK. */
+int64_t mg_config_bk(int64_t M, int64_t N, int64_t K, mg_dtype dtype);
+
+/* C = A * B with A given in the blocked layout produced by mg_prepack_a with
+ * the same BK.  Returns MG_ERR_BAD_CONFIG if BK differs from the selected
+ * configuration's.  B and C as in mg_gemm. */
+mg_status mg_gemm_prepacked(const void* Ap, int64_t BK, const void* B, void* C,
+                            int64_t M, int64_t N, int64_t K,
+                            int64_t stride_bk, int64_t stride_bn,
+                            int64_t stride_cm, int64_t stride_cn,
+                            mg_dtype dtype, hipStream_t stream);
+
+/* ---- configuration table (offline-tuned; read-only) ---------------------- */
+
+typedef struct {
+    int id;
+    int bm, bn, bk;           /* output tile and K step                    */
+    int waves_m, waves_n;     /* wavefront grid of one workgroup           */
+    int stages;               /* LDS buffers in the K pipeline             */
+    int mfma_m, mfma_n, mfma_k;
+    int group_m;              /* tile rows visited together (L2 reuse)     */
+    int xcd_remap;            /* 1: consecutive tiles stay on one XCD      */
+    int lds_bytes;            /* shared memory of one workgroup            */
+    const char* name;
+} mg_config_desc;
+
+int mg_num_configs(void);
+mg_status mg_config_info(int id, mg_config_desc* out);
+/* Force configuration `id` for every following call in this process (-1
+ * restores the table's choice).  For benchmarking and tuning sweeps. */
+mg_status mg_set_config(int id);
+/* Configuration id used by the most recent successful call in this process. */
+int mg_last_config(void);
+/* Configuration the table selects for a dense problem of this shape. */
+int mg_select_config(int64_t M, int64_t N, int64_t K, mg_dtype dtype, int grouped);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MI355GEMM_H */

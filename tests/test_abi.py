@@ -1,0 +1,145 @@
+"""C-ABI contract checks that need no GPU: the library loads, exports every
+function include/mi355gemm.h declares, and rejects bad arguments with the
+documented status codes before making any HIP call.  No kernel is launched
+here: every call either fails validation or is a documented no-op."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import tiled_matrix_multiplication_gemm_amd as mg
+from oracle import layout
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mi355gemm.h")
+
+OK, INVALID, DTYPE, LAYOUT, MISALIGNED, HIP, BADCFG = range(7)
+F16, BF16 = 0, 1
+P = 0x10000      # a 16-byte aligned stand-in address; never dereferenced below
+S = ctypes.c_void_p(0)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mg_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(mg.LIB_PATH):
+        pytest.skip("library not built")
+    return mg.lib()
+
+
+def test_header_and_exports_agree(L):
+    names = declared_functions()
+    assert set(names) == set(mg.EXPORTED)
+    out = subprocess.run(["nm", "-D", "--defined-only", mg.LIB_PATH], capture_output=True, text=True, check=True)
+    exported = set(re.findall(r"\bT (mg_[a-z_]+)\b", out.stdout))
+    for n in names:
+        assert n in exported, n
+        assert hasattr(L, n)
+
+
+def gemm(L, A=P, B=P, C=P, M=64, N=64, K=64, sam=64, sak=1, sbk=64, sbn=1, scm=64, scn=1, din=F16, dout=F16):
+    return L.mg_gemm(A, B, C, M, N, K, sam, sak, sbk, sbn, scm, scn, din, dout, S)
+
+
+def test_status_strings(L):
+    for s in range(7):
+        assert L.mg_status_string(s).decode().startswith("MG_")
+    assert b"unknown" in L.mg_status_string(99)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(A=None), INVALID), (dict(B=None), INVALID), (dict(C=None), INVALID),
+    (dict(M=-1), INVALID), (dict(N=-5), INVALID), (dict(K=-1), INVALID),
+    (dict(din=2, dout=2), DTYPE), (dict(din=F16, dout=BF16), DTYPE), (dict(din=7, dout=F16), DTYPE),
+    (dict(sak=2), LAYOUT), (dict(sbn=64), LAYOUT), (dict(scn=0), LAYOUT),
+    (dict(sam=32), LAYOUT), (dict(sbk=8), LAYOUT),
+    (dict(A=P + 2), MISALIGNED), (dict(B=P + 8), MISALIGNED), (dict(C=P + 4), MISALIGNED),
+    (dict(sam=68), MISALIGNED), (dict(scm=100), MISALIGNED),
+])
+def test_gemm_rejects_bad_arguments(L, kw, status):
+    assert gemm(L, **kw) == status
+
+
+def test_zero_sized_problems_are_noops(L):
+    # M == 0 or N == 0: nothing to compute, null pointers are fine
+    assert gemm(L, A=None, C=None, M=0) == OK
+    assert gemm(L, B=None, C=None, N=0) == OK
+    assert gemm(L, A=None, B=None, C=None, M=0, N=0, K=0) == OK
+
+
+def test_bias_relu_requires_bias(L):
+    assert L.mg_gemm_bias_relu(P, P, None, P, 8, 8, 8, 8, 1, 8, 1, 8, 1, F16, F16, S) == INVALID
+    assert L.mg_gemm_bias_relu(P, P, None, P, 0, 8, 8, 8, 1, 8, 1, 8, 1, F16, F16, S) == OK
+
+
+def grouped(L, X=P, W=P, Y=P, off=P, E=4, T=64, N=64, K=64, sxm=64, swe=64 * 64, swk=64, sym=64, dt=F16):
+    return L.mg_grouped_gemm(X, W, Y, off, E, T, N, K, sxm, swe, swk, sym, dt, S)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(E=-1), INVALID), (dict(T=-1), INVALID), (dict(off=None), INVALID), (dict(X=None), INVALID),
+    (dict(W=None), INVALID), (dict(Y=None), INVALID), (dict(E=0), INVALID), (dict(dt=5), DTYPE),
+    (dict(swe=64 * 63), LAYOUT), (dict(swe=64 * 64 + 4), MISALIGNED), (dict(sxm=60), LAYOUT),
+    (dict(sym=72 + 1), MISALIGNED), (dict(X=P + 2), MISALIGNED),
+])
+def test_grouped_rejects_bad_arguments(L, kw, status):
+    assert grouped(L, **kw) == status
+
+
+def test_grouped_empty_is_noop(L):
+    assert grouped(L, T=0, X=None, Y=None, off=None) == OK
+    assert grouped(L, E=0, T=0, X=None, W=None, Y=None, off=None) == OK
+
+
+def test_prepack_arguments(L):
+    assert L.mg_prepack_a(P, P, 64, 64, 64, 48, F16, S) == BADCFG
+    assert L.mg_prepack_a(P, None, 64, 64, 64, 64, F16, S) == INVALID
+    assert L.mg_prepack_a(P, P + 8, 64, 64, 64, 64, F16, S) == MISALIGNED
+    assert L.mg_prepack_a(None, None, 0, 64, 64, 64, F16, S) == OK
+    assert L.mg_prepacked_bytes(100, 130, 64, F16) == 3 * 100 * 64 * 2
+    assert L.mg_prepacked_bytes(0, 130, 64, F16) == 0
+    bk = L.mg_config_bk(8192, 8192, 8192, BF16)
+    assert bk in (32, 64)
+    # a BK the selected configuration does not use is refused
+    assert L.mg_gemm_prepacked(P, 16, P, P, 64, 64, 64, 64, 1, 64, 1, F16, S) == BADCFG
+
+
+def test_config_table(L):
+    n = L.mg_num_configs()
+    assert n >= 1
+    for i in range(n):
+        d = mg.mg_config_info(i)
+        assert d["id"] == i
+        assert d["bm"] % (32 * d["waves_m"]) == 0 and d["bn"] % (32 * d["waves_n"]) == 0
+        assert d["bk"] in (32, 64) and d["stages"] >= 2
+        # LDS use follows the pages' budget formula and fits gfx950's 160 KB per CU
+        assert d["lds_bytes"] == layout.lds_bytes(d["bm"], d["bn"], d["bk"], 2, d["stages"])
+        assert d["lds_bytes"] <= 160 * 1024
+        # per-lane accumulator registers of one wave: (BM/Wm)*(BN/Wn)/64 fp32
+        acc = (d["bm"] // d["waves_m"]) * (d["bn"] // d["waves_n"]) // 64
+        assert acc <= 256
+    with pytest.raises(RuntimeError):
+        mg.mg_config_info(n)
+    assert L.mg_set_config(n) == BADCFG
+    assert L.mg_set_config(-2) == BADCFG
+    assert L.mg_set_config(-1) == OK
+
+
+def test_table_selection_for_the_workloads(L):
+    sel = lambda *a: L.mg_select_config(*a)
+    big = mg.mg_config_info(sel(8192, 8192, 8192, BF16, 0))
+    assert big["bm"] * big["bn"] >= 128 * 128
+    mid = mg.mg_config_info(sel(1024, 1024, 2048, F16, 0))
+    # a 1024 x 1024 output must still give every CU at least one tile
+    assert (1024 // mid["bm"]) * (1024 // mid["bn"]) >= 128
+    for cid in range(L.mg_num_configs()):
+        assert L.mg_set_config(cid) == OK
+        assert L.mg_select_config(8192, 8192, 8192, BF16, 0) == cid
+    assert L.mg_set_config(-1) == OK

@@ -1,0 +1,250 @@
+"""GPU parity: the HIP kernels, called through the C ABI, against the CPU oracle.
+
+Gates (oracle/compare.py): bit-exact for integer-valued inputs (the fp32
+accumulation of small integers is exact, so one rounding of the exact sum is
+the only correct output), |got - ref| <= 1e-2 + 1e-2 |ref| for random floats,
+unchanged guard bands around every output, and identical bits on a repeated
+call.  Small shapes compare every output element; the 8192^3 and grouped
+workloads compare the seeded 4096-element sample plus the edge set, and
+screen the whole output with Freivalds' check.
+"""
+import numpy as np
+import pytest
+
+import tiled_matrix_multiplication_gemm_amd as mg
+from oracle import compare, layout
+from tiled_matrix_multiplication_gemm_amd import inputs
+from tests.gpu_util import (F16, BF16, Guarded, announce, assert_bitexact, assert_tolerance, to_dev, to_host)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    mg.lib()
+    yield
+    mg.mg_set_config(-1)
+
+
+def run_dense(case, cfg=-1, ldc_pad=0, lda_pad=0, ldb_pad=0):
+    """Run one dense case through the ABI; returns (result bits, guards intact)."""
+    import torch
+
+    M, N, K = case.M, case.N, case.K
+    dt = case.dtype
+
+    def padded(bits, rows, cols, pad):
+        if pad == 0:
+            return to_dev(bits, dt)
+        full = np.zeros((rows, cols + pad), dtype=np.uint16)
+        full[:, :cols] = bits
+        return to_dev(full, dt)[:, :cols]
+
+    A = padded(case.A, M, K, lda_pad)
+    B = padded(case.B, K, N, ldb_pad)
+    out = Guarded(M, N, dt, ld=N + ldc_pad)
+    mg.mg_set_config(cfg)
+    try:
+        if case.bias is not None:
+            mg.mg_gemm_bias_relu(A, B, to_dev(case.bias, dt), out=out.mat)
+        else:
+            mg.mg_gemm(A, B, out=out.mat)
+        torch.cuda.synchronize()
+    finally:
+        mg.mg_set_config(-1)
+    return out.result(), out.guards_intact()
+
+
+def check_full(orc, case, cfg=-1, **kw):
+    announce("dense %s M=%d N=%d K=%d dt=%d int=%s cfg=%d %s" % (case.name, case.M, case.N, case.K, case.dtype,
+                                                                  case.integer, cfg, kw))
+    got, guards = run_dense(case, cfg, **kw)
+    assert guards, "write outside the output"
+    ref, ref_q = orc.gemm(case.A, case.B, case.dtype, bias=case.bias, relu=case.relu)
+    if case.integer:
+        assert_bitexact(got, ref_q, case.dtype, case.name)
+    else:
+        assert_tolerance(got, ref, case.dtype, case.name)
+
+
+SMALL = [(1, 1, 1), (7, 33, 129), (33, 7, 1000), (129, 129, 33), (64, 64, 64), (65, 200, 72),
+         (300, 257, 130), (1000, 7, 33), (256, 384, 200), (513, 129, 257)]
+
+
+@pytest.mark.parametrize("cfg", range(6))
+@pytest.mark.parametrize("dtype", [F16, BF16])
+def test_small_ragged_shapes_every_config(orc, cfg, dtype):
+    for i, (M, N, K) in enumerate(SMALL):
+        for integer in (True, False):
+            for epi in (False, True):
+                seed = 1000 + 10 * i + 2 * integer + epi
+                if integer:
+                    c = inputs.integer_dense(M, N, K, dtype, seed, epilogue=epi, name="small")
+                else:
+                    c = inputs.random_dense(M, N, K, dtype, seed, epilogue=epi, name="small")
+                check_full(orc, c, cfg)
+
+
+@pytest.mark.parametrize("pads", [(8, 0, 0), (0, 16, 0), (0, 0, 8), (24, 8, 40)])
+def test_leading_strides_larger_than_rows(orc, pads):
+    c = inputs.integer_dense(130, 70, 90, F16, 77, epilogue=True, name="strided")
+    check_full(orc, c, -1, lda_pad=pads[0], ldb_pad=pads[1], ldc_pad=pads[2])
+
+
+def test_k_zero_gives_the_empty_sum(orc):
+    import torch
+
+    announce("K=0")
+    for dt in (F16, BF16):
+        A = torch.empty((5, 0), dtype=torch.float16 if dt == F16 else torch.bfloat16, device="cuda")
+        B = torch.empty((0, 9), dtype=A.dtype, device="cuda")
+        out = Guarded(5, 9, dt, ld=16)
+        mg.mg_gemm(A, B, out=out.mat)
+        bias_v = np.array([1, -2, 0.5, 3, -1, 0, 2, -4, 7], dtype=np.float64)
+        out2 = Guarded(5, 9, dt, ld=16)
+        mg.mg_gemm_bias_relu(A, B, to_dev(inputs.to_bits(bias_v, dt), dt), out=out2.mat)
+        torch.cuda.synchronize()
+        assert out.guards_intact() and out2.guards_intact()
+        assert np.all((out.result() & 0x7FFF) == 0)
+        got = compare.to_f64(out2.result(), dt)
+        assert np.array_equal(got, np.broadcast_to(np.maximum(bias_v, 0), (5, 9)))
+
+
+@pytest.mark.parametrize("variant", ["int", "float"])
+def test_workload_256_f16(orc, variant):
+    check_full(orc, inputs.dense_workload("gemm_256_f16", variant))
+
+
+@pytest.mark.parametrize("variant", ["int", "stress", "float"])
+def test_workload_1024x1024x2048_f16(orc, variant):
+    check_full(orc, inputs.dense_workload("gemm_1024x1024x2048_f16", variant))
+
+
+@pytest.mark.parametrize("variant", ["int", "float"])
+def test_workload_bias_relu_1024x1024x2048_f16(orc, variant):
+    check_full(orc, inputs.dense_workload("gemm_bias_relu_1024x1024x2048_f16", variant))
+
+
+def test_rounding_ties_to_even_in_bf16_and_f16(orc):
+    # sums of entries in 1..4 over K=2048 land far above 256 (bf16) and 2048
+    # (fp16), where many exact sums fall on ties of the output spacing
+    for dt in (BF16, F16):
+        c = inputs.integer_dense(128, 192, 2048, dt, 4242, lo=1, hi=4, name="ties")
+        check_full(orc, c)
+
+
+@pytest.mark.parametrize("variant", ["int", "float"])
+def test_workload_8192_bf16_sampled(orc, variant):
+    import torch
+
+    name = "gemm_8192_bf16"
+    w = inputs.DENSE_WORKLOADS[name]
+    c = inputs.dense_workload(name, variant)
+    announce("dense %s %s (sampled)" % (name, variant))
+    A, B = to_dev(c.A, c.dtype), to_dev(c.B, c.dtype)
+    C = mg.mg_gemm(A, B)
+    torch.cuda.synchronize()
+    got = to_host(C)
+    C2 = mg.mg_gemm(A, B)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(C2), got), "not deterministic"
+    rows, cols = compare.sample_positions(c.M, c.N, 4096, w["seed_sample"])
+    er, ec = compare.edge_positions(c.M, c.N)
+    rows, cols = np.concatenate([rows, er]), np.concatenate([cols, ec])
+    ref, ref_q = orc.gemm_sampled(c.A, c.B, c.dtype, rows, cols)
+    if c.integer:
+        assert_bitexact(got[rows, cols], ref_q, c.dtype, name)
+    else:
+        assert_tolerance(got[rows, cols], ref, c.dtype, name)
+    bad = compare.freivalds_rows(got, compare.to_f64(c.A, c.dtype), compare.to_f64(c.B, c.dtype), c.dtype, seed=5)
+    assert bad.size == 0, "Freivalds screen fails on rows %s" % bad[:10]
+
+
+def run_grouped(case):
+    import torch
+
+    X, W = to_dev(case.X, case.dtype), to_dev(case.W, case.dtype)
+    off = torch.from_numpy(case.offsets.astype(np.int32)).cuda()
+    out = Guarded(case.T, case.N, case.dtype)
+    mg.mg_grouped_gemm(X, W, off, out=out.mat)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("variant", ["int", "float"])
+def test_workload_grouped_moe_sampled(orc, variant):
+    name = "grouped_moe_e32_t8192_k1024_n4096_f16"
+    w = inputs.GROUPED_WORKLOADS[name]
+    c = inputs.grouped_workload(name, variant)
+    announce("grouped %s %s counts[min=%d max=%d]" % (name, variant, c.counts.min(), c.counts.max()))
+    out = run_grouped(c)
+    assert out.guards_intact()
+    got = out.result()
+    rows, cols = compare.sample_positions(c.T, c.N, 4096, w["seed_sample"])
+    er, ec = compare.edge_positions(c.T, c.N, segment_starts=c.offsets)
+    rows, cols = np.concatenate([rows, er]), np.concatenate([cols, ec])
+    ref, ref_q = orc.grouped_sampled(c.X, c.W, c.offsets, c.dtype, rows, cols)
+    if c.integer:
+        assert_bitexact(got[rows, cols], ref_q, c.dtype, name)
+    else:
+        assert_tolerance(got[rows, cols], ref, c.dtype, name)
+    Xf = compare.to_f64(c.X, c.dtype)
+    for e in range(c.E):
+        r0, r1 = c.offsets[e], c.offsets[e + 1]
+        bad = compare.freivalds_rows(got[r0:r1], Xf[r0:r1], compare.to_f64(c.W[e], c.dtype), c.dtype, seed=e)
+        assert bad.size == 0, "expert %d: Freivalds screen fails on rows %s" % (e, bad[:10])
+
+
+@pytest.mark.parametrize("dtype", [F16, BF16])
+def test_grouped_skewed_counts_full(orc, dtype):
+    counts = np.array([0, 1, 255, 257, 0, 64, 3, 129, 0, 0, 40, 300])
+    T = int(counts.sum())
+    for integer in (True, False):
+        c = inputs.random_grouped(E=len(counts), T=T, K=136, N=200, dtype=dtype, seed=31 + integer, counts=counts,
+                                  integer=integer)
+        announce("grouped skewed dt=%d int=%s T=%d" % (dtype, integer, T))
+        out = run_grouped(c)
+        assert out.guards_intact()
+        ref, ref_q = orc.grouped_gemm(c.X, c.W, c.offsets, dtype)
+        if integer:
+            assert_bitexact(out.result(), ref_q, dtype, "grouped skewed")
+        else:
+            assert_tolerance(out.result(), ref, dtype, "grouped skewed")
+
+
+def test_grouped_every_config(orc):
+    counts = np.array([5, 0, 130, 67, 1])
+    c = inputs.random_grouped(E=5, T=int(counts.sum()), K=72, N=136, dtype=F16, seed=3, counts=counts, integer=True)
+    ref, ref_q = orc.grouped_gemm(c.X, c.W, c.offsets, F16)
+    for cfg in range(mg.mg_num_configs()):
+        announce("grouped cfg=%d" % cfg)
+        mg.mg_set_config(cfg)
+        try:
+            out = run_grouped(c)
+        finally:
+            mg.mg_set_config(-1)
+        assert out.guards_intact()
+        assert_bitexact(out.result(), ref_q, F16, "grouped cfg %d" % cfg)
+
+
+@pytest.mark.parametrize("M,N,K", [(130, 70, 200), (64, 64, 64), (1024, 1024, 2048)])
+def test_prepack_layout_and_packed_gemm(orc, M, N, K):
+    import torch
+
+    c = inputs.integer_dense(M, N, K, F16, 555 + M, name="prepack")
+    announce("prepack M=%d N=%d K=%d" % (M, N, K))
+    BK = mg.mg_config_bk(M, N, K)
+    A = to_dev(c.A, F16)
+    Ap = mg.mg_prepack_a(A, BK)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(Ap).reshape(Ap.shape), layout.prepack_a(c.A, BK))
+    out = Guarded(M, N, F16)
+    mg.mg_gemm_prepacked(Ap, BK, to_dev(c.B, F16), M, K, out=out.mat)
+    torch.cuda.synchronize()
+    assert out.guards_intact()
+    _, ref_q = orc.gemm(c.A, c.B, F16)
+    assert_bitexact(out.result(), ref_q, F16, "prepacked")

@@ -1,0 +1,241 @@
+"""Python binding of libmi355gemm.so (tiled GEMM for one MI355X).
+
+Argument marshalling only: each function takes torch tensors that already
+live in GPU memory, passes their pointers, sizes, strides, dtype and torch's
+current HIP stream to the C ABI declared in include/mi355gemm.h, and raises
+RuntimeError with the library's message on a non-OK status.  All arithmetic
+happens in the library's HIP kernels; there is no fallback.  torch is used
+for device memory and streams only.
+
+The library is built in-tree (``python -m tiled_matrix_multiplication_gemm_amd.build``)
+and loaded on first use; using any entry point without it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmi355gemm.so")
+
+MG_F16 = 0
+MG_BF16 = 1
+
+_lock = threading.Lock()
+_lib = None
+
+
+class ConfigDesc(ctypes.Structure):
+    _fields_ = [
+        ("id", ctypes.c_int), ("bm", ctypes.c_int), ("bn", ctypes.c_int), ("bk", ctypes.c_int),
+        ("waves_m", ctypes.c_int), ("waves_n", ctypes.c_int), ("stages", ctypes.c_int),
+        ("mfma_m", ctypes.c_int), ("mfma_n", ctypes.c_int), ("mfma_k", ctypes.c_int),
+        ("group_m", ctypes.c_int), ("xcd_remap", ctypes.c_int), ("lds_bytes", ctypes.c_int),
+        ("name", ctypes.c_char_p),
+    ]
+
+
+EXPORTED = (
+    "mg_status_string", "mg_gemm", "mg_gemm_bias_relu", "mg_grouped_gemm", "mg_prepacked_bytes",
+    "mg_prepack_a", "mg_config_bk", "mg_gemm_prepacked", "mg_num_configs", "mg_config_info",
+    "mg_set_config", "mg_last_config", "mg_select_config",
+)
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library with argument types declared (raises if not built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libmi355gemm.so is not built; run `python -m tiled_matrix_multiplication_gemm_amd.build`")
+        import torch  # noqa: F401  -- load torch's HIP runtime first so both share one runtime
+
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, cint = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.mg_status_string.restype = ctypes.c_char_p
+        L.mg_status_string.argtypes = [cint]
+        L.mg_gemm.restype = cint
+        L.mg_gemm.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, i64, cint, cint, vp]
+        L.mg_gemm_bias_relu.restype = cint
+        L.mg_gemm_bias_relu.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, i64, cint, cint, vp]
+        L.mg_grouped_gemm.restype = cint
+        L.mg_grouped_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, cint, vp]
+        L.mg_prepacked_bytes.restype = ctypes.c_size_t
+        L.mg_prepacked_bytes.argtypes = [i64, i64, i64, cint]
+        L.mg_prepack_a.restype = cint
+        L.mg_prepack_a.argtypes = [vp, vp, i64, i64, i64, i64, cint, vp]
+        L.mg_config_bk.restype = i64
+        L.mg_config_bk.argtypes = [i64, i64, i64, cint]
+        L.mg_gemm_prepacked.restype = cint
+        L.mg_gemm_prepacked.argtypes = [vp, i64, vp, vp, i64, i64, i64, i64, i64, i64, i64, cint, vp]
+        L.mg_num_configs.restype = cint
+        L.mg_num_configs.argtypes = []
+        L.mg_config_info.restype = cint
+        L.mg_config_info.argtypes = [cint, ctypes.POINTER(ConfigDesc)]
+        L.mg_set_config.restype = cint
+        L.mg_set_config.argtypes = [cint]
+        L.mg_last_config.restype = cint
+        L.mg_last_config.argtypes = []
+        L.mg_select_config.restype = cint
+        L.mg_select_config.argtypes = [i64, i64, i64, cint, cint]
+        _lib = L
+        return L
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise RuntimeError(lib().mg_status_string(status).decode())
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.float16:
+        return MG_F16
+    if t.dtype == torch.bfloat16:
+        return MG_BF16
+    raise RuntimeError("MG_ERR_UNSUPPORTED_DTYPE: tensor dtype %s is not float16/bfloat16" % t.dtype)
+
+
+def _stream(t):
+    import torch
+
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _require_gpu(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise RuntimeError("mi355gemm operates on GPU tensors only (got a %s tensor)" % t.device)
+
+
+def mg_gemm(a, b, out=None):
+    """out[M,N] = a[M,K] @ b[K,N] (fp16/bf16, fp32 accumulation)."""
+    import torch
+
+    _require_gpu(a, b)
+    M, K = a.shape
+    K2, N = b.shape
+    if K2 != K:
+        raise RuntimeError("MG_ERR_INVALID_ARG: inner dimensions differ (%d vs %d)" % (K, K2))
+    if out is None:
+        out = torch.empty((M, N), dtype=a.dtype, device=a.device)
+    _check(lib().mg_gemm(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, a.stride(0), a.stride(1),
+                         b.stride(0), b.stride(1), out.stride(0), out.stride(1), _dtype_code(a), _dtype_code(out),
+                         _stream(a)))
+    return out
+
+
+def mg_gemm_bias_relu(a, b, bias, out=None):
+    """out = ReLU(a @ b + bias) in one kernel."""
+    import torch
+
+    _require_gpu(a, b, bias)
+    M, K = a.shape
+    K2, N = b.shape
+    if K2 != K or bias.shape != (N,) or (N > 1 and bias.stride(0) != 1):
+        raise RuntimeError("MG_ERR_INVALID_ARG: shapes a[M,K], b[K,N], contiguous bias[N] expected")
+    if bias.dtype != a.dtype:
+        raise RuntimeError("MG_ERR_UNSUPPORTED_DTYPE: bias must have the output dtype")
+    if out is None:
+        out = torch.empty((M, N), dtype=a.dtype, device=a.device)
+    _check(lib().mg_gemm_bias_relu(a.data_ptr(), b.data_ptr(), bias.data_ptr(), out.data_ptr(), M, N, K,
+                                   a.stride(0), a.stride(1), b.stride(0), b.stride(1), out.stride(0),
+                                   out.stride(1), _dtype_code(a), _dtype_code(out), _stream(a)))
+    return out
+
+
+def mg_grouped_gemm(x, w, offsets, out=None):
+    """out[o_e:o_{e+1}] = x[o_e:o_{e+1}] @ w[e] for every expert e (one launch).
+
+    x: [T,K], w: [E,K,N], offsets: int32 device tensor [E+1] (0, ..., T)."""
+    import torch
+
+    _require_gpu(x, w, offsets)
+    T, K = x.shape
+    E, K2, N = w.shape
+    if K2 != K or offsets.shape != (E + 1,) or offsets.dtype != torch.int32 or not offsets.is_contiguous():
+        raise RuntimeError("MG_ERR_INVALID_ARG: x[T,K], w[E,K,N], contiguous int32 offsets[E+1] expected")
+    if w.stride(2) != 1 and N > 1:
+        raise RuntimeError("MG_ERR_UNSUPPORTED_LAYOUT: w must have a unit inner stride")
+    if w.dtype != x.dtype:
+        raise RuntimeError("MG_ERR_UNSUPPORTED_DTYPE: x and w must share a dtype")
+    if out is None:
+        out = torch.empty((T, N), dtype=x.dtype, device=x.device)
+    if x.stride(1) != 1 and K > 1 or out.stride(1) != 1 and N > 1:
+        raise RuntimeError("MG_ERR_UNSUPPORTED_LAYOUT: unit inner strides required")
+    _check(lib().mg_grouped_gemm(x.data_ptr(), w.data_ptr(), out.data_ptr(), offsets.data_ptr(), E, T, N, K,
+                                 x.stride(0), w.stride(0), w.stride(1), out.stride(0), _dtype_code(x), _stream(x)))
+    return out
+
+
+def mg_prepacked_bytes(M: int, K: int, BK: int, dtype: int = MG_F16) -> int:
+    return int(lib().mg_prepacked_bytes(M, K, BK, dtype))
+
+
+def mg_config_bk(M: int, N: int, K: int, dtype: int = MG_F16) -> int:
+    return int(lib().mg_config_bk(M, N, K, dtype))
+
+
+def mg_prepack_a(a, BK: int, out=None):
+    """Blocked copy of a[M,K] as [ceil(K/BK), M, BK] (zero-padded K tail)."""
+    import torch
+
+    _require_gpu(a)
+    M, K = a.shape
+    if out is None:
+        out = torch.empty(((K + BK - 1) // BK, M, BK), dtype=a.dtype, device=a.device)
+    if a.stride(1) != 1 and K > 1:
+        raise RuntimeError("MG_ERR_UNSUPPORTED_LAYOUT: unit inner stride required")
+    _check(lib().mg_prepack_a(a.data_ptr(), out.data_ptr(), M, K, a.stride(0), BK, _dtype_code(a), _stream(a)))
+    return out
+
+
+def mg_gemm_prepacked(ap, BK: int, b, M: int, K: int, out=None):
+    """out[M,N] = A @ b with A given in the blocked layout of mg_prepack_a."""
+    import torch
+
+    _require_gpu(ap, b)
+    K2, N = b.shape
+    if K2 != K:
+        raise RuntimeError("MG_ERR_INVALID_ARG: inner dimensions differ")
+    if out is None:
+        out = torch.empty((M, N), dtype=b.dtype, device=b.device)
+    _check(lib().mg_gemm_prepacked(ap.data_ptr(), BK, b.data_ptr(), out.data_ptr(), M, N, K, b.stride(0),
+                                   b.stride(1), out.stride(0), out.stride(1), _dtype_code(b), _stream(b)))
+    return out
+
+
+def mg_num_configs() -> int:
+    return int(lib().mg_num_configs())
+
+
+def mg_config_info(cid: int) -> dict:
+    d = ConfigDesc()
+    _check(lib().mg_config_info(cid, ctypes.byref(d)))
+    out = {f: getattr(d, f) for f, _ in ConfigDesc._fields_}
+    out["name"] = out["name"].decode()
+    return out
+
+
+def mg_set_config(cid: int) -> None:
+    _check(lib().mg_set_config(cid))
+
+
+def mg_last_config() -> int:
+    return int(lib().mg_last_config())
+
+
+def mg_select_config(M: int, N: int, K: int, dtype: int = MG_F16, grouped: bool = False) -> int:
+    return int(lib().mg_select_config(M, N, K, dtype, int(bool(grouped))))
+
+
+# short names
+gemm = mg_gemm
+gemm_bias_relu = mg_gemm_bias_relu
+grouped_gemm = mg_grouped_gemm
+prepack_a = mg_prepack_a
+gemm_prepacked = mg_gemm_prepacked

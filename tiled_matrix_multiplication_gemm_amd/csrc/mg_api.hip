@@ -1,0 +1,298 @@
+// C ABI of libmi355gemm.so: argument validation (host only, before any HIP
+// call), configuration selection from the static table, and kernel launch on
+// the caller's stream.  See include/mi355gemm.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <stdint.h>
+
+#include "mi355gemm.h"
+#include "mg_tile.h"
+
+namespace {
+
+using namespace mg;
+
+// ---- configuration table ---------------------------------------------------
+// One row per compiled tile shape.  The table is static: rows are chosen by
+// shape class in select_config(), which an offline sweep tunes; there is no
+// run-time search.
+using Cfg0 = TileCfg<256, 256, 64, 2, 2>;  // large square problems
+using Cfg1 = TileCfg<128, 128, 64, 2, 2>;  // mid-size, grouped
+using Cfg2 = TileCfg<64, 64, 64, 2, 2>;    // small problems: enough tiles to fill 256 CUs
+using Cfg3 = TileCfg<128, 256, 64, 2, 2>;
+using Cfg4 = TileCfg<256, 128, 64, 2, 2>;
+using Cfg5 = TileCfg<128, 128, 32, 2, 2>;
+
+constexpr int kNumConfigs = 6;
+constexpr int kGroupM = 8;
+
+template <class C>
+constexpr mg_config_desc describe(int id, const char* name) {
+    return mg_config_desc{id, C::BM, C::BN, C::BK, C::WM, C::WN, C::STAGES, 32, 32, 16, kGroupM, 1, C::LDS_BYTES,
+                          name};
+}
+
+const mg_config_desc kTable[kNumConfigs] = {
+    describe<Cfg0>(0, "t256x256k64_w2x2"), describe<Cfg1>(1, "t128x128k64_w2x2"),
+    describe<Cfg2>(2, "t64x64k64_w2x2"),   describe<Cfg3>(3, "t128x256k64_w2x2"),
+    describe<Cfg4>(4, "t256x128k64_w2x2"), describe<Cfg5>(5, "t128x128k32_w2x2"),
+};
+
+std::atomic<int> g_forced{-1};
+std::atomic<int> g_last{-1};
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int select_config(int64_t M, int64_t N, int64_t K, int grouped) {
+    (void)K;
+    int forced = g_forced.load();
+    if (forced >= 0) return forced;
+    if (grouped) return 1;
+    if (cdiv(M, 256) * cdiv(N, 256) >= 512) return 0;
+    if (cdiv(M, 128) * cdiv(N, 128) >= 256) return 1;
+    return 2;
+}
+
+// ---- validation --------------------------------------------------------------
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// A rows x cols matrix with row stride ld and inner stride inner.
+mg_status check_matrix(const void* p, int64_t rows, int64_t cols, int64_t ld, int64_t inner) {
+    if (rows < 0 || cols < 0) return MG_ERR_INVALID_ARG;
+    if (rows == 0 || cols == 0) return MG_OK;  // no extent: never dereferenced
+    if (p == nullptr) return MG_ERR_INVALID_ARG;
+    if (cols > 1 && inner != 1) return MG_ERR_UNSUPPORTED_LAYOUT;
+    if (rows > 1 && ld < cols) return MG_ERR_UNSUPPORTED_LAYOUT;
+    if (!aligned16(p)) return MG_ERR_MISALIGNED;
+    if (rows > 1 && (ld % 8) != 0) return MG_ERR_MISALIGNED;
+    return MG_OK;
+}
+
+mg_status check_dtype(mg_dtype in, mg_dtype out) {
+    if ((in != MG_F16 && in != MG_BF16) || in != out) return MG_ERR_UNSUPPORTED_DTYPE;
+    return MG_OK;
+}
+
+#define MG_TRY(expr)                         \
+    do {                                     \
+        mg_status s_ = (expr);               \
+        if (s_ != MG_OK) return s_;          \
+    } while (0)
+
+// ---- launch --------------------------------------------------------------------
+template <class C, int DT, bool EPI, int MODE>
+mg_status launch_cfg(const KArgs& a, int64_t grid, hipStream_t stream) {
+    (void)hipGetLastError();  // clear a stale error so the check below is ours
+    hipLaunchKernelGGL((gemm_tile_kernel<C, DT, EPI, MODE>), dim3((unsigned)grid), dim3(C::NT), 0, stream, a);
+    return hipGetLastError() == hipSuccess ? MG_OK : MG_ERR_HIP;
+}
+
+template <class C>
+mg_status launch_dt(int dt, bool epi, int mode, const KArgs& a, int64_t grid, hipStream_t s) {
+    if (dt == DT_F16) {
+        if (mode == MODE_GROUPED) return launch_cfg<C, DT_F16, false, MODE_GROUPED>(a, grid, s);
+        if (mode == MODE_PACKED_A) return launch_cfg<C, DT_F16, false, MODE_PACKED_A>(a, grid, s);
+        return epi ? launch_cfg<C, DT_F16, true, MODE_DENSE>(a, grid, s)
+                   : launch_cfg<C, DT_F16, false, MODE_DENSE>(a, grid, s);
+    }
+    if (mode == MODE_GROUPED) return launch_cfg<C, DT_BF16, false, MODE_GROUPED>(a, grid, s);
+    if (mode == MODE_PACKED_A) return launch_cfg<C, DT_BF16, false, MODE_PACKED_A>(a, grid, s);
+    return epi ? launch_cfg<C, DT_BF16, true, MODE_DENSE>(a, grid, s)
+               : launch_cfg<C, DT_BF16, false, MODE_DENSE>(a, grid, s);
+}
+
+mg_status launch(int cfg, int dt, bool epi, int mode, KArgs& a, hipStream_t s) {
+    const mg_config_desc& d = kTable[cfg];
+    a.tiles_n = (int32_t)cdiv(a.N, d.bn);
+    int64_t grid;
+    if (mode == MODE_GROUPED) {
+        a.tiles_m = 0;
+        grid = (cdiv(a.M, d.bm) + a.E) * a.tiles_n;
+    } else {
+        a.tiles_m = (int32_t)cdiv(a.M, d.bm);
+        grid = (int64_t)a.tiles_m * a.tiles_n;
+    }
+    if (grid <= 0) return MG_OK;
+    if (grid > 0x7fffffff) return MG_ERR_INVALID_ARG;
+    a.group_m = d.group_m;
+    a.xcd_remap = d.xcd_remap;
+    mg_status st;
+    switch (cfg) {
+        case 0: st = launch_dt<Cfg0>(dt, epi, mode, a, grid, s); break;
+        case 1: st = launch_dt<Cfg1>(dt, epi, mode, a, grid, s); break;
+        case 2: st = launch_dt<Cfg2>(dt, epi, mode, a, grid, s); break;
+        case 3: st = launch_dt<Cfg3>(dt, epi, mode, a, grid, s); break;
+        case 4: st = launch_dt<Cfg4>(dt, epi, mode, a, grid, s); break;
+        case 5: st = launch_dt<Cfg5>(dt, epi, mode, a, grid, s); break;
+        default: return MG_ERR_BAD_CONFIG;
+    }
+    if (st == MG_OK) g_last.store(cfg);
+    return st;
+}
+
+mg_status gemm_common(const void* A, const void* B, const void* bias, void* C, int64_t M, int64_t N, int64_t K,
+                      int64_t sam, int64_t sak, int64_t sbk, int64_t sbn, int64_t scm, int64_t scn,
+                      mg_dtype in_dtype, mg_dtype out_dtype, bool epi, hipStream_t stream) {
+    if (M < 0 || N < 0 || K < 0) return MG_ERR_INVALID_ARG;
+    MG_TRY(check_dtype(in_dtype, out_dtype));
+    MG_TRY(check_matrix(A, M, K, sam, sak));
+    MG_TRY(check_matrix(B, K, N, sbk, sbn));
+    MG_TRY(check_matrix(C, M, N, scm, scn));
+    if (epi && N > 0 && M > 0 && bias == nullptr) return MG_ERR_INVALID_ARG;
+    if (M == 0 || N == 0) return MG_OK;
+    const int cfg = select_config(M, N, K, 0);
+    if (cfg < 0 || cfg >= kNumConfigs) return MG_ERR_BAD_CONFIG;
+    KArgs a{};
+    a.A = (const uint16_t*)A;
+    a.B = (const uint16_t*)B;
+    a.C = (uint16_t*)C;
+    a.bias = (const uint16_t*)bias;
+    a.M = M; a.N = N; a.K = K;
+    a.lda = sam; a.ldb = sbk; a.ldc = scm;
+    return launch(cfg, (int)in_dtype, epi, MODE_DENSE, a, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mg_status_string(mg_status status) {
+    switch (status) {
+        case MG_OK: return "MG_OK";
+        case MG_ERR_INVALID_ARG: return "MG_ERR_INVALID_ARG: null pointer with a nonzero extent, or a negative size";
+        case MG_ERR_UNSUPPORTED_DTYPE: return "MG_ERR_UNSUPPORTED_DTYPE: types must be fp16 or bf16, in == out";
+        case MG_ERR_UNSUPPORTED_LAYOUT: return "MG_ERR_UNSUPPORTED_LAYOUT: inner stride must be 1 and rows must not overlap";
+        case MG_ERR_MISALIGNED: return "MG_ERR_MISALIGNED: base pointers must be 16-byte aligned, leading strides multiples of 8";
+        case MG_ERR_HIP: return "MG_ERR_HIP: the HIP runtime reported an error at launch";
+        case MG_ERR_BAD_CONFIG: return "MG_ERR_BAD_CONFIG: unknown configuration or K step";
+    }
+    return "unknown mg_status";
+}
+
+mg_status mg_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int64_t stride_am,
+                  int64_t stride_ak, int64_t stride_bk, int64_t stride_bn, int64_t stride_cm, int64_t stride_cn,
+                  mg_dtype in_dtype, mg_dtype out_dtype, hipStream_t stream) {
+    return gemm_common(A, B, nullptr, C, M, N, K, stride_am, stride_ak, stride_bk, stride_bn, stride_cm, stride_cn,
+                       in_dtype, out_dtype, false, stream);
+}
+
+mg_status mg_gemm_bias_relu(const void* A, const void* B, const void* bias, void* C, int64_t M, int64_t N, int64_t K,
+                            int64_t stride_am, int64_t stride_ak, int64_t stride_bk, int64_t stride_bn,
+                            int64_t stride_cm, int64_t stride_cn, mg_dtype in_dtype, mg_dtype out_dtype,
+                            hipStream_t stream) {
+    return gemm_common(A, B, bias, C, M, N, K, stride_am, stride_ak, stride_bk, stride_bn, stride_cm, stride_cn,
+                       in_dtype, out_dtype, true, stream);
+}
+
+mg_status mg_grouped_gemm(const void* X, const void* W, void* Y, const int32_t* expert_offsets, int64_t E, int64_t T,
+                          int64_t N, int64_t K, int64_t stride_xm, int64_t stride_we, int64_t stride_wk,
+                          int64_t stride_ym, mg_dtype dtype, hipStream_t stream) {
+    if (E < 0 || T < 0 || N < 0 || K < 0 || E > 0x7fffffff || T > 0x7fffffff) return MG_ERR_INVALID_ARG;
+    MG_TRY(check_dtype(dtype, dtype));
+    if (E == 0 && T > 0) return MG_ERR_INVALID_ARG;
+    MG_TRY(check_matrix(X, T, K, stride_xm, 1));
+    MG_TRY(check_matrix(Y, T, N, stride_ym, 1));
+    if (E > 0 && K > 0 && N > 0) {
+        MG_TRY(check_matrix(W, K, N, stride_wk, 1));
+        if (E > 1 && stride_we < (K - 1) * stride_wk + N) return MG_ERR_UNSUPPORTED_LAYOUT;
+        if (stride_we % 8 != 0) return MG_ERR_MISALIGNED;
+    }
+    if (T == 0 || N == 0) return MG_OK;
+    if (expert_offsets == nullptr) return MG_ERR_INVALID_ARG;
+    const int cfg = select_config(T, N, K, 1);
+    if (cfg < 0 || cfg >= kNumConfigs) return MG_ERR_BAD_CONFIG;
+    KArgs a{};
+    a.A = (const uint16_t*)X;
+    a.B = (const uint16_t*)W;
+    a.C = (uint16_t*)Y;
+    a.offsets = expert_offsets;
+    a.M = T; a.N = N; a.K = K;
+    a.lda = stride_xm; a.ldb = stride_wk; a.ldc = stride_ym;
+    a.stride_we = stride_we;
+    a.E = (int32_t)E;
+    return launch(cfg, (int)dtype, false, MODE_GROUPED, a, stream);
+}
+
+size_t mg_prepacked_bytes(int64_t M, int64_t K, int64_t BK, mg_dtype dtype) {
+    (void)dtype;
+    if (M <= 0 || K <= 0 || BK <= 0) return 0;
+    return (size_t)(cdiv(K, BK) * M * BK * 2);
+}
+
+int64_t mg_config_bk(int64_t M, int64_t N, int64_t K, mg_dtype dtype) {
+    (void)dtype;
+    const int cfg = select_config(M, N, K, 0);
+    if (cfg < 0 || cfg >= kNumConfigs) return -1;
+    return kTable[cfg].bk;
+}
+
+mg_status mg_prepack_a(const void* A, void* Ap, int64_t M, int64_t K, int64_t stride_am, int64_t BK, mg_dtype dtype,
+                       hipStream_t stream) {
+    if (M < 0 || K < 0) return MG_ERR_INVALID_ARG;
+    MG_TRY(check_dtype(dtype, dtype));
+    if (BK != 32 && BK != 64) return MG_ERR_BAD_CONFIG;
+    MG_TRY(check_matrix(A, M, K, stride_am, 1));
+    if (M == 0 || K == 0) return MG_OK;
+    if (Ap == nullptr) return MG_ERR_INVALID_ARG;
+    if (!aligned16(Ap)) return MG_ERR_MISALIGNED;
+    const int64_t chunks = cdiv(K, BK) * M * (BK / 8);
+    int64_t grid = cdiv(chunks, 256);
+    if (grid > 65536) grid = 65536;
+    (void)hipGetLastError();
+    if (BK == 64)
+        hipLaunchKernelGGL((prepack_a_kernel<64>), dim3((unsigned)grid), dim3(256), 0, stream, (const uint16_t*)A,
+                           (uint16_t*)Ap, M, K, stride_am);
+    else
+        hipLaunchKernelGGL((prepack_a_kernel<32>), dim3((unsigned)grid), dim3(256), 0, stream, (const uint16_t*)A,
+                           (uint16_t*)Ap, M, K, stride_am);
+    return hipGetLastError() == hipSuccess ? MG_OK : MG_ERR_HIP;
+}
+
+mg_status mg_gemm_prepacked(const void* Ap, int64_t BK, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                            int64_t stride_bk, int64_t stride_bn, int64_t stride_cm, int64_t stride_cn,
+                            mg_dtype dtype, hipStream_t stream) {
+    if (M < 0 || N < 0 || K < 0) return MG_ERR_INVALID_ARG;
+    MG_TRY(check_dtype(dtype, dtype));
+    MG_TRY(check_matrix(B, K, N, stride_bk, stride_bn));
+    MG_TRY(check_matrix(C, M, N, stride_cm, stride_cn));
+    if (M > 0 && K > 0) {
+        if (Ap == nullptr) return MG_ERR_INVALID_ARG;
+        if (!aligned16(Ap)) return MG_ERR_MISALIGNED;
+    }
+    if (M == 0 || N == 0) return MG_OK;
+    const int cfg = select_config(M, N, K, 0);
+    if (cfg < 0 || cfg >= kNumConfigs) return MG_ERR_BAD_CONFIG;
+    if (kTable[cfg].bk != BK) return MG_ERR_BAD_CONFIG;
+    KArgs a{};
+    a.A = (const uint16_t*)Ap;
+    a.B = (const uint16_t*)B;
+    a.C = (uint16_t*)C;
+    a.M = M; a.N = N; a.K = K;
+    a.lda = BK; a.ldb = stride_bk; a.ldc = stride_cm;
+    return launch(cfg, (int)dtype, false, MODE_PACKED_A, a, stream);
+}
+
+int mg_num_configs(void) { return kNumConfigs; }
+
+mg_status mg_config_info(int id, mg_config_desc* out) {
+    if (id < 0 || id >= kNumConfigs) return MG_ERR_BAD_CONFIG;
+    if (out == nullptr) return MG_ERR_INVALID_ARG;
+    *out = kTable[id];
+    return MG_OK;
+}
+
+mg_status mg_set_config(int id) {
+    if (id < -1 || id >= kNumConfigs) return MG_ERR_BAD_CONFIG;
+    g_forced.store(id);
+    return MG_OK;
+}
+
+int mg_last_config(void) { return g_last.load(); }
+
+int mg_select_config(int64_t M, int64_t N, int64_t K, mg_dtype dtype, int grouped) {
+    (void)dtype;
+    return select_config(M, N, K, grouped);
+}
+
+}  // extern "C"
