@@ -44,9 +44,11 @@ def run_dense(case, cfg=-1, ldc_pad=0, lda_pad=0, ldb_pad=0):
         full[:, :cols] = bits
         return to_dev(full, dt)[:, :cols]
 
-    A = padded(case.A, M, K, lda_pad)
-    B = padded(case.B, K, N, ldb_pad)
-    out = Guarded(M, N, dt, ld=N + ldc_pad)
+    # leading strides must be multiples of 8 elements: round up, then add the extra padding
+    up8 = lambda n: (n + 7) // 8 * 8
+    A = padded(case.A, M, K, up8(K) - K + lda_pad)
+    B = padded(case.B, K, N, up8(N) - N + ldb_pad)
+    out = Guarded(M, N, dt, ld=up8(N) + ldc_pad)
     mg.mg_set_config(cfg)
     try:
         if case.bias is not None:
@@ -231,14 +233,17 @@ def test_grouped_every_config(orc):
         assert_bitexact(out.result(), ref_q, F16, "grouped cfg %d" % cfg)
 
 
-@pytest.mark.parametrize("M,N,K", [(130, 70, 200), (64, 64, 64), (1024, 1024, 2048)])
+@pytest.mark.parametrize("M,N,K", [(130, 72, 203), (64, 64, 64), (1024, 1024, 2048)])
 def test_prepack_layout_and_packed_gemm(orc, M, N, K):
     import torch
 
     c = inputs.integer_dense(M, N, K, F16, 555 + M, name="prepack")
     announce("prepack M=%d N=%d K=%d" % (M, N, K))
     BK = mg.mg_config_bk(M, N, K)
-    A = to_dev(c.A, F16)
+    lda = (K + 7) // 8 * 8
+    Apad = np.zeros((M, lda), dtype=np.uint16)
+    Apad[:, :K] = c.A
+    A = to_dev(Apad, F16)[:, :K]
     Ap = mg.mg_prepack_a(A, BK)
     torch.cuda.synchronize()
     assert np.array_equal(to_host(Ap).reshape(Ap.shape), layout.prepack_a(c.A, BK))
