@@ -142,6 +142,11 @@ typedef struct {
     int group_m;              /* tile rows visited together (L2 reuse)     */
     int xcd_remap;            /* 1: consecutive tiles stay on one XCD      */
     int lds_bytes;            /* shared memory of one workgroup            */
+    int direct_lds;           /* 1: has the direct-to-LDS kernel, used when
+                                 K % direct_bk == 0 and N % 8 == 0         */
+    int direct_bk;            /* K slice of the direct-to-LDS kernel       */
+    int direct_stages;        /* LDS ring slots of the direct kernel       */
+    int direct_lds_bytes;     /* shared memory of the direct kernel        */
     const char* name;
 } mg_config_desc;
 

@@ -125,6 +125,10 @@ def test_config_table(L):
         # per-lane accumulator registers of one wave: (BM/Wm)*(BN/Wn)/64 fp32
         acc = (d["bm"] // d["waves_m"]) * (d["bn"] // d["waves_n"]) // 64
         assert acc <= 256
+        if d["direct_lds"]:
+            assert d["direct_bk"] in (32, 64) and d["direct_stages"] >= 2
+            assert d["direct_lds_bytes"] == layout.lds_bytes(d["bm"], d["bn"], d["direct_bk"], 2, d["direct_stages"])
+            assert d["direct_lds_bytes"] <= 160 * 1024
     with pytest.raises(RuntimeError):
         mg.mg_config_info(n)
     assert L.mg_set_config(n) == BADCFG

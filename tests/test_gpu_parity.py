@@ -73,11 +73,19 @@ def check_full(orc, case, cfg=-1, **kw):
         assert_tolerance(got, ref, case.dtype, case.name)
 
 
-SMALL = [(1, 1, 1), (7, 33, 129), (33, 7, 1000), (129, 129, 33), (64, 64, 64), (65, 200, 72),
-         (300, 257, 130), (1000, 7, 33), (256, 384, 200), (513, 129, 257)]
+# general-kernel shapes (K % 64 != 0 or N % 8 != 0) and direct-to-LDS shapes
+# (K % 64 == 0, N % 8 == 0) with ragged M and N edges
+SMALL = [(1, 1, 1), (7, 33, 129), (33, 7, 1000), (129, 129, 33), (65, 200, 72),
+         (300, 257, 130), (1000, 7, 33), (256, 384, 200), (513, 129, 257),
+         (64, 64, 64), (1, 8, 64), (65, 200, 128), (129, 136, 64), (300, 264, 192), (513, 520, 256)]
+NUM_CONFIGS = 7
 
 
-@pytest.mark.parametrize("cfg", range(6))
+def test_config_count_matches_library():
+    assert mg.mg_num_configs() == NUM_CONFIGS
+
+
+@pytest.mark.parametrize("cfg", range(NUM_CONFIGS))
 @pytest.mark.parametrize("dtype", [F16, BF16])
 def test_small_ragged_shapes_every_config(orc, cfg, dtype):
     for i, (M, N, K) in enumerate(SMALL):
@@ -201,12 +209,13 @@ def test_workload_grouped_moe_sampled(orc, variant):
         assert bad.size == 0, "expert %d: Freivalds screen fails on rows %s" % (e, bad[:10])
 
 
+@pytest.mark.parametrize("K", [136, 128])
 @pytest.mark.parametrize("dtype", [F16, BF16])
-def test_grouped_skewed_counts_full(orc, dtype):
+def test_grouped_skewed_counts_full(orc, dtype, K):
     counts = np.array([0, 1, 255, 257, 0, 64, 3, 129, 0, 0, 40, 300])
     T = int(counts.sum())
     for integer in (True, False):
-        c = inputs.random_grouped(E=len(counts), T=T, K=136, N=200, dtype=dtype, seed=31 + integer, counts=counts,
+        c = inputs.random_grouped(E=len(counts), T=T, K=K, N=200, dtype=dtype, seed=31 + integer, counts=counts,
                                   integer=integer)
         announce("grouped skewed dt=%d int=%s T=%d" % (dtype, integer, T))
         out = run_grouped(c)
@@ -220,17 +229,19 @@ def test_grouped_skewed_counts_full(orc, dtype):
 
 def test_grouped_every_config(orc):
     counts = np.array([5, 0, 130, 67, 1])
-    c = inputs.random_grouped(E=5, T=int(counts.sum()), K=72, N=136, dtype=F16, seed=3, counts=counts, integer=True)
-    ref, ref_q = orc.grouped_gemm(c.X, c.W, c.offsets, F16)
-    for cfg in range(mg.mg_num_configs()):
-        announce("grouped cfg=%d" % cfg)
-        mg.mg_set_config(cfg)
-        try:
-            out = run_grouped(c)
-        finally:
-            mg.mg_set_config(-1)
-        assert out.guards_intact()
-        assert_bitexact(out.result(), ref_q, F16, "grouped cfg %d" % cfg)
+    for K in (72, 192):
+        c = inputs.random_grouped(E=5, T=int(counts.sum()), K=K, N=136, dtype=F16, seed=3, counts=counts,
+                                  integer=True)
+        ref, ref_q = orc.grouped_gemm(c.X, c.W, c.offsets, F16)
+        for cfg in range(mg.mg_num_configs()):
+            announce("grouped cfg=%d K=%d" % (cfg, K))
+            mg.mg_set_config(cfg)
+            try:
+                out = run_grouped(c)
+            finally:
+                mg.mg_set_config(-1)
+            assert out.guards_intact()
+            assert_bitexact(out.result(), ref_q, F16, "grouped cfg %d K %d" % (cfg, K))
 
 
 @pytest.mark.parametrize("M,N,K", [(130, 72, 203), (64, 64, 64), (1024, 1024, 2048)])

@@ -32,7 +32,8 @@ class ConfigDesc(ctypes.Structure):
         ("waves_m", ctypes.c_int), ("waves_n", ctypes.c_int), ("stages", ctypes.c_int),
         ("mfma_m", ctypes.c_int), ("mfma_n", ctypes.c_int), ("mfma_k", ctypes.c_int),
         ("group_m", ctypes.c_int), ("xcd_remap", ctypes.c_int), ("lds_bytes", ctypes.c_int),
-        ("name", ctypes.c_char_p),
+        ("direct_lds", ctypes.c_int), ("direct_bk", ctypes.c_int), ("direct_stages", ctypes.c_int),
+        ("direct_lds_bytes", ctypes.c_int), ("name", ctypes.c_char_p),
     ]
 
 

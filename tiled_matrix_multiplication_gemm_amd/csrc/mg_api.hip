@@ -4,10 +4,12 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <type_traits>
 #include <stdint.h>
 
 #include "mi355gemm.h"
 #include "mg_tile.h"
+#include "mg_dlds.h"
 
 namespace {
 
@@ -17,26 +19,42 @@ using namespace mg;
 // One row per compiled tile shape.  The table is static: rows are chosen by
 // shape class in select_config(), which an offline sweep tunes; there is no
 // run-time search.
-using Cfg0 = TileCfg<256, 256, 64, 2, 2>;  // large square problems
+// Each row has a general kernel (register-staged loads, any K and N) and,
+// where BK = 64, a direct-to-LDS fast kernel used when K % 64 == 0 and
+// N % 8 == 0.
+using Cfg0 = TileCfg<256, 256, 64, 2, 4>;  // large square problems, eight waves (two per SIMD)
 using Cfg1 = TileCfg<128, 128, 64, 2, 2>;  // mid-size, grouped
 using Cfg2 = TileCfg<64, 64, 64, 2, 2>;    // small problems: enough tiles to fill 256 CUs
 using Cfg3 = TileCfg<128, 256, 64, 2, 2>;
 using Cfg4 = TileCfg<256, 128, 64, 2, 2>;
 using Cfg5 = TileCfg<128, 128, 32, 2, 2>;
+using Cfg6 = TileCfg<256, 256, 64, 2, 4>;
+// fast kernels: <BM, BN, waves M, waves N, K slice, LDS ring slots>
+using Fast0 = DldsCfg<256, 256, 2, 4, 32, 4>;
+using Fast1 = DldsCfg<128, 128, 2, 2, 64, 3>;
+using Fast2 = DldsCfg<64, 64, 2, 2, 64, 3>;
+using Fast3 = DldsCfg<128, 256, 2, 2, 32, 4>;
+using Fast4 = DldsCfg<256, 128, 2, 2, 32, 4>;
+using Fast6 = DldsCfg<256, 256, 2, 4, 64, 2>;
 
-constexpr int kNumConfigs = 6;
+constexpr int kNumConfigs = 7;
 constexpr int kGroupM = 8;
 
-template <class C>
+template <class C, class F>
 constexpr mg_config_desc describe(int id, const char* name) {
-    return mg_config_desc{id, C::BM, C::BN, C::BK, C::WM, C::WN, C::STAGES, 32, 32, 16, kGroupM, 1, C::LDS_BYTES,
-                          name};
+    if constexpr (std::is_void<F>::value)
+        return mg_config_desc{id, C::BM, C::BN, C::BK, C::WM, C::WN, C::STAGES, 32, 32, 16, kGroupM, 1,
+                              C::LDS_BYTES, 0, 0, 0, 0, name};
+    else
+        return mg_config_desc{id, C::BM, C::BN, C::BK, C::WM, C::WN, C::STAGES, 32, 32, 16, kGroupM, 1,
+                              C::LDS_BYTES, 1, F::BK, F::STAGES, F::LDS_BYTES, name};
 }
 
 const mg_config_desc kTable[kNumConfigs] = {
-    describe<Cfg0>(0, "t256x256k64_w2x2"), describe<Cfg1>(1, "t128x128k64_w2x2"),
-    describe<Cfg2>(2, "t64x64k64_w2x2"),   describe<Cfg3>(3, "t128x256k64_w2x2"),
-    describe<Cfg4>(4, "t256x128k64_w2x2"), describe<Cfg5>(5, "t128x128k32_w2x2"),
+    describe<Cfg0, Fast0>(0, "t256x256_w2x4"), describe<Cfg1, Fast1>(1, "t128x128_w2x2"),
+    describe<Cfg2, Fast2>(2, "t64x64_w2x2"),   describe<Cfg3, Fast3>(3, "t128x256_w2x2"),
+    describe<Cfg4, Fast4>(4, "t256x128_w2x2"), describe<Cfg5, void>(5, "t128x128k32_w2x2"),
+    describe<Cfg6, Fast6>(6, "t256x256_w2x4_k64"),
 };
 
 std::atomic<int> g_forced{-1};
@@ -88,18 +106,38 @@ mg_status launch_cfg(const KArgs& a, int64_t grid, hipStream_t stream) {
     return hipGetLastError() == hipSuccess ? MG_OK : MG_ERR_HIP;
 }
 
-template <class C>
+template <class F, int DT, bool EPI, int MODE>
+mg_status launch_fast(const KArgs& a, int64_t grid, hipStream_t stream) {
+    (void)hipGetLastError();
+    hipLaunchKernelGGL((gemm_dlds_kernel<F, DT, EPI, MODE>), dim3((unsigned)grid), dim3(F::NT), 0, stream, a);
+    return hipGetLastError() == hipSuccess ? MG_OK : MG_ERR_HIP;
+}
+
+template <class C, int DT>
+mg_status launch_general(bool epi, int mode, const KArgs& a, int64_t grid, hipStream_t s) {
+    if (mode == MODE_GROUPED) return launch_cfg<C, DT, false, MODE_GROUPED>(a, grid, s);
+    if (mode == MODE_PACKED_A) return launch_cfg<C, DT, false, MODE_PACKED_A>(a, grid, s);
+    return epi ? launch_cfg<C, DT, true, MODE_DENSE>(a, grid, s) : launch_cfg<C, DT, false, MODE_DENSE>(a, grid, s);
+}
+
+template <class F, int DT>
+mg_status launch_direct(bool epi, int mode, const KArgs& a, int64_t grid, hipStream_t s) {
+    if (mode == MODE_GROUPED) return launch_fast<F, DT, false, MODE_GROUPED>(a, grid, s);
+    return epi ? launch_fast<F, DT, true, MODE_DENSE>(a, grid, s) : launch_fast<F, DT, false, MODE_DENSE>(a, grid, s);
+}
+
+// F = void: the row has no direct-to-LDS kernel.
+template <class C, class F>
 mg_status launch_dt(int dt, bool epi, int mode, const KArgs& a, int64_t grid, hipStream_t s) {
-    if (dt == DT_F16) {
-        if (mode == MODE_GROUPED) return launch_cfg<C, DT_F16, false, MODE_GROUPED>(a, grid, s);
-        if (mode == MODE_PACKED_A) return launch_cfg<C, DT_F16, false, MODE_PACKED_A>(a, grid, s);
-        return epi ? launch_cfg<C, DT_F16, true, MODE_DENSE>(a, grid, s)
-                   : launch_cfg<C, DT_F16, false, MODE_DENSE>(a, grid, s);
+    if constexpr (!std::is_void<F>::value) {
+        const bool direct = mode != MODE_PACKED_A && a.K % F::BK == 0 && a.N % 8 == 0 &&
+                            (int64_t)F::BM * a.lda * 2 < (int64_t)1 << 31 && 64 * a.ldb * 2 < (int64_t)1 << 31;
+        if (direct)
+            return dt == DT_F16 ? launch_direct<F, DT_F16>(epi, mode, a, grid, s)
+                                : launch_direct<F, DT_BF16>(epi, mode, a, grid, s);
     }
-    if (mode == MODE_GROUPED) return launch_cfg<C, DT_BF16, false, MODE_GROUPED>(a, grid, s);
-    if (mode == MODE_PACKED_A) return launch_cfg<C, DT_BF16, false, MODE_PACKED_A>(a, grid, s);
-    return epi ? launch_cfg<C, DT_BF16, true, MODE_DENSE>(a, grid, s)
-               : launch_cfg<C, DT_BF16, false, MODE_DENSE>(a, grid, s);
+    return dt == DT_F16 ? launch_general<C, DT_F16>(epi, mode, a, grid, s)
+                        : launch_general<C, DT_BF16>(epi, mode, a, grid, s);
 }
 
 mg_status launch(int cfg, int dt, bool epi, int mode, KArgs& a, hipStream_t s) {
@@ -119,12 +157,13 @@ mg_status launch(int cfg, int dt, bool epi, int mode, KArgs& a, hipStream_t s) {
     a.xcd_remap = d.xcd_remap;
     mg_status st;
     switch (cfg) {
-        case 0: st = launch_dt<Cfg0>(dt, epi, mode, a, grid, s); break;
-        case 1: st = launch_dt<Cfg1>(dt, epi, mode, a, grid, s); break;
-        case 2: st = launch_dt<Cfg2>(dt, epi, mode, a, grid, s); break;
-        case 3: st = launch_dt<Cfg3>(dt, epi, mode, a, grid, s); break;
-        case 4: st = launch_dt<Cfg4>(dt, epi, mode, a, grid, s); break;
-        case 5: st = launch_dt<Cfg5>(dt, epi, mode, a, grid, s); break;
+        case 0: st = launch_dt<Cfg0, Fast0>(dt, epi, mode, a, grid, s); break;
+        case 1: st = launch_dt<Cfg1, Fast1>(dt, epi, mode, a, grid, s); break;
+        case 2: st = launch_dt<Cfg2, Fast2>(dt, epi, mode, a, grid, s); break;
+        case 3: st = launch_dt<Cfg3, Fast3>(dt, epi, mode, a, grid, s); break;
+        case 4: st = launch_dt<Cfg4, Fast4>(dt, epi, mode, a, grid, s); break;
+        case 5: st = launch_dt<Cfg5, void>(dt, epi, mode, a, grid, s); break;
+        case 6: st = launch_dt<Cfg6, Fast6>(dt, epi, mode, a, grid, s); break;
         default: return MG_ERR_BAD_CONFIG;
     }
     if (st == MG_OK) g_last.store(cfg);

@@ -1,0 +1,358 @@
+// Fast-path tile kernel for gfx950: both operands move global -> LDS with
+// direct 16-byte loads (global_load_lds_dwordx4, no register staging), and the
+// row-major B operand is read out of LDS with the transposing
+// ds_read_b64_tr_b16, so no thread ever shuffles B in registers.
+//
+// One workgroup computes a BM x BN tile; the K loop streams BK = 64 wide
+// slices through two LDS stages (slice i+1 lands while slice i feeds the
+// matrix cores; "Using Triton to optimise GEMM across chips", section 2.2),
+// with XOR-swizzled 16-byte chunks against bank conflicts (FlagOS cross-chip
+// page, section 2.3).
+//
+// Preconditions (checked by the host): K % 64 == 0, N % 8 == 0, and a tile's
+// operand offsets fit in 31 bits (BM * lda and 64 * ldb elements).  Rows past
+// M and column chunks past N are clamped to the last valid ones, so every
+// load is in bounds; what they feed are output rows / columns that are never
+// stored.
+#pragma once
+
+#include "mg_tile.h"
+
+namespace mg {
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4_t;
+
+// One 16-byte direct load per lane: global memory -> LDS at
+// dst + 16 * lane (dst must be the same for the whole wave).
+__device__ __forceinline__ void direct_load16(const void* src, lds_void_t* dst) {
+    __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+
+// Transposing LDS read: within each group of 16 lanes, lane t receives
+// element t of each of the four 16-element rows that lanes 4r .. 4r+3 point at.
+__device__ __forceinline__ i16x4 lds_read_tr16(const char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p);
+}
+
+template <int BM_, int BN_, int WM_, int WN_, int BK_ = 64, int R_ = 2>
+struct DldsCfg {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
+    static constexpr int R = R_;                        // LDS slots in the ring (= slices in flight + 1)
+    static constexpr int NW = WM * WN;                  // waves per workgroup
+    static constexpr int NT = NW * 64;
+    static constexpr int WTM = BM / WM, WTN = BN / WN;  // output of one wave
+    static constexpr int FM = WTM / 32, FN = WTN / 32;  // 32x32 MFMA tiles per wave
+    static constexpr int STEPS = BK / 16;               // k16 MFMA steps per slice
+    static constexpr int AROW = BK * 2;                 // bytes of one A row in LDS
+    static constexpr int ACH = BK / 8;                  // 16-byte chunks per A row
+    static constexpr int A_BYTES = BM * AROW;           // one slice of A
+    static constexpr int B_BYTES = BK * BN * 2;         // one slice of B: BK k-rows of 2*BN bytes
+    static constexpr int SLOT = A_BYTES + B_BYTES;
+    static constexpr int JA = A_BYTES / 1024 / NW;      // 1 KB direct loads per wave per slice
+    static constexpr int JB = B_BYTES / 1024 / NW;
+    static constexpr int STAGES = R;
+    static constexpr int LDS_BYTES = R * SLOT;
+    static constexpr int BCH = BN / 8;                  // 16-byte chunks per B k-row
+    static_assert(BK == 32 || BK == 64, "K slice must be 32 or 64");
+    static_assert(R >= 2 && R <= 8, "ring of 2..8 slots");
+    static_assert(JA * NW * 1024 == A_BYTES && JB * NW * 1024 == B_BYTES, "slice must split evenly over waves");
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32x32");
+    static_assert(LDS_BYTES <= 160 * 1024, "gfx950 has 160 KB of LDS per CU");
+};
+
+// Chunk swizzles, chosen so that the 16 lanes served per LDS cycle hit 16
+// distinct 16-byte bank groups.  A: the MFMA operand read takes one chunk
+// column of 32 consecutive rows (rows of 64 or 128 bytes).  B: k-rows are
+// 2*BN bytes; a transposing read takes 32-byte pieces of 4 consecutive
+// k-rows at the same columns.
+template <int ACH>
+__device__ __forceinline__ int swz_a(int row) {
+    if constexpr (ACH == 8) return (row ^ (row >> 3)) & 7;
+    else return (row >> 2) & 3;
+}
+template <int BCH>
+__device__ __forceinline__ int swz_b(int krow) { return (4 * (krow & 3)) & (BCH - 1); }
+
+// s_waitcnt vmcnt(N): wait until at most N vector memory operations of this
+// wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit count");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier for the LDS ring.  Unlike __syncthreads() it does not
+// drain this wave's outstanding global->LDS loads (a release fence would
+// wait for all of them, emptying the ring at every slice); each wave waits
+// for exactly the loads it needs with wait_vmcnt before calling it.  Its own
+// LDS reads are completed first, so that once every wave has passed, no read
+// of a slot can still be in flight when new loads are issued into it.  The
+// memory clobbers keep the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void ring_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// One LDS ring slot: a distinct shared-memory object per (slot index, kernel).
+template <class Cfg, int DT, bool EPI, int MODE>
+struct DldsTag {};
+template <int BYTES, int I, class Tag>
+__device__ __forceinline__ char* lds_slot() {
+    __shared__ __attribute__((aligned(1024))) char buf[BYTES];
+    return buf;
+}
+
+template <class Cfg, int DT, bool EPI, int MODE>
+__global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;
+    constexpr int FM = Cfg::FM, FN = Cfg::FN, JA = Cfg::JA, JB = Cfg::JB, BCH = Cfg::BCH;
+    constexpr int ACH = Cfg::ACH, AROW = Cfg::AROW, STEPS = Cfg::STEPS, R = Cfg::R;
+    // R ring slots of [A slice | B slice], each its own LDS object so that the
+    // compiler can tell reads of one slot from direct loads landing in another
+    // (a single array would make it wait for every load in flight before each
+    // LDS read).
+    using Tag = DldsTag<Cfg, DT, EPI, MODE>;
+    auto slot_ptr = [&](int i) -> char* {  // i is a compile-time constant at every use
+        switch (i) {
+            case 0: return lds_slot<Cfg::SLOT, 0, Tag>();
+            case 1: return lds_slot<Cfg::SLOT, 1, Tag>();
+            case 2: if constexpr (R > 2) return lds_slot<Cfg::SLOT, 2, Tag>(); else return nullptr;
+            case 3: if constexpr (R > 3) return lds_slot<Cfg::SLOT, 3, Tag>(); else return nullptr;
+            case 4: if constexpr (R > 4) return lds_slot<Cfg::SLOT, 4, Tag>(); else return nullptr;
+            case 5: if constexpr (R > 5) return lds_slot<Cfg::SLOT, 5, Tag>(); else return nullptr;
+            case 6: if constexpr (R > 6) return lds_slot<Cfg::SLOT, 6, Tag>(); else return nullptr;
+            default: if constexpr (R > 7) return lds_slot<Cfg::SLOT, 7, Tag>(); else return nullptr;
+        }
+    };
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
+
+    // ---- which tile (same order as the general kernel) --------------------
+    int logical = args.xcd_remap ? xcd_logical(blockIdx.x, gridDim.x) : (int)blockIdx.x;
+    const uint16_t* Ag = args.A;
+    const uint16_t* Bg = args.B;
+    uint16_t* Cg = args.C;
+    int64_t M = args.M;
+    int pm, pn;
+    if constexpr (MODE == MODE_GROUPED) {
+        const int T = (int)args.M;
+        auto segment = [&](int e, int& r0, int& rows) {
+            int a = args.offsets[e], b = args.offsets[e + 1];
+            a = a < 0 ? 0 : (a > T ? T : a);
+            b = b < a ? a : (b > T ? T : b);
+            r0 = a;
+            rows = b - a;
+        };
+        int G = 0;
+        for (int e = 0; e < args.E; ++e) {
+            int r0, rows;
+            segment(e, r0, rows);
+            G += (rows + BM - 1) / BM;
+        }
+        if (logical >= G * args.tiles_n) return;
+        const int g = logical % G;
+        pn = logical / G;
+        int e = 0, cum = 0, r0 = 0, rows = 0;
+        for (; e < args.E; ++e) {
+            segment(e, r0, rows);
+            const int t = (rows + BM - 1) / BM;
+            if (g < cum + t) break;
+            cum += t;
+        }
+        if (e >= args.E) return;
+        pm = g - cum;
+        M = rows;
+        Ag += (int64_t)r0 * args.lda;
+        Bg += (int64_t)e * args.stride_we;
+        Cg += (int64_t)r0 * args.ldc;
+    } else {
+        grouped_order(logical, args.tiles_m, args.tiles_n, args.group_m, pm, pn);
+    }
+    const int64_t N = args.N, K = args.K;
+    const int64_t m0 = (int64_t)pm * BM, n0 = (int64_t)pn * BN;
+    const int nk = (int)(K / BK);
+
+    // ---- per-lane source offsets of the direct loads ---------------------
+    // Offsets are 32-bit byte offsets from a workgroup-uniform base that
+    // advances by one k-slice per step (the host guarantees they fit).
+    // A: load q = wave*JA + j fills bytes [q KB, q KB + 1 KB) of a slice,
+    //    i.e. 1024/AROW rows; lane L lands in row q*1024/AROW + L/ACH, physical
+    //    chunk L%ACH, and therefore fetches logical chunk (L%ACH) ^ swz_a(row).
+    uint32_t offA_g[JA];
+#pragma unroll
+    for (int j = 0; j < JA; ++j) {
+        const int q = wave * JA + j;
+        const int row = q * (1024 / AROW) + lane / ACH;
+        const int c = (lane % ACH) ^ swz_a<ACH>(row);
+        const int64_t r = (m0 + row < M ? row : M - 1 - m0);
+        offA_g[j] = (uint32_t)((r * args.lda + 8 * c) * 2);
+    }
+    // B: load q covers k-rows (512/BN) q .. ; lane L lands in k-row
+    //    q*512/BN + 8L/BN, physical chunk L % BCH.
+    uint32_t offB_g[JB];
+#pragma unroll
+    for (int j = 0; j < JB; ++j) {
+        const int q = wave * JB + j;
+        const int krow = q * (512 / BN) + (8 * lane) / BN;
+        const int c = (lane % BCH) ^ swz_b<BCH>(krow);
+        const int64_t cn = (n0 + 8 * c <= N - 8) ? 8 * c : N - 8 - n0;
+        offB_g[j] = (uint32_t)((krow * args.ldb + cn) * 2);
+    }
+    const char* baseA = (const char*)(Ag + m0 * args.lda);
+    const char* baseB = (const char*)(Bg + n0);
+    const int64_t stepA = (int64_t)BK * 2;              // bytes per k-slice
+    const int64_t stepB = (int64_t)BK * args.ldb * 2;
+
+    // direct loads of k-slice kt into ring slot `slot` (a compile-time index)
+    auto issue = [&](int kt, int slot) {
+        const char* a = baseA + kt * stepA;
+        const char* b = baseB + kt * stepB;
+        char* sa = slot_ptr(slot);
+        char* sb = sa + Cfg::A_BYTES;
+#pragma unroll
+        for (int j = 0; j < JA; ++j)
+            direct_load16(a + offA_g[j], (lds_void_t*)(sa + (wave * JA + j) * 1024));
+#pragma unroll
+        for (int j = 0; j < JB; ++j)
+            direct_load16(b + offB_g[j], (lds_void_t*)(sb + (wave * JB + j) * 1024));
+    };
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    // ---- operand fragments ------------------------------------------------
+    // Fragments of one k16 step: FM A fragments (ds_read_b128 of one swizzled
+    // chunk of 32 rows) and FN B fragments (two transposing reads each).
+    // Two register sets alternate so that the reads of step s+1 are in flight
+    // while the MFMAs of step s issue.
+    const int rowA0 = wm * Cfg::WTM + (lane & 31);
+    const int g16 = lane >> 4, t16 = lane & 15;
+    int offBj[FN];  // byte offset of this lane's B piece in k-row (t16 >> 2), per n fragment
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        const int n = wn * Cfg::WTN + j * 32 + 16 * (g16 & 1) + 4 * (t16 & 3);
+        const int kr = 8 * (g16 >> 1) + (t16 >> 2);  // swizzle only depends on kr & 3
+        offBj[j] = kr * (2 * BN) + ((n >> 3) ^ swz_b<BCH>(kr)) * 16 + (n & 7) * 2;
+    }
+    struct Frags {
+        u32x4 a[FM], b[FN];
+    };
+    auto read_frags = [&](Frags& f, int slot, int s) {
+        const char* sa = slot_ptr(slot);
+        const char* sb = sa + Cfg::A_BYTES;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int row = rowA0 + i * 32;
+            const int c = (2 * s + (lane >> 5)) ^ swz_a<ACH>(row);
+            f.a[i] = *(const lds_u32x4_t*)(sa + row * AROW + c * 16);
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            // k-rows 16s + {0..3} and 16s + {4..7} (+8 for the upper half-wave)
+            const i16x4 lo = lds_read_tr16(sb + offBj[j] + (16 * s) * (2 * BN));
+            const i16x4 hi = lds_read_tr16(sb + offBj[j] + (16 * s + 4) * (2 * BN));
+            f.b[j] = u32x4{__builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 0, 1)),
+                           __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 2, 3)),
+                           __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 0, 1)),
+                           __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 2, 3))};
+        }
+    };
+    auto mfma_step = [&](const Frags& f) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<DT>(f.a[i], f.b[j], acc[i][j]);
+    };
+    // Interleave the next step's LDS reads (FM + 2 FN instructions) with this
+    // step's MFMAs (FM * FN instructions), one read after each MFMA.
+    auto interleave = [&]() {
+        constexpr int R = FM + 2 * FN, Q = FM * FN;
+#pragma unroll
+        for (int q = 0; q < (R < Q ? R : Q); ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
+        }
+        if constexpr (Q > R) __builtin_amdgcn_sched_group_barrier(0x008, Q - R, 0);
+        if constexpr (R > Q) __builtin_amdgcn_sched_group_barrier(0x100, R - Q, 0);
+    };
+
+    // ---- main loop over k-slices -------------------------------------------
+    // Ring of R LDS slots; slice t lives in slot t % R.  Within slice t the
+    // fragments of step s+1 are read while the MFMAs of step s issue.  In the
+    // last step the wave waits for its own loads of slice t+1, the workgroup
+    // synchronises (slice t+1 complete everywhere, every read of slice t
+    // done), slice t+R is issued into slice t's slot, and the first
+    // fragments of slice t+1 are read under the last step's MFMAs.  Up to
+    // R-1 slices are in flight while one is consumed.
+    if (nk > 0) {
+        constexpr int L = JA + JB;  // loads per wave per slice
+        Frags F0, F1;
+        const int pre = nk < R ? nk : R;
+        for (int t = 0; t < pre; ++t) issue(t, t);
+        if (pre == R) wait_vmcnt<L * (R - 1)>();  // slice 0 landed, R-1 slices still in flight
+        else wait_vmcnt<0>();
+        ring_barrier();
+        read_frags(F0, 0, 0);
+        // trips of R slices; slice t = trip + u sits in slot u
+        for (int trip = 0; trip < nk; trip += R) {
+#pragma unroll
+            for (int u = 0; u < R; ++u) {
+                const int t = trip + u;
+                if (t >= nk) break;
+#pragma unroll
+                for (int s = 0; s < STEPS; ++s) {
+                    Frags& cur = (s & 1) ? F1 : F0;
+                    Frags& nxt = (s & 1) ? F0 : F1;
+                    if (s + 1 < STEPS) {
+                        read_frags(nxt, u, s + 1);
+                    } else {
+                        // slices issued so far: 0 .. min(t-1+R, nk-1); in steady state
+                        // the R-2 slices after t+1 stay in flight, near the end wait for all
+                        if (t - 1 + R <= nk - 1) wait_vmcnt<L * (R - 2)>();
+                        else wait_vmcnt<0>();
+                        ring_barrier();
+                        if (t + R < nk) issue(t + R, u);
+                        if (t + 1 < nk) read_frags(nxt, (u + 1) % R, 0);
+                    }
+                    mfma_step(cur);
+                    interleave();
+                }
+            }
+        }
+    }
+
+    // ---- epilogue: (bias, ReLU), one rounding, masked stores --------------
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        const int64_t col = n0 + wn * Cfg::WTN + j * 32 + (lane & 31);
+        float bj = 0.0f;
+        if constexpr (EPI) bj = (col < N) ? to_float<DT>(args.bias[col]) : 0.0f;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t row = m0 + wm * Cfg::WTM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                float v = acc[i][j][r];
+                if constexpr (EPI) {
+                    v = v + bj;
+                    v = (v > 0.0f) ? v : 0.0f;
+                }
+                if (row < M && col < N) Cg[row * args.ldc + col] = from_float<DT>(v);
+            }
+        }
+    }
+}
+
+}  // namespace mg
