@@ -42,7 +42,43 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-also", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the CPU-baseline sample")
+    ap.add_argument("--pmc-probe", action="store_true",
+                    help="for counter collection: one GEMM, a plain copy of known size, one GEMM; no timing")
     return ap.parse_args()
+
+
+def pmc_probe(name):
+    """GEMM, then an elementwise copy reading and writing COPY_BYTES, then GEMM.
+    Under rocprofv3 --pmc the copy calibrates FETCH_SIZE / WRITE_SIZE."""
+    import torch
+
+    from tiled_matrix_multiplication_gemm_amd import profiling
+
+    c, fn = dense_setup(name)
+    fn()
+    torch.cuda.synchronize()
+    n = profiling.COPY_BYTES // 2
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    fn()
+    torch.cuda.synchronize()
+    print("pmc probe done: %s" % name)
+
+
+def stored_traffic(name):
+    """HBM bytes per dispatch from the committed counter summary, if it was
+    taken on the current kernel sources (else None)."""
+    from tiled_matrix_multiplication_gemm_amd import profiling
+
+    path = os.path.join(ROOT, "profiles", "%s_traffic.txt" % name)
+    if not os.path.exists(path):
+        return None
+    s = profiling.read_summary(path)
+    if s.get("source_hash") != profiling.source_hash():
+        return None
+    return float(s["traffic_bytes"])
 
 
 def upload(bits, dt):
@@ -159,6 +195,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     mg.lib()
+    if args.pmc_probe:
+        pmc_probe(args.workload)
+        return
 
     main_res = measure_dense(args.workload, args.steps, args.warmup)
     c = main_res["case"]
@@ -181,7 +220,8 @@ def main():
                    "layout": "row-major A[M,K], B[K,N]", "accumulate": "fp32",
                    "tile_config": main_res["tile_config"]},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_MFMA_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_MFMA_TFLOPS, 4), "traffic": stored_traffic(args.workload),
+                     "compulsory_bytes": main_res["compulsory_bytes"],
                      "kernel_ms_mean": round(main_res["kernel_ms"], 4),
                      "kernel_ms_median": round(main_res["kernel_ms_median"], 4),
                      "kernel": "gemm_tile_kernel (%s)" % main_res["tile_config"]},
