@@ -147,6 +147,8 @@ typedef struct {
     int direct_bk;            /* K slice of the direct-to-LDS kernel       */
     int direct_stages;        /* LDS ring slots of the direct kernel       */
     int direct_lds_bytes;     /* shared memory of the direct kernel        */
+    int direct_ksplit;        /* waves that split K inside the workgroup,
+                                 each with its own LDS ring (1: none)      */
     const char* name;
 } mg_config_desc;
 

@@ -127,7 +127,10 @@ def test_config_table(L):
         assert acc <= 256
         if d["direct_lds"]:
             assert d["direct_bk"] in (32, 64) and d["direct_stages"] >= 2
-            assert d["direct_lds_bytes"] == layout.lds_bytes(d["bm"], d["bn"], d["direct_bk"], 2, d["direct_stages"])
+            # one ring per wave when the waves split K
+            assert d["direct_ksplit"] >= 1
+            assert d["direct_lds_bytes"] == d["direct_ksplit"] * layout.lds_bytes(d["bm"], d["bn"], d["direct_bk"], 2,
+                                                                                 d["direct_stages"])
             assert d["direct_lds_bytes"] <= 160 * 1024
     with pytest.raises(RuntimeError):
         mg.mg_config_info(n)

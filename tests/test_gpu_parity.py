@@ -77,8 +77,9 @@ def check_full(orc, case, cfg=-1, **kw):
 # (K % 64 == 0, N % 8 == 0) with ragged M and N edges
 SMALL = [(1, 1, 1), (7, 33, 129), (33, 7, 1000), (129, 129, 33), (65, 200, 72),
          (300, 257, 130), (1000, 7, 33), (256, 384, 200), (513, 129, 257),
-         (64, 64, 64), (1, 8, 64), (65, 200, 128), (129, 136, 64), (300, 264, 192), (513, 520, 256)]
-NUM_CONFIGS = 7
+         (64, 64, 64), (1, 8, 64), (65, 200, 128), (129, 136, 64), (300, 264, 192), (513, 520, 256),
+         (70, 72, 32), (96, 40, 96)]
+NUM_CONFIGS = 8
 
 
 def test_config_count_matches_library():

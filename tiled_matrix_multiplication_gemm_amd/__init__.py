@@ -33,7 +33,7 @@ class ConfigDesc(ctypes.Structure):
         ("mfma_m", ctypes.c_int), ("mfma_n", ctypes.c_int), ("mfma_k", ctypes.c_int),
         ("group_m", ctypes.c_int), ("xcd_remap", ctypes.c_int), ("lds_bytes", ctypes.c_int),
         ("direct_lds", ctypes.c_int), ("direct_bk", ctypes.c_int), ("direct_stages", ctypes.c_int),
-        ("direct_lds_bytes", ctypes.c_int), ("name", ctypes.c_char_p),
+        ("direct_lds_bytes", ctypes.c_int), ("direct_ksplit", ctypes.c_int), ("name", ctypes.c_char_p),
     ]
 
 

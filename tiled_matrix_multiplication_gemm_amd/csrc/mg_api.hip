@@ -10,6 +10,7 @@
 #include "mi355gemm.h"
 #include "mg_tile.h"
 #include "mg_dlds.h"
+#include "mg_kslab.h"
 
 namespace {
 
@@ -36,25 +37,35 @@ using Fast2 = DldsCfg<64, 64, 2, 2, 64, 3>;
 using Fast3 = DldsCfg<128, 256, 2, 2, 32, 4>;
 using Fast4 = DldsCfg<256, 128, 2, 2, 32, 4>;
 using Fast6 = DldsCfg<256, 256, 2, 4, 64, 2>;
+using Cfg7 = TileCfg<64, 64, 64, 2, 2>;
+using Fast7 = SlabCfg<64, 64, 4, 32, 4>;  // K split over the 4 waves of the workgroup
 
-constexpr int kNumConfigs = 7;
+constexpr int kNumConfigs = 8;
 constexpr int kGroupM = 8;
+
+template <class F>
+struct is_slab : std::false_type {};
+template <int BM, int BN, int NW, int BK, int RW>
+struct is_slab<SlabCfg<BM, BN, NW, BK, RW>> : std::true_type {};
 
 template <class C, class F>
 constexpr mg_config_desc describe(int id, const char* name) {
     if constexpr (std::is_void<F>::value)
         return mg_config_desc{id, C::BM, C::BN, C::BK, C::WM, C::WN, C::STAGES, 32, 32, 16, kGroupM, 1,
-                              C::LDS_BYTES, 0, 0, 0, 0, name};
+                              C::LDS_BYTES, 0, 0, 0, 0, 0, name};
+    else if constexpr (is_slab<F>::value)
+        return mg_config_desc{id, C::BM, C::BN, C::BK, C::WM, C::WN, C::STAGES, 32, 32, 16, kGroupM, 1,
+                              C::LDS_BYTES, 1, F::BK, F::STAGES, F::LDS_BYTES, F::NW, name};
     else
         return mg_config_desc{id, C::BM, C::BN, C::BK, C::WM, C::WN, C::STAGES, 32, 32, 16, kGroupM, 1,
-                              C::LDS_BYTES, 1, F::BK, F::STAGES, F::LDS_BYTES, name};
+                              C::LDS_BYTES, 1, F::BK, F::STAGES, F::LDS_BYTES, 1, name};
 }
 
 const mg_config_desc kTable[kNumConfigs] = {
-    describe<Cfg0, Fast0>(0, "t256x256_w2x4"), describe<Cfg1, Fast1>(1, "t128x128_w2x2"),
+    describe<Cfg0, Fast0>(0, "t256x256_w2x4_k32r4"), describe<Cfg1, Fast1>(1, "t128x128_w2x2"),
     describe<Cfg2, Fast2>(2, "t64x64_w2x2"),   describe<Cfg3, Fast3>(3, "t128x256_w2x2"),
     describe<Cfg4, Fast4>(4, "t256x128_w2x2"), describe<Cfg5, void>(5, "t128x128k32_w2x2"),
-    describe<Cfg6, Fast6>(6, "t256x256_w2x4_k64"),
+    describe<Cfg6, Fast6>(6, "t256x256_w2x4_k64r2"), describe<Cfg7, Fast7>(7, "t64x64_ksplit4"),
 };
 
 std::atomic<int> g_forced{-1};
@@ -62,14 +73,22 @@ std::atomic<int> g_last{-1};
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Shape classes, from the offline sweep (per-row timings on MI355X for the
+// 8192^3, 1024x1024x2048 and grouped MoE workloads):
+//  - grouped MoE: 256x256 tiles, eight waves (each expert's weight slab is
+//    read by one or two tiles);
+//  - enough 256x256 tiles to fill the chip several times: row 0;
+//  - outputs with fewer than 256 tiles of 128x128: 64x64 tiles with K split
+//    over the waves of a workgroup (row 7);
+//  - in between: 128x128 tiles.
 int select_config(int64_t M, int64_t N, int64_t K, int grouped) {
     (void)K;
     int forced = g_forced.load();
     if (forced >= 0) return forced;
-    if (grouped) return 1;
+    if (grouped) return 0;
     if (cdiv(M, 256) * cdiv(N, 256) >= 512) return 0;
     if (cdiv(M, 128) * cdiv(N, 128) >= 256) return 1;
-    return 2;
+    return 7;
 }
 
 // ---- validation --------------------------------------------------------------
@@ -120,17 +139,31 @@ mg_status launch_general(bool epi, int mode, const KArgs& a, int64_t grid, hipSt
     return epi ? launch_cfg<C, DT, true, MODE_DENSE>(a, grid, s) : launch_cfg<C, DT, false, MODE_DENSE>(a, grid, s);
 }
 
+template <class F, int DT, bool EPI>
+mg_status launch_slab(const KArgs& a, int64_t grid, hipStream_t stream) {
+    (void)hipGetLastError();
+    hipLaunchKernelGGL((gemm_kslab_kernel<F, DT, EPI>), dim3((unsigned)grid), dim3(F::NT), 0, stream, a);
+    return hipGetLastError() == hipSuccess ? MG_OK : MG_ERR_HIP;
+}
+
 template <class F, int DT>
 mg_status launch_direct(bool epi, int mode, const KArgs& a, int64_t grid, hipStream_t s) {
-    if (mode == MODE_GROUPED) return launch_fast<F, DT, false, MODE_GROUPED>(a, grid, s);
-    return epi ? launch_fast<F, DT, true, MODE_DENSE>(a, grid, s) : launch_fast<F, DT, false, MODE_DENSE>(a, grid, s);
+    if constexpr (is_slab<F>::value) {
+        (void)mode;
+        return epi ? launch_slab<F, DT, true>(a, grid, s) : launch_slab<F, DT, false>(a, grid, s);
+    } else {
+        if (mode == MODE_GROUPED) return launch_fast<F, DT, false, MODE_GROUPED>(a, grid, s);
+        return epi ? launch_fast<F, DT, true, MODE_DENSE>(a, grid, s)
+                   : launch_fast<F, DT, false, MODE_DENSE>(a, grid, s);
+    }
 }
 
 // F = void: the row has no direct-to-LDS kernel.
 template <class C, class F>
 mg_status launch_dt(int dt, bool epi, int mode, const KArgs& a, int64_t grid, hipStream_t s) {
     if constexpr (!std::is_void<F>::value) {
-        const bool direct = mode != MODE_PACKED_A && a.K % F::BK == 0 && a.N % 8 == 0 &&
+        const bool direct = mode != MODE_PACKED_A && !(is_slab<F>::value && mode == MODE_GROUPED) &&
+                            a.K % F::BK == 0 && a.N % 8 == 0 &&
                             (int64_t)F::BM * a.lda * 2 < (int64_t)1 << 31 && 64 * a.ldb * 2 < (int64_t)1 << 31;
         if (direct)
             return dt == DT_F16 ? launch_direct<F, DT_F16>(epi, mode, a, grid, s)
@@ -164,6 +197,7 @@ mg_status launch(int cfg, int dt, bool epi, int mode, KArgs& a, hipStream_t s) {
         case 4: st = launch_dt<Cfg4, Fast4>(dt, epi, mode, a, grid, s); break;
         case 5: st = launch_dt<Cfg5, void>(dt, epi, mode, a, grid, s); break;
         case 6: st = launch_dt<Cfg6, Fast6>(dt, epi, mode, a, grid, s); break;
+        case 7: st = launch_dt<Cfg7, Fast7>(dt, epi, mode, a, grid, s); break;
         default: return MG_ERR_BAD_CONFIG;
     }
     if (st == MG_OK) g_last.store(cfg);

@@ -333,7 +333,11 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
         }
     }
 
-    // ---- epilogue: (bias, ReLU), one rounding, masked stores --------------
+    // ---- epilogue: (bias, ReLU), one rounding, stores -------------------
+    // One 32x32 MFMA tile at a time (a scheduling barrier keeps the compiler
+    // from pulling every accumulator out of the AGPRs at once); interior tiles
+    // store without bounds checks.
+    const bool interior = (m0 + BM <= M) && (n0 + BN <= N);
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
         const int64_t col = n0 + wn * Cfg::WTN + j * 32 + (lane & 31);
@@ -341,15 +345,18 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
         if constexpr (EPI) bj = (col < N) ? to_float<DT>(args.bias[col]) : 0.0f;
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
+            __builtin_amdgcn_sched_barrier(0);
+            const int64_t row0 = m0 + wm * Cfg::WTM + i * 32 + 4 * (lane >> 5);
+            uint16_t* cp = Cg + row0 * args.ldc + col;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int64_t row = m0 + wm * Cfg::WTM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                const int dr = 8 * (r >> 2) + (r & 3);
                 float v = acc[i][j][r];
                 if constexpr (EPI) {
                     v = v + bj;
                     v = (v > 0.0f) ? v : 0.0f;
                 }
-                if (row < M && col < N) Cg[row * args.ldc + col] = from_float<DT>(v);
+                if (interior || (row0 + dr < M && col < N)) cp[dr * args.ldc] = from_float<DT>(v);
             }
         }
     }
