@@ -31,12 +31,12 @@ using Cfg4 = TileCfg<256, 128, 64, 2, 2>;
 using Cfg5 = TileCfg<128, 128, 32, 2, 2>;
 using Cfg6 = TileCfg<256, 256, 64, 2, 4>;
 // fast kernels: <BM, BN, waves M, waves N, K slice, LDS ring slots>
-using Fast0 = DldsCfg<256, 256, 2, 4, 32, 4>;
+using Fast0 = DldsCfg<256, 256, 2, 4, 32, 5>;
 using Fast1 = DldsCfg<128, 128, 2, 2, 64, 3>;
 using Fast2 = DldsCfg<64, 64, 2, 2, 64, 3>;
 using Fast3 = DldsCfg<128, 256, 2, 2, 32, 4>;
 using Fast4 = DldsCfg<256, 128, 2, 2, 32, 4>;
-using Fast6 = DldsCfg<256, 256, 2, 4, 64, 2>;
+using Fast6 = DldsCfg<256, 256, 2, 2, 32, 5>;
 using Cfg7 = TileCfg<64, 64, 64, 2, 2>;
 using Fast7 = SlabCfg<64, 64, 4, 32, 4>;  // K split over the 4 waves of the workgroup
 
@@ -62,10 +62,10 @@ constexpr mg_config_desc describe(int id, const char* name) {
 }
 
 const mg_config_desc kTable[kNumConfigs] = {
-    describe<Cfg0, Fast0>(0, "t256x256_w2x4_k32r4"), describe<Cfg1, Fast1>(1, "t128x128_w2x2"),
+    describe<Cfg0, Fast0>(0, "t256x256_w2x4_k32r5"), describe<Cfg1, Fast1>(1, "t128x128_w2x2"),
     describe<Cfg2, Fast2>(2, "t64x64_w2x2"),   describe<Cfg3, Fast3>(3, "t128x256_w2x2"),
     describe<Cfg4, Fast4>(4, "t256x128_w2x2"), describe<Cfg5, void>(5, "t128x128k32_w2x2"),
-    describe<Cfg6, Fast6>(6, "t256x256_w2x4_k64r2"), describe<Cfg7, Fast7>(7, "t64x64_ksplit4"),
+    describe<Cfg6, Fast6>(6, "t256x256_w2x2_k32r5"), describe<Cfg7, Fast7>(7, "t64x64_ksplit4"),
 };
 
 std::atomic<int> g_forced{-1};

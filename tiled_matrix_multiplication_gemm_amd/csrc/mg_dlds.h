@@ -16,6 +16,8 @@
 // stored.
 #pragma once
 
+#include <type_traits>
+
 #include "mg_tile.h"
 
 namespace mg {
@@ -40,7 +42,7 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const char* p) {
 template <int BM_, int BN_, int WM_, int WN_, int BK_ = 64, int R_ = 2>
 struct DldsCfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
-    static constexpr int R = R_;                        // LDS slots in the ring (= slices in flight + 1)
+    static constexpr int R = R_;                        // LDS slots in the ring (= slices in flight + 2)
     static constexpr int NW = WM * WN;                  // waves per workgroup
     static constexpr int NT = NW * 64;
     static constexpr int WTM = BM / WM, WTN = BN / WN;  // output of one wave
@@ -57,7 +59,7 @@ struct DldsCfg {
     static constexpr int LDS_BYTES = R * SLOT;
     static constexpr int BCH = BN / 8;                  // 16-byte chunks per B k-row
     static_assert(BK == 32 || BK == 64, "K slice must be 32 or 64");
-    static_assert(R >= 2 && R <= 8, "ring of 2..8 slots");
+    static_assert(R >= 3 && R <= 8, "ring of 3..8 slots");
     static_assert(JA * NW * 1024 == A_BYTES && JB * NW * 1024 == B_BYTES, "slice must split evenly over waves");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32x32");
     static_assert(LDS_BYTES <= 160 * 1024, "gfx950 has 160 KB of LDS per CU");
@@ -87,12 +89,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 // Workgroup barrier for the LDS ring.  Unlike __syncthreads() it does not
 // drain this wave's outstanding global->LDS loads (a release fence would
 // wait for all of them, emptying the ring at every slice); each wave waits
-// for exactly the loads it needs with wait_vmcnt before calling it.  Its own
-// LDS reads are completed first, so that once every wave has passed, no read
-// of a slot can still be in flight when new loads are issued into it.  The
-// memory clobbers keep the compiler from moving LDS accesses across it.
+// for exactly the loads it needs with wait_vmcnt before calling it.  Nor
+// does it wait for this wave's LDS reads: the slot refilled after it is one
+// whose reads every wave has already consumed (below).  The memory clobbers
+// keep the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void ring_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
@@ -276,59 +278,89 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
             for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<DT>(f.a[i], f.b[j], acc[i][j]);
     };
     // Interleave the next step's LDS reads (FM + 2 FN instructions) with this
-    // step's MFMAs (FM * FN instructions), one read after each MFMA.
-    auto interleave = [&]() {
-        constexpr int R = FM + 2 * FN, Q = FM * FN;
+    // step's MFMAs (FM * FN instructions): two reads after each of the first
+    // MFMAs, so that every read has several MFMAs' time to land before the
+    // step ends.  Reads issued back to back in front of the MFMAs, or spread
+    // to the end of the step, leave the matrix core idle.  In the step that
+    // refills the ring, the NL direct loads are spread the same way, one per
+    // MFMA: issued as one burst, they back up in the address unit and stall
+    // the issuing waves.
+    auto interleave = [&](auto nl) {
+        constexpr int NL = decltype(nl)::value;
+        constexpr int NR = FM + 2 * FN, Q = FM * FN;
+        constexpr int PAIRS = (NR + 1) / 2 < Q ? (NR + 1) / 2 : Q;
 #pragma unroll
-        for (int q = 0; q < (R < Q ? R : Q); ++q) {
+        for (int q = 0; q < Q; ++q) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
+            if (q < PAIRS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two DS reads
+            if (q < NL) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one direct load
         }
-        if constexpr (Q > R) __builtin_amdgcn_sched_group_barrier(0x008, Q - R, 0);
-        if constexpr (R > Q) __builtin_amdgcn_sched_group_barrier(0x100, R - Q, 0);
+        if constexpr (NR > 2 * PAIRS) __builtin_amdgcn_sched_group_barrier(0x100, NR - 2 * PAIRS, 0);
+        if constexpr (NL > Q) __builtin_amdgcn_sched_group_barrier(0x020, NL - Q, 0);
     };
 
     // ---- main loop over k-slices -------------------------------------------
     // Ring of R LDS slots; slice t lives in slot t % R.  Within slice t the
     // fragments of step s+1 are read while the MFMAs of step s issue.  In the
     // last step the wave waits for its own loads of slice t+1, the workgroup
-    // synchronises (slice t+1 complete everywhere, every read of slice t
-    // done), slice t+R is issued into slice t's slot, and the first
-    // fragments of slice t+1 are read under the last step's MFMAs.  Up to
-    // R-1 slices are in flight while one is consumed.
+    // synchronises (slice t+1 complete everywhere), slice t+R-1 is issued into
+    // the slot of slice t-1, and the first fragments of slice t+1 are read
+    // under the last step's MFMAs.  Every read of slice t-1 was consumed by an
+    // MFMA of slice t-1, before the barrier, so no wave needs to drain its
+    // LDS reads at the barrier.  Up to R-2 slices are in flight while one is
+    // consumed.
+    //
+    // Trips of R slices (slice trip + u in slot u, u a compile-time index).
+    // While every slice of a trip still has a slice t + R - 1 to issue, the
+    // trip is one straight-line block with constant waits, which lets the
+    // scheduler interleave reads and MFMAs across the slice boundary; the
+    // last trips take the general form with run-time conditions.
+    constexpr int L = JA + JB;  // loads per wave per slice
+    Frags F0, F1;
+    auto slice = [&](const int t, const int u, const bool steady) {
+#pragma unroll
+        for (int s = 0; s < STEPS; ++s) {
+            Frags& cur = (s & 1) ? F1 : F0;
+            Frags& nxt = (s & 1) ? F0 : F1;
+            if (s + 1 < STEPS) {
+                read_frags(nxt, u, s + 1);
+            } else if (steady) {
+                wait_vmcnt<L * (R - 3)>();
+                ring_barrier();
+                issue(t + R - 1, (u + R - 1) % R);
+                read_frags(nxt, (u + 1) % R, 0);
+            } else {
+                // slices issued so far: 0 .. min(t+R-2, nk-1); in steady state
+                // the R-3 slices after t+1 stay in flight, near the end wait for all
+                if (t + R - 2 <= nk - 1) wait_vmcnt<L * (R - 3)>();
+                else wait_vmcnt<0>();
+                ring_barrier();
+                if (t + R - 1 < nk) issue(t + R - 1, (u + R - 1) % R);
+                if (t + 1 < nk) read_frags(nxt, (u + 1) % R, 0);
+            }
+            mfma_step(cur);
+            if (steady && s + 1 == STEPS) interleave(std::integral_constant<int, JA + JB>{});
+            else interleave(std::integral_constant<int, 0>{});
+        }
+    };
     if (nk > 0) {
-        constexpr int L = JA + JB;  // loads per wave per slice
-        Frags F0, F1;
-        const int pre = nk < R ? nk : R;
+        const int pre = nk < R - 1 ? nk : R - 1;
         for (int t = 0; t < pre; ++t) issue(t, t);
-        if (pre == R) wait_vmcnt<L * (R - 1)>();  // slice 0 landed, R-1 slices still in flight
+        if (pre == R - 1) wait_vmcnt<L * (R - 2)>();  // slice 0 landed, R-2 slices still in flight
         else wait_vmcnt<0>();
         ring_barrier();
         read_frags(F0, 0, 0);
-        // trips of R slices; slice t = trip + u sits in slot u
-        for (int trip = 0; trip < nk; trip += R) {
+        int trip = 0;
+        // steady trips: slices trip .. trip+R-1 all satisfy t + R - 1 < nk
+        for (; trip + 2 * R - 1 <= nk; trip += R) {
+#pragma unroll
+            for (int u = 0; u < R; ++u) slice(trip + u, u, true);
+        }
+        for (; trip < nk; trip += R) {
 #pragma unroll
             for (int u = 0; u < R; ++u) {
-                const int t = trip + u;
-                if (t >= nk) break;
-#pragma unroll
-                for (int s = 0; s < STEPS; ++s) {
-                    Frags& cur = (s & 1) ? F1 : F0;
-                    Frags& nxt = (s & 1) ? F0 : F1;
-                    if (s + 1 < STEPS) {
-                        read_frags(nxt, u, s + 1);
-                    } else {
-                        // slices issued so far: 0 .. min(t-1+R, nk-1); in steady state
-                        // the R-2 slices after t+1 stay in flight, near the end wait for all
-                        if (t - 1 + R <= nk - 1) wait_vmcnt<L * (R - 2)>();
-                        else wait_vmcnt<0>();
-                        ring_barrier();
-                        if (t + R < nk) issue(t + R, u);
-                        if (t + 1 < nk) read_frags(nxt, (u + 1) % R, 0);
-                    }
-                    mfma_step(cur);
-                    interleave();
-                }
+                if (trip + u >= nk) break;
+                slice(trip + u, u, false);
             }
         }
     }
