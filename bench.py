@@ -54,7 +54,12 @@ def pmc_probe(name):
 
     from tiled_matrix_multiplication_gemm_amd import profiling
 
-    c, fn = dense_setup(name)
+    from tiled_matrix_multiplication_gemm_amd import inputs
+
+    if name in inputs.GROUPED_WORKLOADS:
+        c, fn = grouped_setup(name)
+    else:
+        c, fn = dense_setup(name)
     fn()
     torch.cuda.synchronize()
     n = profiling.COPY_BYTES // 2
@@ -140,18 +145,24 @@ def measure_dense(name, steps, warmup):
                 compulsory_bytes=hbm_bytes)
 
 
-def measure_grouped(name, steps, warmup):
+def grouped_setup(name, variant="float"):
     import numpy as np
     import torch
 
     import tiled_matrix_multiplication_gemm_amd as mg
     from tiled_matrix_multiplication_gemm_amd import inputs
 
-    c = inputs.grouped_workload(name, "float")
+    c = inputs.grouped_workload(name, variant)
     X, W = upload(c.X, c.dtype), upload(c.W, c.dtype)
     off = torch.from_numpy(c.offsets.astype(np.int32)).cuda()
     Y = torch.empty((c.T, c.N), dtype=X.dtype, device="cuda")
-    fn = lambda: mg.mg_grouped_gemm(X, W, off, out=Y)
+    return c, (lambda: mg.mg_grouped_gemm(X, W, off, out=Y))
+
+
+def measure_grouped(name, steps, warmup):
+    import tiled_matrix_multiplication_gemm_amd as mg
+
+    c, fn = grouped_setup(name)
     wall, mean_ms, med_ms = time_calls(fn, steps, warmup)
     flops = 2.0 * c.T * c.K * c.N
     hbm_bytes = 2.0 * (c.T * c.K + c.E * c.K * c.N + c.T * c.N) + 4.0 * (c.E + 1)

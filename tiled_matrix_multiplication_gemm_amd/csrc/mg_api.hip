@@ -29,7 +29,7 @@ using Cfg2 = TileCfg<64, 64, 64, 2, 2>;    // small problems: enough tiles to fi
 using Cfg3 = TileCfg<128, 256, 64, 2, 2>;
 using Cfg4 = TileCfg<256, 128, 64, 2, 2>;
 using Cfg5 = TileCfg<128, 128, 32, 2, 2>;
-using Cfg6 = TileCfg<256, 256, 64, 2, 4>;
+using Cfg6 = TileCfg<256, 256, 64, 2, 4>;  // general fallback keeps eight waves
 // fast kernels: <BM, BN, waves M, waves N, K slice, LDS ring slots>
 using Fast0 = DldsCfg<256, 256, 2, 4, 32, 5>;
 using Fast1 = DldsCfg<128, 128, 2, 2, 64, 3>;

@@ -3,13 +3,14 @@
 // row-major B operand is read out of LDS with the transposing
 // ds_read_b64_tr_b16, so no thread ever shuffles B in registers.
 //
-// One workgroup computes a BM x BN tile; the K loop streams BK = 64 wide
-// slices through two LDS stages (slice i+1 lands while slice i feeds the
-// matrix cores; "Using Triton to optimise GEMM across chips", section 2.2),
-// with XOR-swizzled 16-byte chunks against bank conflicts (FlagOS cross-chip
-// page, section 2.3).
+// One workgroup computes a BM x BN tile; the K loop streams BK-wide slices
+// (BK = 32 or 64) through a ring of R LDS slots, so that up to R-2 slices are
+// in flight while one feeds the matrix cores (the multi-stage pipeline of
+// "Using Triton to optimise GEMM across chips", section 2.2, sized here by
+// memory latency), with XOR-swizzled 16-byte chunks against bank conflicts
+// (FlagOS cross-chip page, section 2.3).
 //
-// Preconditions (checked by the host): K % 64 == 0, N % 8 == 0, and a tile's
+// Preconditions (checked by the host): K % BK == 0, N % 8 == 0, and a tile's
 // operand offsets fit in 31 bits (BM * lda and 64 * ldb elements).  Rows past
 // M and column chunks past N are clamped to the last valid ones, so every
 // load is in bounds; what they feed are output rows / columns that are never
@@ -39,7 +40,7 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const char* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p);
 }
 
-template <int BM_, int BN_, int WM_, int WN_, int BK_ = 64, int R_ = 2>
+template <int BM_, int BN_, int WM_, int WN_, int BK_ = 64, int R_ = 3>
 struct DldsCfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
     static constexpr int R = R_;                        // LDS slots in the ring (= slices in flight + 2)
@@ -137,39 +138,20 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
     const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
 
     // ---- which tile (same order as the general kernel) --------------------
-    int logical = args.xcd_remap ? xcd_logical(blockIdx.x, gridDim.x) : (int)blockIdx.x;
+    int total = (int)gridDim.x;
+    if constexpr (MODE == MODE_GROUPED) {
+        total = grouped_tiles<BM>(args);
+        if ((int)blockIdx.x >= total) return;
+    }
+    int logical = args.xcd_remap ? xcd_logical(blockIdx.x, total) : (int)blockIdx.x;
     const uint16_t* Ag = args.A;
     const uint16_t* Bg = args.B;
     uint16_t* Cg = args.C;
     int64_t M = args.M;
     int pm, pn;
     if constexpr (MODE == MODE_GROUPED) {
-        const int T = (int)args.M;
-        auto segment = [&](int e, int& r0, int& rows) {
-            int a = args.offsets[e], b = args.offsets[e + 1];
-            a = a < 0 ? 0 : (a > T ? T : a);
-            b = b < a ? a : (b > T ? T : b);
-            r0 = a;
-            rows = b - a;
-        };
-        int G = 0;
-        for (int e = 0; e < args.E; ++e) {
-            int r0, rows;
-            segment(e, r0, rows);
-            G += (rows + BM - 1) / BM;
-        }
-        if (logical >= G * args.tiles_n) return;
-        const int g = logical % G;
-        pn = logical / G;
-        int e = 0, cum = 0, r0 = 0, rows = 0;
-        for (; e < args.E; ++e) {
-            segment(e, r0, rows);
-            const int t = (rows + BM - 1) / BM;
-            if (g < cum + t) break;
-            cum += t;
-        }
-        if (e >= args.E) return;
-        pm = g - cum;
+        int e, r0, rows;
+        if (!grouped_tile<BM>(args, logical, e, r0, rows, pm, pn)) return;
         M = rows;
         Ag += (int64_t)r0 * args.lda;
         Bg += (int64_t)e * args.stride_we;
@@ -251,15 +233,20 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
     struct Frags {
         u32x4 a[FM], b[FN];
     };
-    auto read_frags = [&](Frags& f, int slot, int s) {
+    // `lv` is the number of this wave's 32-row MFMA blocks that hold output
+    // rows below M (FM as a compile-time constant for full tiles): fragments
+    // and MFMAs of the blocks past M are skipped.
+    auto read_frags = [&](Frags& f, int slot, int s, auto lv) {
         const char* sa = slot_ptr(slot);
         const char* sb = sa + Cfg::A_BYTES;
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
+            if (i >= lv) break;
             const int row = rowA0 + i * 32;
             const int c = (2 * s + (lane >> 5)) ^ swz_a<ACH>(row);
             f.a[i] = *(const lds_u32x4_t*)(sa + row * AROW + c * 16);
         }
+        if (lv == 0) return;
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
             // k-rows 16s + {0..3} and 16s + {4..7} (+8 for the upper half-wave)
@@ -271,11 +258,13 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
                            __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 2, 3))};
         }
     };
-    auto mfma_step = [&](const Frags& f) {
+    auto mfma_step = [&](const Frags& f, auto lv) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+        for (int i = 0; i < FM; ++i) {
+            if (i >= lv) break;
 #pragma unroll
             for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<DT>(f.a[i], f.b[j], acc[i][j]);
+        }
     };
     // Interleave the next step's LDS reads (FM + 2 FN instructions) with this
     // step's MFMAs (FM * FN instructions): two reads after each of the first
@@ -317,18 +306,18 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
     // last trips take the general form with run-time conditions.
     constexpr int L = JA + JB;  // loads per wave per slice
     Frags F0, F1;
-    auto slice = [&](const int t, const int u, const bool steady) {
+    auto slice = [&](const int t, const int u, const bool steady, auto lv) {
 #pragma unroll
         for (int s = 0; s < STEPS; ++s) {
             Frags& cur = (s & 1) ? F1 : F0;
             Frags& nxt = (s & 1) ? F0 : F1;
             if (s + 1 < STEPS) {
-                read_frags(nxt, u, s + 1);
+                read_frags(nxt, u, s + 1, lv);
             } else if (steady) {
                 wait_vmcnt<L * (R - 3)>();
                 ring_barrier();
                 issue(t + R - 1, (u + R - 1) % R);
-                read_frags(nxt, (u + 1) % R, 0);
+                read_frags(nxt, (u + 1) % R, 0, lv);
             } else {
                 // slices issued so far: 0 .. min(t+R-2, nk-1); in steady state
                 // the R-3 slices after t+1 stay in flight, near the end wait for all
@@ -336,34 +325,44 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
                 else wait_vmcnt<0>();
                 ring_barrier();
                 if (t + R - 1 < nk) issue(t + R - 1, (u + R - 1) % R);
-                if (t + 1 < nk) read_frags(nxt, (u + 1) % R, 0);
+                if (t + 1 < nk) read_frags(nxt, (u + 1) % R, 0, lv);
             }
-            mfma_step(cur);
+            mfma_step(cur, lv);
             if (steady && s + 1 == STEPS) interleave(std::integral_constant<int, JA + JB>{});
             else interleave(std::integral_constant<int, 0>{});
         }
     };
-    if (nk > 0) {
+    auto main_loop = [&](auto lv) {
+        if (nk <= 0) return;
         const int pre = nk < R - 1 ? nk : R - 1;
         for (int t = 0; t < pre; ++t) issue(t, t);
         if (pre == R - 1) wait_vmcnt<L * (R - 2)>();  // slice 0 landed, R-2 slices still in flight
         else wait_vmcnt<0>();
         ring_barrier();
-        read_frags(F0, 0, 0);
+        read_frags(F0, 0, 0, lv);
         int trip = 0;
         // steady trips: slices trip .. trip+R-1 all satisfy t + R - 1 < nk
         for (; trip + 2 * R - 1 <= nk; trip += R) {
 #pragma unroll
-            for (int u = 0; u < R; ++u) slice(trip + u, u, true);
+            for (int u = 0; u < R; ++u) slice(trip + u, u, true, lv);
         }
         for (; trip < nk; trip += R) {
 #pragma unroll
             for (int u = 0; u < R; ++u) {
                 if (trip + u >= nk) break;
-                slice(trip + u, u, false);
+                slice(trip + u, u, false, lv);
             }
         }
-    }
+    };
+    // Waves whose rows all lie below M run the loop with every MFMA; the
+    // others (edge tiles, the ragged last tile of an expert) skip the 32-row
+    // blocks past M.  Both forms take the same barriers in the same order, and
+    // the choice is made on a scalar (wave-uniform) value.
+    const int64_t wave_rows = M - m0 - wm * Cfg::WTM;
+    const int live = __builtin_amdgcn_readfirstlane(
+        (int)(wave_rows >= Cfg::WTM ? FM : (wave_rows <= 0 ? 0 : (wave_rows + 31) / 32)));
+    if (live == FM) main_loop(std::integral_constant<int, FM>{});
+    else main_loop(live);
 
     // ---- epilogue: (bias, ReLU), one rounding, stores -------------------
     // One 32x32 MFMA tile at a time (a scheduling barrier keeps the compiler

@@ -44,6 +44,55 @@ struct KArgs {
     int32_t xcd_remap;
 };
 
+// Grouped GEMM: which tile workgroup `logical` computes.  Tiles run expert by
+// expert; within an expert, column slab by column slab, with the expert's row
+// tiles of one slab adjacent.  Consecutive workgroups therefore share the
+// expert's X rows (which stay in L2 across its column slabs) and the row
+// tiles of a slab share its W columns.  Offsets are clamped into [0, T] so
+// that malformed offsets cannot send a workgroup outside X or Y.
+// grouped_tiles() counts the tiles: the host sizes the grid for the worst
+// case (it does not read the device offsets), and the XCD renumbering must
+// spread the real tiles, not the grid, over the 8 XCDs.
+template <int BM>
+__device__ __forceinline__ int grouped_tiles(const KArgs& args) {
+    const int T = (int)args.M;
+    int total = 0;
+    int a = args.offsets[0];
+    a = a < 0 ? 0 : (a > T ? T : a);
+    for (int e = 0; e < args.E; ++e) {
+        int b = args.offsets[e + 1];
+        b = b < a ? a : (b > T ? T : b);
+        total += (b - a + BM - 1) / BM;
+        a = b;
+    }
+    return total * args.tiles_n;
+}
+template <int BM>
+__device__ __forceinline__ bool grouped_tile(const KArgs& args, int logical, int& e, int& r0, int& rows, int& pm,
+                                             int& pn) {
+    const int T = (int)args.M;
+    int base = 0;
+    int a = args.offsets[0];
+    a = a < 0 ? 0 : (a > T ? T : a);
+    for (e = 0; e < args.E; ++e) {
+        int b = args.offsets[e + 1];
+        b = b < a ? a : (b > T ? T : b);
+        const int mt = (b - a + BM - 1) / BM;
+        const int cnt = mt * args.tiles_n;
+        if (logical < base + cnt) {
+            const int local = logical - base;
+            pn = local / mt;
+            pm = local % mt;
+            r0 = a;
+            rows = b - a;
+            return true;
+        }
+        base += cnt;
+        a = b;
+    }
+    return false;
+}
+
 template <int BM_, int BN_, int BK_, int WM_, int WN_>
 struct TileCfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
@@ -144,42 +193,20 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_tile_kernel(const KArgs args) {
     const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
 
     // ---- which tile -------------------------------------------------------
-    int logical = args.xcd_remap ? xcd_logical(blockIdx.x, gridDim.x) : (int)blockIdx.x;
+    int total = (int)gridDim.x;
+    if constexpr (MODE == MODE_GROUPED) {
+        total = grouped_tiles<BM>(args);
+        if ((int)blockIdx.x >= total) return;
+    }
+    int logical = args.xcd_remap ? xcd_logical(blockIdx.x, total) : (int)blockIdx.x;
     const uint16_t* Ag = args.A;
     const uint16_t* Bg = args.B;
     uint16_t* Cg = args.C;
     int64_t M = args.M;
     int pm, pn;
     if constexpr (MODE == MODE_GROUPED) {
-        // Tile rows of all experts, expert by expert, row-tile index fastest.
-        // Offsets are clamped into [0, T] so that malformed offsets cannot
-        // send a workgroup outside X or Y.
-        const int T = (int)args.M;
-        auto segment = [&](int e, int& r0, int& rows) {
-            int a = args.offsets[e], b = args.offsets[e + 1];
-            a = a < 0 ? 0 : (a > T ? T : a);
-            b = b < a ? a : (b > T ? T : b);
-            r0 = a;
-            rows = b - a;
-        };
-        int G = 0;
-        for (int e = 0; e < args.E; ++e) {
-            int r0, rows;
-            segment(e, r0, rows);
-            G += (rows + BM - 1) / BM;
-        }
-        if (logical >= G * args.tiles_n) return;
-        const int g = logical % G;
-        pn = logical / G;
-        int e = 0, cum = 0, r0 = 0, rows = 0;
-        for (; e < args.E; ++e) {
-            segment(e, r0, rows);
-            const int t = (rows + BM - 1) / BM;
-            if (g < cum + t) break;
-            cum += t;
-        }
-        if (e >= args.E) return;
-        pm = g - cum;
+        int e, r0, rows;
+        if (!grouped_tile<BM>(args, logical, e, r0, rows, pm, pn)) return;
         M = rows;
         Ag += (int64_t)r0 * args.lda;
         Bg += (int64_t)e * args.stride_we;
