@@ -14,7 +14,7 @@ Beside the main figure the line carries:
   also          the same measurement for the 1024x1024x2048 fp16 GEMM, its
                 fused bias+ReLU form and the grouped MoE GEMM.
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--no-also]
+Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 50] [--no-cpu-baseline] [--no-also]
 """
 from __future__ import annotations
 
@@ -36,8 +36,8 @@ PEAK_HBM_GBS = 8000.0       # HBM3E
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="gemm_8192_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-also", action="store_true")
@@ -139,10 +139,19 @@ def measure_dense(name, steps, warmup):
     c, fn = dense_setup(name)
     wall, mean_ms, med_ms = time_calls(fn, steps, warmup)
     flops = 2.0 * c.M * c.N * c.K
-    cfg = mg.mg_config_info(mg.mg_last_config())["name"]
+    d = mg.mg_config_info(mg.mg_last_config())
     hbm_bytes = 2.0 * (c.M * c.K + c.K * c.N + c.M * c.N) + (2.0 * c.N if c.bias is not None else 0.0)
-    return dict(case=c, flops=flops, wall=wall, kernel_ms=mean_ms, kernel_ms_median=med_ms, tile_config=cfg,
-                compulsory_bytes=hbm_bytes)
+    return dict(case=c, flops=flops, wall=wall, kernel_ms=mean_ms, kernel_ms_median=med_ms, tile_config=d["name"],
+                kernel=kernel_name(d, c.K, c.N), compulsory_bytes=hbm_bytes)
+
+
+def kernel_name(d, K, N):
+    """The kernel family a table row launches for this K and N (the host
+    takes the direct-to-LDS kernel when K is a multiple of its slice and N of
+    8; dense problems only)."""
+    if d["direct_lds"] and K % d["direct_bk"] == 0 and N % 8 == 0:
+        return "gemm_kslab_kernel" if d["direct_ksplit"] > 1 else "gemm_dlds_kernel"
+    return "gemm_tile_kernel"
 
 
 def grouped_setup(name, variant="float"):
@@ -235,7 +244,7 @@ def main():
                      "compulsory_bytes": main_res["compulsory_bytes"],
                      "kernel_ms_mean": round(main_res["kernel_ms"], 4),
                      "kernel_ms_median": round(main_res["kernel_ms_median"], 4),
-                     "kernel": "gemm_tile_kernel (%s)" % main_res["tile_config"]},
+                     "kernel": "%s (%s)" % (main_res["kernel"], main_res["tile_config"])},
     }
     sys.stdout.flush()
     if not args.no_also:

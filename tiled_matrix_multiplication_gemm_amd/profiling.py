@@ -1,6 +1,6 @@
 """Summaries of rocprofv3 output for the GEMM kernels.
 
-  python -m tiled_matrix_multiplication_gemm_amd.profiling trace  <kernel_stats.csv> <out.txt> --cmd "..."
+  python -m tiled_matrix_multiplication_gemm_amd.profiling trace  <kernel_stats.csv> <out.txt> --cmd "..." [--last N]
   python -m tiled_matrix_multiplication_gemm_amd.profiling traffic <fetch_dir> <write_dir> <out.txt> --cmd "..."
   python -m tiled_matrix_multiplication_gemm_amd.profiling counters <out.txt> <dir>... --cmd "..."
 
@@ -129,17 +129,34 @@ def write_counters(dirs, out, cmd, kernel_key: str = "gemm_"):
     return vals
 
 
-def write_trace(stats_csv, out, cmd):
+def write_trace(stats_csv, out, cmd, last=0):
+    """Per-kernel calls and mean duration from the --stats summary; with
+    `last`, also the mean over the last `last` dispatches of each kernel from
+    the kernel trace beside it (the timed calls, without the warm-up ones,
+    whose first call includes loading the code object)."""
     with open(stats_csv) as f:
         rows = list(csv.DictReader(f))
+    timed = {}
+    trace_csv = stats_csv.replace("kernel_stats.csv", "kernel_trace.csv")
+    if last > 0 and os.path.exists(trace_csv):
+        per = {}
+        with open(trace_csv) as f:
+            for r in csv.DictReader(f):
+                per.setdefault(r["Kernel_Name"], []).append(
+                    (int(r["Dispatch_Id"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+        for name, v in per.items():
+            d = [ns for _, ns in sorted(v)][-last:]
+            timed[name] = (len(d), sum(d) / len(d))
     with open(out, "w") as f:
         f.write("# rocprofv3 --kernel-trace --stats summary\n")
         f.write("# command: %s\n" % cmd)
         f.write("# source_hash = %s\n" % source_hash())
-        f.write("%-100s %6s %14s %12s\n" % ("kernel", "calls", "mean_ns", "pct"))
+        f.write("%-100s %6s %14s %12s %18s\n" % ("kernel", "calls", "mean_ns", "pct", "mean_ns_timed"))
         for r in rows:
-            f.write("%-100s %6s %14.1f %12s\n" % (r["Name"][:100], r["Calls"], float(r["AverageNs"]),
-                                                  r["Percentage"]))
+            t = timed.get(r["Name"])
+            tt = "%.1f (last %d)" % (t[1], t[0]) if t else "-"
+            f.write("%-100s %6s %14.1f %12s %18s\n" % (r["Name"][:100], r["Calls"], float(r["AverageNs"]),
+                                                        r["Percentage"], tt))
 
 
 def main():
@@ -149,6 +166,7 @@ def main():
     a.add_argument("stats_csv")
     a.add_argument("out")
     a.add_argument("--cmd", required=True)
+    a.add_argument("--last", type=int, default=0, help="also average the last N dispatches (the timed calls)")
     b = sub.add_parser("traffic")
     b.add_argument("fetch_dir")
     b.add_argument("write_dir")
@@ -162,7 +180,7 @@ def main():
     if args.what == "counters":
         write_counters(args.dirs, args.out, args.cmd)
     elif args.what == "trace":
-        write_trace(args.stats_csv, args.out, args.cmd)
+        write_trace(args.stats_csv, args.out, args.cmd, args.last)
     else:
         print(write_traffic(args.fetch_dir, args.write_dir, args.out, args.cmd))
 
