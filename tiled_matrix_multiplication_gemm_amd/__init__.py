@@ -47,6 +47,8 @@ EXPORTED = (
 def lib() -> ctypes.CDLL:
     """The loaded C library with argument types declared (raises if not built)."""
     global _lib
+    if _lib is not None:
+        return _lib
     with _lock:
         if _lib is not None:
             return _lib
@@ -102,9 +104,13 @@ def _dtype_code(t) -> int:
 
 
 def _stream(t):
+    """torch's current HIP stream on t's device, as a raw handle."""
     import torch
 
-    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return raw(t.device.index)
+    return torch.cuda.current_stream(t.device).cuda_stream
 
 
 def _require_gpu(*ts):

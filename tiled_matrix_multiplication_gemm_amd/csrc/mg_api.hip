@@ -78,8 +78,8 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 //  - grouped MoE: 256x256 tiles, eight waves (each expert's weight slab is
 //    read by one or two tiles);
 //  - enough 256x256 tiles to fill the chip several times: row 0;
-//  - outputs with fewer than 256 tiles of 128x128: 64x64 tiles with K split
-//    over the waves of a workgroup (row 7);
+//  - outputs with fewer than 256 tiles of 128x128: 64x64 tiles, one per CU
+//    (row 2; the K-split row 7 is within 4 %);
 //  - in between: 128x128 tiles.
 int select_config(int64_t M, int64_t N, int64_t K, int grouped) {
     (void)K;
@@ -88,7 +88,7 @@ int select_config(int64_t M, int64_t N, int64_t K, int grouped) {
     if (grouped) return 0;
     if (cdiv(M, 256) * cdiv(N, 256) >= 512) return 0;
     if (cdiv(M, 128) * cdiv(N, 128) >= 256) return 1;
-    return 7;
+    return 2;
 }
 
 // ---- validation --------------------------------------------------------------

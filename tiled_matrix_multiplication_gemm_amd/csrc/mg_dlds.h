@@ -34,6 +34,19 @@ __device__ __forceinline__ void direct_load16(const void* src, lds_void_t* dst) 
     __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
 }
 
+// Buffer resource over [base, base + 2^31) (word 3 = 0x00020000: untyped
+// 32-bit data format, the gfx9 family's value; no swizzle, stride 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
+}
+
+// The same direct load through a buffer resource: the per-lane part of the
+// address is a 32-bit offset and the uniform part lives in scalar registers,
+// so a load costs no vector address arithmetic (buffer_load_dwordx4 ... lds).
+__device__ __forceinline__ void direct_load16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset, lds_void_t* dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, voffset, 0, 0, 0);
+}
+
 // Transposing LDS read: within each group of 16 lanes, lane t receives
 // element t of each of the four 16-element rows that lanes 4r .. 4r+3 point at.
 __device__ __forceinline__ i16x4 lds_read_tr16(const char* p) {
@@ -134,7 +147,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar registers
     const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
 
     // ---- which tile (same order as the general kernel) --------------------
@@ -195,17 +208,16 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
     const int64_t stepB = (int64_t)BK * args.ldb * 2;
 
     // direct loads of k-slice kt into ring slot `slot` (a compile-time index)
+    // (buffer resources rebased on the slice: offsets stay below 2^31)
     auto issue = [&](int kt, int slot) {
-        const char* a = baseA + kt * stepA;
-        const char* b = baseB + kt * stepB;
+        const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(baseA + kt * stepA);
+        const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(baseB + kt * stepB);
         char* sa = slot_ptr(slot);
         char* sb = sa + Cfg::A_BYTES;
 #pragma unroll
-        for (int j = 0; j < JA; ++j)
-            direct_load16(a + offA_g[j], (lds_void_t*)(sa + (wave * JA + j) * 1024));
+        for (int j = 0; j < JA; ++j) direct_load16(ra, offA_g[j], (lds_void_t*)(sa + (wave * JA + j) * 1024));
 #pragma unroll
-        for (int j = 0; j < JB; ++j)
-            direct_load16(b + offB_g[j], (lds_void_t*)(sb + (wave * JB + j) * 1024));
+        for (int j = 0; j < JB; ++j) direct_load16(rb, offB_g[j], (lds_void_t*)(sb + (wave * JB + j) * 1024));
     };
 
     f32x16 acc[FM][FN];
