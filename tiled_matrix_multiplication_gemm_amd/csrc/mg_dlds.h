@@ -275,7 +275,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
         for (int i = 0; i < FM; ++i) {
             if (i >= lv) break;
 #pragma unroll
-            for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<DT>(f.a[i], f.b[j], acc[i][j]);
+            for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<DT>(f.b[j], f.a[i], acc[i][j]);
         }
     };
     // Interleave the next step's LDS reads (FM + 2 FN instructions) with this
@@ -377,29 +377,39 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
     else main_loop(live);
 
     // ---- epilogue: (bias, ReLU), one rounding, stores -------------------
-    // One 32x32 MFMA tile at a time (a scheduling barrier keeps the compiler
-    // from pulling every accumulator out of the AGPRs at once); interior tiles
-    // store without bounds checks.
+    // The MFMAs take B as their first operand, so each accumulator tile holds
+    // C transposed: register r of lane l is C[l % 32][8 (r / 4) + 4 (l / 32)
+    // + r % 4] of the 32x32 tile.  A lane thus owns 4 adjacent columns of one
+    // row per group of 4 registers and writes them with one 8-byte store
+    // (N % 8 == 0 on this path, so a group is entirely inside or outside N).
+    // One 32x32 tile at a time (a scheduling barrier keeps the compiler from
+    // pulling every accumulator out at once); interior tiles skip the checks.
     const bool interior = (m0 + BM <= M) && (n0 + BN <= N);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-        const int64_t col = n0 + wn * Cfg::WTN + j * 32 + (lane & 31);
-        float bj = 0.0f;
-        if constexpr (EPI) bj = (col < N) ? to_float<DT>(args.bias[col]) : 0.0f;
+    for (int i = 0; i < FM; ++i) {
+        const int64_t row = m0 + wm * Cfg::WTM + i * 32 + (lane & 31);
+        const bool row_ok = interior || row < M;
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
+        for (int j = 0; j < FN; ++j) {
             __builtin_amdgcn_sched_barrier(0);
-            const int64_t row0 = m0 + wm * Cfg::WTM + i * 32 + 4 * (lane >> 5);
-            uint16_t* cp = Cg + row0 * args.ldc + col;
+            const int64_t col0 = n0 + wn * Cfg::WTN + j * 32 + 4 * (lane >> 5);
+            uint16_t* cp = Cg + row * args.ldc + col0;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int dr = 8 * (r >> 2) + (r & 3);
-                float v = acc[i][j][r];
-                if constexpr (EPI) {
-                    v = v + bj;
-                    v = (v > 0.0f) ? v : 0.0f;
+            for (int q = 0; q < 4; ++q) {
+                const int64_t col = col0 + 8 * q;
+                float v[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    v[t] = acc[i][j][4 * q + t];
+                    if constexpr (EPI) {
+                        const float bt = (col + t < N) ? to_float<DT>(args.bias[col + t]) : 0.0f;
+                        v[t] = v[t] + bt;
+                        v[t] = (v[t] > 0.0f) ? v[t] : 0.0f;
+                    }
                 }
-                if (interior || (row0 + dr < M && col < N)) cp[dr * args.ldc] = from_float<DT>(v);
+                const uint32_t lo = (uint32_t)from_float<DT>(v[0]) | ((uint32_t)from_float<DT>(v[1]) << 16);
+                const uint32_t hi = (uint32_t)from_float<DT>(v[2]) | ((uint32_t)from_float<DT>(v[3]) << 16);
+                if (row_ok && (interior || col < N)) *(uint2*)(cp + 8 * q) = make_uint2(lo, hi);
             }
         }
     }
