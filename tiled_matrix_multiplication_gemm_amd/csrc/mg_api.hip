@@ -73,22 +73,36 @@ std::atomic<int> g_last{-1};
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Shape classes, from the offline sweep (per-row timings on MI355X for the
-// 8192^3, 1024x1024x2048 and grouped MoE workloads):
-//  - grouped MoE: 256x256 tiles, eight waves (each expert's weight slab is
-//    read by one or two tiles);
-//  - enough 256x256 tiles to fill the chip several times: row 0;
-//  - outputs with fewer than 256 tiles of 128x128: 64x64 tiles, one per CU
-//    (row 2; the K-split row 7 is within 4 %);
-//  - in between: 128x128 tiles.
+// Row choice for dense problems: a workgroup's tile runs on one CU, and the
+// tiles run in rounds of 256 (one per CU), so the time of a row is modelled
+// as rounds * (BM * BN / rate), with `rate` the row's measured per-CU output
+// rate relative to 256x256 tiles (offline sweep on MI355X, 8192^3 bf16).
+// Large outputs get 256x256 tiles, outputs too small to give every CU one of
+// them get smaller tiles (1024 x 1024 -> 64x64).  Grouped GEMMs use the
+// 256x256 row (each expert's weight slab is read by one or two tiles).
 int select_config(int64_t M, int64_t N, int64_t K, int grouped) {
     (void)K;
     int forced = g_forced.load();
     if (forced >= 0) return forced;
     if (grouped) return 0;
-    if (cdiv(M, 256) * cdiv(N, 256) >= 512) return 0;
-    if (cdiv(M, 128) * cdiv(N, 128) >= 256) return 1;
-    return 2;
+    struct Cand {
+        int id, bm, bn;
+        double rate;
+    };
+    static const Cand cands[] = {{0, 256, 256, 1.00}, {3, 128, 256, 0.76}, {4, 256, 128, 0.68},
+                                 {1, 128, 128, 0.49}, {2, 64, 64, 0.50}};
+    constexpr int64_t kCUs = 256;
+    int best = 0;
+    double best_t = 0.0;
+    for (const Cand& c : cands) {
+        const int64_t tiles = cdiv(M, c.bm) * cdiv(N, c.bn);
+        const double t = (double)cdiv(tiles, kCUs) * ((double)c.bm * c.bn / c.rate);
+        if (best_t == 0.0 || t < best_t) {
+            best_t = t;
+            best = c.id;
+        }
+    }
+    return best;
 }
 
 // ---- validation --------------------------------------------------------------

@@ -157,7 +157,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_kslab_kernel(const KArgs args) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<DT>(f.a[i], f.b[j], acc[i][j]);
+            for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<DT>(f.b[j], f.a[i], acc[i][j]);
     };
 
     // ---- this wave's K loop: private ring, no workgroup barrier ----------
@@ -234,18 +234,26 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_kslab_kernel(const KArgs args) {
                     v[4 * r4 + 3] += p.w;
                 }
             }
-            const int64_t col = n0 + j * 32 + (lane & 31);
-            float bj = 0.0f;
-            if constexpr (EPI) bj = (col < N) ? to_float<DT>(args.bias[col]) : 0.0f;
+            // accumulators hold C transposed (B is the first MFMA operand):
+            // register 4q+t of lane l is C[l % 32][8q + 4 (l / 32) + t]
+            const int64_t row = m0 + i * 32 + (lane & 31);
+            const int64_t col0 = n0 + j * 32 + 4 * (lane >> 5);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t row = m0 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                float x = v[r];
-                if constexpr (EPI) {
-                    x = x + bj;
-                    x = (x > 0.0f) ? x : 0.0f;
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int64_t col = col0 + 8 * q4;
+                float x[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    x[t] = v[4 * q4 + t];
+                    if constexpr (EPI) {
+                        const float bt = (col + t < N) ? to_float<DT>(args.bias[col + t]) : 0.0f;
+                        x[t] = x[t] + bt;
+                        x[t] = (x[t] > 0.0f) ? x[t] : 0.0f;
+                    }
                 }
-                if (row < M && col < N) Cg[row * args.ldc + col] = from_float<DT>(x);
+                const uint32_t lo = (uint32_t)from_float<DT>(x[0]) | ((uint32_t)from_float<DT>(x[1]) << 16);
+                const uint32_t hi = (uint32_t)from_float<DT>(x[2]) | ((uint32_t)from_float<DT>(x[3]) << 16);
+                if (row < M && col < N) *(uint2*)(Cg + row * args.ldc + col) = make_uint2(lo, hi);
             }
         }
 }
