@@ -27,6 +27,8 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4_t;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2_t;
 
 // One 16-byte direct load per lane: global memory -> LDS at
 // dst + 16 * lane (dst must be the same for the whole wave).
@@ -72,6 +74,12 @@ struct DldsCfg {
     static constexpr int STAGES = R;
     static constexpr int LDS_BYTES = R * SLOT;
     static constexpr int BCH = BN / 8;                  // 16-byte chunks per B k-row
+    // epilogue staging: each wave's output block passes through LDS (rows of
+    // WTN bf16/fp16) so that the stores write whole 16-byte chunks of rows
+    static constexpr int STAGE_BYTES = WTM * WTN * 2;
+    static constexpr int STAGE_PER_SLOT = SLOT / STAGE_BYTES;
+    static constexpr bool STAGED = STAGE_PER_SLOT >= 1 && STAGE_PER_SLOT * R >= NW &&
+                                   (WTN / 8 == 4 || WTN / 8 == 8 || WTN / 8 == 16);
     static_assert(BK == 32 || BK == 64, "K slice must be 32 or 64");
     static_assert(R >= 3 && R <= 8, "ring of 3..8 slots");
     static_assert(JA * NW * 1024 == A_BYTES && JB * NW * 1024 == B_BYTES, "slice must split evenly over waves");
@@ -379,37 +387,80 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
     // ---- epilogue: (bias, ReLU), one rounding, stores -------------------
     // The MFMAs take B as their first operand, so each accumulator tile holds
     // C transposed: register r of lane l is C[l % 32][8 (r / 4) + 4 (l / 32)
-    // + r % 4] of the 32x32 tile.  A lane thus owns 4 adjacent columns of one
-    // row per group of 4 registers and writes them with one 8-byte store
-    // (N % 8 == 0 on this path, so a group is entirely inside or outside N).
+    // + r % 4] of the 32x32 tile, i.e. a lane owns 4 adjacent columns of one
+    // row per group of 4 registers.  Those 8 bytes go to LDS (the ring is free
+    // once every wave has left the K loop), row-major per wave with XOR-
+    // swizzled 16-byte chunks; the wave then reads back whole chunks and
+    // writes each output row as contiguous 16-byte pieces, 8 rows per store
+    // (N % 8 == 0 on this path, so a chunk is entirely inside or outside N).
     // One 32x32 tile at a time (a scheduling barrier keeps the compiler from
     // pulling every accumulator out at once); interior tiles skip the checks.
     const bool interior = (m0 + BM <= M) && (n0 + BN <= N);
+    auto pack4 = [&](const f32x16& c, int q, int64_t col) -> u32x2 {
+        float v[4];
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-        const int64_t row = m0 + wm * Cfg::WTM + i * 32 + (lane & 31);
-        const bool row_ok = interior || row < M;
+        for (int t = 0; t < 4; ++t) {
+            v[t] = c[4 * q + t];
+            if constexpr (EPI) {
+                const float bt = (col + t < N) ? to_float<DT>(args.bias[col + t]) : 0.0f;
+                v[t] = v[t] + bt;
+                v[t] = (v[t] > 0.0f) ? v[t] : 0.0f;
+            }
+        }
+        return u32x2{(uint32_t)from_float<DT>(v[0]) | ((uint32_t)from_float<DT>(v[1]) << 16),
+                     (uint32_t)from_float<DT>(v[2]) | ((uint32_t)from_float<DT>(v[3]) << 16)};
+    };
+    if constexpr (Cfg::STAGED) {
+        constexpr int CH = Cfg::WTN / 8;  // 16-byte chunks per staged row
+        constexpr int RB = Cfg::WTN * 2;  // bytes per staged row
+        auto stage_swz = [](int row) { return (row ^ (row >> 3)) & (CH - 1); };
+        wait_vmcnt<0>();
+        ring_barrier();  // every wave is out of the K loop: the ring is free
+        char* stage = nullptr;
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            __builtin_amdgcn_sched_barrier(0);
-            const int64_t col0 = n0 + wn * Cfg::WTN + j * 32 + 4 * (lane >> 5);
-            uint16_t* cp = Cg + row * args.ldc + col0;
+        for (int u = 0; u < R; ++u)
+            if (wave / Cfg::STAGE_PER_SLOT == u) stage = slot_ptr(u) + (wave % Cfg::STAGE_PER_SLOT) * Cfg::STAGE_BYTES;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int64_t col = col0 + 8 * q;
-                float v[4];
+        for (int i = 0; i < FM; ++i) {
+            const int row = i * 32 + (lane & 31);
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    v[t] = acc[i][j][4 * q + t];
-                    if constexpr (EPI) {
-                        const float bt = (col + t < N) ? to_float<DT>(args.bias[col + t]) : 0.0f;
-                        v[t] = v[t] + bt;
-                        v[t] = (v[t] > 0.0f) ? v[t] : 0.0f;
-                    }
+            for (int j = 0; j < FN; ++j) {
+                __builtin_amdgcn_sched_barrier(0);
+                const int cl = j * 32 + 4 * (lane >> 5);  // first column of this lane's group, q = 0
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int c = cl + 8 * q;
+                    const u32x2 w = pack4(acc[i][j], q, n0 + wn * Cfg::WTN + c);
+                    *(lds_u32x2_t*)(stage + row * RB + ((c >> 3) ^ stage_swz(row)) * 16 + (c & 7) * 2) = w;
                 }
-                const uint32_t lo = (uint32_t)from_float<DT>(v[0]) | ((uint32_t)from_float<DT>(v[1]) << 16);
-                const uint32_t hi = (uint32_t)from_float<DT>(v[2]) | ((uint32_t)from_float<DT>(v[3]) << 16);
-                if (row_ok && (interior || col < N)) *(uint2*)(cp + 8 * q) = make_uint2(lo, hi);
+            }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // own writes done before reading them back
+        constexpr int ROWS_PER_LOAD = 64 / CH;
+        const int rsub = lane / CH, ch = lane % CH;
+        const int64_t col = n0 + wn * Cfg::WTN + ch * 8;
+#pragma unroll
+        for (int it = 0; it < Cfg::WTM / ROWS_PER_LOAD; ++it) {
+            const int row = it * ROWS_PER_LOAD + rsub;
+            const u32x4 w = *(const lds_u32x4_t*)(stage + row * RB + (ch ^ stage_swz(row)) * 16);
+            const int64_t grow = m0 + wm * Cfg::WTM + row;
+            if (interior || (grow < M && col < N)) *(u32x4*)(Cg + grow * args.ldc + col) = w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int64_t row = m0 + wm * Cfg::WTM + i * 32 + (lane & 31);
+            const bool row_ok = interior || row < M;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                __builtin_amdgcn_sched_barrier(0);
+                const int64_t col0 = n0 + wn * Cfg::WTN + j * 32 + 4 * (lane >> 5);
+                uint16_t* cp = Cg + row * args.ldc + col0;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const u32x2 w = pack4(acc[i][j], q, col0 + 8 * q);
+                    if (row_ok && (interior || col0 + 8 * q < N)) *(u32x2*)(cp + 8 * q) = w;
+                }
             }
         }
     }
