@@ -33,7 +33,7 @@ using Cfg6 = TileCfg<256, 256, 64, 2, 4>;  // general fallback keeps eight waves
 // fast kernels: <BM, BN, waves M, waves N, K slice, LDS ring slots>
 using Fast0 = DldsCfg<256, 256, 2, 4, 32, 5>;
 using Fast1 = DldsCfg<128, 128, 2, 2, 64, 3>;
-using Fast2 = DldsCfg<64, 64, 2, 2, 64, 3>;
+using Fast2 = DldsCfg<64, 64, 2, 2, 64, 6>;
 using Fast3 = DldsCfg<128, 256, 2, 2, 32, 4>;
 using Fast4 = DldsCfg<256, 128, 2, 2, 32, 4>;
 using Fast6 = DldsCfg<256, 256, 2, 2, 32, 5>;
