@@ -175,6 +175,37 @@ def test_workload_8192_bf16_sampled(orc, variant):
     assert bad.size == 0, "Freivalds screen fails on rows %s" % bad[:10]
 
 
+@pytest.mark.parametrize("integer", [True, False])
+def test_large_ragged_edges_sampled(orc, integer):
+    """A large output whose edges cut through 256x256 tiles (the edge-row
+    form of the tile kernel at full size), with bias and ReLU: the seeded
+    sample, every output in the last partial row and column tiles' corners,
+    and the edge set against the oracle."""
+    import torch
+
+    M, N, K, dt = 3000, 5000, 4096, BF16
+    if integer:
+        c = inputs.integer_dense(M, N, K, dt, 4401, epilogue=True, name="ragged_large")
+    else:
+        c = inputs.random_dense(M, N, K, dt, 4402, epilogue=True, name="ragged_large")
+    announce("dense ragged_large %dx%dx%d int=%s (sampled)" % (M, N, K, integer))
+    out = Guarded(M, N, dt)
+    mg.mg_gemm_bias_relu(to_dev(c.A, dt), to_dev(c.B, dt), to_dev(c.bias, dt), out=out.mat)
+    torch.cuda.synchronize()
+    assert out.guards_intact(), "write outside the output"
+    got = out.result()
+    rows, cols = compare.sample_positions(M, N, 4096, 4403)
+    er, ec = compare.edge_positions(M, N)
+    tr = np.repeat(np.arange(M - (M % 256), M), 8)  # rows of the last, partial row tile
+    tc = np.tile(np.arange(N - 8, N), M % 256)
+    rows, cols = np.concatenate([rows, er, tr]), np.concatenate([cols, ec, tc])
+    ref, ref_q = orc.gemm_sampled(c.A, c.B, dt, rows, cols, bias=c.bias, relu=True)
+    if integer:
+        assert_bitexact(got[rows, cols], ref_q, dt, c.name)
+    else:
+        assert_tolerance(got[rows, cols], ref, dt, c.name)
+
+
 def run_grouped(case):
     import torch
 

@@ -8,45 +8,11 @@
 #include <stdint.h>
 
 #include "mi355gemm.h"
-#include "mg_tile.h"
-#include "mg_dlds.h"
-#include "mg_kslab.h"
+#include "mg_table.h"
 
 namespace {
 
 using namespace mg;
-
-// ---- configuration table ---------------------------------------------------
-// One row per compiled tile shape.  The table is static: rows are chosen by
-// shape class in select_config(), which an offline sweep tunes; there is no
-// run-time search.
-// Each row has a general kernel (register-staged loads, any K and N) and,
-// where BK = 64, a direct-to-LDS fast kernel used when K % 64 == 0 and
-// N % 8 == 0.
-using Cfg0 = TileCfg<256, 256, 64, 2, 4>;  // large square problems, eight waves (two per SIMD)
-using Cfg1 = TileCfg<128, 128, 64, 2, 2>;  // mid-size, grouped
-using Cfg2 = TileCfg<64, 64, 64, 2, 2>;    // small problems: enough tiles to fill 256 CUs
-using Cfg3 = TileCfg<128, 256, 64, 2, 2>;
-using Cfg4 = TileCfg<256, 128, 64, 2, 2>;
-using Cfg5 = TileCfg<128, 128, 32, 2, 2>;
-using Cfg6 = TileCfg<256, 256, 64, 2, 4>;  // general fallback keeps eight waves
-// fast kernels: <BM, BN, waves M, waves N, K slice, LDS ring slots>
-using Fast0 = DldsCfg<256, 256, 2, 4, 32, 5>;
-using Fast1 = DldsCfg<128, 128, 2, 2, 64, 3>;
-using Fast2 = DldsCfg<64, 64, 2, 2, 64, 6>;
-using Fast3 = DldsCfg<128, 256, 2, 2, 32, 4>;
-using Fast4 = DldsCfg<256, 128, 2, 2, 32, 4>;
-using Fast6 = DldsCfg<256, 256, 2, 2, 32, 5>;
-using Cfg7 = TileCfg<64, 64, 64, 2, 2>;
-using Fast7 = SlabCfg<64, 64, 4, 32, 4>;  // K split over the 4 waves of the workgroup
-
-constexpr int kNumConfigs = 8;
-constexpr int kGroupM = 8;
-
-template <class F>
-struct is_slab : std::false_type {};
-template <int BM, int BN, int NW, int BK, int RW>
-struct is_slab<SlabCfg<BM, BN, NW, BK, RW>> : std::true_type {};
 
 template <class C, class F>
 constexpr mg_config_desc describe(int id, const char* name) {
@@ -132,61 +98,6 @@ mg_status check_dtype(mg_dtype in, mg_dtype out) {
     } while (0)
 
 // ---- launch --------------------------------------------------------------------
-template <class C, int DT, bool EPI, int MODE>
-mg_status launch_cfg(const KArgs& a, int64_t grid, hipStream_t stream) {
-    (void)hipGetLastError();  // clear a stale error so the check below is ours
-    hipLaunchKernelGGL((gemm_tile_kernel<C, DT, EPI, MODE>), dim3((unsigned)grid), dim3(C::NT), 0, stream, a);
-    return hipGetLastError() == hipSuccess ? MG_OK : MG_ERR_HIP;
-}
-
-template <class F, int DT, bool EPI, int MODE>
-mg_status launch_fast(const KArgs& a, int64_t grid, hipStream_t stream) {
-    (void)hipGetLastError();
-    hipLaunchKernelGGL((gemm_dlds_kernel<F, DT, EPI, MODE>), dim3((unsigned)grid), dim3(F::NT), 0, stream, a);
-    return hipGetLastError() == hipSuccess ? MG_OK : MG_ERR_HIP;
-}
-
-template <class C, int DT>
-mg_status launch_general(bool epi, int mode, const KArgs& a, int64_t grid, hipStream_t s) {
-    if (mode == MODE_GROUPED) return launch_cfg<C, DT, false, MODE_GROUPED>(a, grid, s);
-    if (mode == MODE_PACKED_A) return launch_cfg<C, DT, false, MODE_PACKED_A>(a, grid, s);
-    return epi ? launch_cfg<C, DT, true, MODE_DENSE>(a, grid, s) : launch_cfg<C, DT, false, MODE_DENSE>(a, grid, s);
-}
-
-template <class F, int DT, bool EPI>
-mg_status launch_slab(const KArgs& a, int64_t grid, hipStream_t stream) {
-    (void)hipGetLastError();
-    hipLaunchKernelGGL((gemm_kslab_kernel<F, DT, EPI>), dim3((unsigned)grid), dim3(F::NT), 0, stream, a);
-    return hipGetLastError() == hipSuccess ? MG_OK : MG_ERR_HIP;
-}
-
-template <class F, int DT>
-mg_status launch_direct(bool epi, int mode, const KArgs& a, int64_t grid, hipStream_t s) {
-    if constexpr (is_slab<F>::value) {
-        (void)mode;
-        return epi ? launch_slab<F, DT, true>(a, grid, s) : launch_slab<F, DT, false>(a, grid, s);
-    } else {
-        if (mode == MODE_GROUPED) return launch_fast<F, DT, false, MODE_GROUPED>(a, grid, s);
-        return epi ? launch_fast<F, DT, true, MODE_DENSE>(a, grid, s)
-                   : launch_fast<F, DT, false, MODE_DENSE>(a, grid, s);
-    }
-}
-
-// F = void: the row has no direct-to-LDS kernel.
-template <class C, class F>
-mg_status launch_dt(int dt, bool epi, int mode, const KArgs& a, int64_t grid, hipStream_t s) {
-    if constexpr (!std::is_void<F>::value) {
-        const bool direct = mode != MODE_PACKED_A && !(is_slab<F>::value && mode == MODE_GROUPED) &&
-                            a.K % F::BK == 0 && a.N % 8 == 0 &&
-                            (int64_t)F::BM * a.lda * 2 < (int64_t)1 << 31 && 64 * a.ldb * 2 < (int64_t)1 << 31;
-        if (direct)
-            return dt == DT_F16 ? launch_direct<F, DT_F16>(epi, mode, a, grid, s)
-                                : launch_direct<F, DT_BF16>(epi, mode, a, grid, s);
-    }
-    return dt == DT_F16 ? launch_general<C, DT_F16>(epi, mode, a, grid, s)
-                        : launch_general<C, DT_BF16>(epi, mode, a, grid, s);
-}
-
 mg_status launch(int cfg, int dt, bool epi, int mode, KArgs& a, hipStream_t s) {
     const mg_config_desc& d = kTable[cfg];
     a.tiles_n = (int32_t)cdiv(a.N, d.bn);
@@ -204,14 +115,14 @@ mg_status launch(int cfg, int dt, bool epi, int mode, KArgs& a, hipStream_t s) {
     a.xcd_remap = d.xcd_remap;
     mg_status st;
     switch (cfg) {
-        case 0: st = launch_dt<Cfg0, Fast0>(dt, epi, mode, a, grid, s); break;
-        case 1: st = launch_dt<Cfg1, Fast1>(dt, epi, mode, a, grid, s); break;
-        case 2: st = launch_dt<Cfg2, Fast2>(dt, epi, mode, a, grid, s); break;
-        case 3: st = launch_dt<Cfg3, Fast3>(dt, epi, mode, a, grid, s); break;
-        case 4: st = launch_dt<Cfg4, Fast4>(dt, epi, mode, a, grid, s); break;
-        case 5: st = launch_dt<Cfg5, void>(dt, epi, mode, a, grid, s); break;
-        case 6: st = launch_dt<Cfg6, Fast6>(dt, epi, mode, a, grid, s); break;
-        case 7: st = launch_dt<Cfg7, Fast7>(dt, epi, mode, a, grid, s); break;
+        case 0: st = launch_row0(dt, epi, mode, a, grid, s); break;
+        case 1: st = launch_row1(dt, epi, mode, a, grid, s); break;
+        case 2: st = launch_row2(dt, epi, mode, a, grid, s); break;
+        case 3: st = launch_row3(dt, epi, mode, a, grid, s); break;
+        case 4: st = launch_row4(dt, epi, mode, a, grid, s); break;
+        case 5: st = launch_row5(dt, epi, mode, a, grid, s); break;
+        case 6: st = launch_row6(dt, epi, mode, a, grid, s); break;
+        case 7: st = launch_row7(dt, epi, mode, a, grid, s); break;
         default: return MG_ERR_BAD_CONFIG;
     }
     if (st == MG_OK) g_last.store(cfg);

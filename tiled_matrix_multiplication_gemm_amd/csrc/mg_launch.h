@@ -1,0 +1,70 @@
+// Kernel launchers: pick the direct-to-LDS, K-split or general kernel of a
+// table row for the problem and launch it.  Included by the per-row
+// translation units only.
+#pragma once
+
+#include "mg_table.h"
+
+namespace mg {
+
+template <class C, int DT, bool EPI, int MODE>
+mg_status launch_cfg(const KArgs& a, int64_t grid, hipStream_t stream) {
+    (void)hipGetLastError();  // clear a stale error so the check below is ours
+    hipLaunchKernelGGL((gemm_tile_kernel<C, DT, EPI, MODE>), dim3((unsigned)grid), dim3(C::NT), 0, stream, a);
+    return hipGetLastError() == hipSuccess ? MG_OK : MG_ERR_HIP;
+}
+
+template <class F, int DT, bool EPI, int MODE>
+mg_status launch_fast(const KArgs& a, int64_t grid, hipStream_t stream) {
+    (void)hipGetLastError();
+    hipLaunchKernelGGL((gemm_dlds_kernel<F, DT, EPI, MODE>), dim3((unsigned)grid), dim3(F::NT), 0, stream, a);
+    return hipGetLastError() == hipSuccess ? MG_OK : MG_ERR_HIP;
+}
+
+template <class C, int DT>
+mg_status launch_general(bool epi, int mode, const KArgs& a, int64_t grid, hipStream_t s) {
+    if (mode == MODE_GROUPED) return launch_cfg<C, DT, false, MODE_GROUPED>(a, grid, s);
+    if (mode == MODE_PACKED_A) return launch_cfg<C, DT, false, MODE_PACKED_A>(a, grid, s);
+    return epi ? launch_cfg<C, DT, true, MODE_DENSE>(a, grid, s) : launch_cfg<C, DT, false, MODE_DENSE>(a, grid, s);
+}
+
+template <class F, int DT, bool EPI>
+mg_status launch_slab(const KArgs& a, int64_t grid, hipStream_t stream) {
+    (void)hipGetLastError();
+    hipLaunchKernelGGL((gemm_kslab_kernel<F, DT, EPI>), dim3((unsigned)grid), dim3(F::NT), 0, stream, a);
+    return hipGetLastError() == hipSuccess ? MG_OK : MG_ERR_HIP;
+}
+
+template <class F, int DT>
+mg_status launch_direct(bool epi, int mode, const KArgs& a, int64_t grid, hipStream_t s) {
+    if constexpr (is_slab<F>::value) {
+        (void)mode;
+        return epi ? launch_slab<F, DT, true>(a, grid, s) : launch_slab<F, DT, false>(a, grid, s);
+    } else {
+        if (mode == MODE_GROUPED) return launch_fast<F, DT, false, MODE_GROUPED>(a, grid, s);
+        return epi ? launch_fast<F, DT, true, MODE_DENSE>(a, grid, s)
+                   : launch_fast<F, DT, false, MODE_DENSE>(a, grid, s);
+    }
+}
+
+// F = void: the row has no direct-to-LDS kernel.
+template <class C, class F>
+mg_status launch_dt(int dt, bool epi, int mode, const KArgs& a, int64_t grid, hipStream_t s) {
+    if constexpr (!std::is_void<F>::value) {
+        const bool direct = mode != MODE_PACKED_A && !(is_slab<F>::value && mode == MODE_GROUPED) &&
+                            a.K % F::BK == 0 && a.N % 8 == 0 &&
+                            (int64_t)F::BM * a.lda * 2 < (int64_t)1 << 31 && 64 * a.ldb * 2 < (int64_t)1 << 31;
+        if (direct)
+            return dt == DT_F16 ? launch_direct<F, DT_F16>(epi, mode, a, grid, s)
+                                : launch_direct<F, DT_BF16>(epi, mode, a, grid, s);
+    }
+    return dt == DT_F16 ? launch_general<C, DT_F16>(epi, mode, a, grid, s)
+                        : launch_general<C, DT_BF16>(epi, mode, a, grid, s);
+}
+
+}  // namespace mg
+
+#define MG_DEFINE_ROW(n, C, F)                                                                      \
+    namespace mg {                                                                                  \
+    MG_DECLARE_ROW(n) { return launch_dt<C, F>(dt, epi, mode, a, grid, s); }                       \
+    }

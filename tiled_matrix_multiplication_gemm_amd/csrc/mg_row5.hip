@@ -1,0 +1,4 @@
+// Kernels of table row 5 (see mg_table.h).
+#include "mg_launch.h"
+
+MG_DEFINE_ROW(5, Cfg5, void)

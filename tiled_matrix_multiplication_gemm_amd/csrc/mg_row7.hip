@@ -1,0 +1,4 @@
+// Kernels of table row 7 (see mg_table.h).
+#include "mg_launch.h"
+
+MG_DEFINE_ROW(7, Cfg7, Fast7)

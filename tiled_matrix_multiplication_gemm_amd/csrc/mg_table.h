@@ -1,0 +1,62 @@
+// The table of compiled tile shapes, shared by the host code and the
+// per-row translation units that instantiate the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <type_traits>
+#include <stdint.h>
+
+#include "mi355gemm.h"
+#include "mg_tile.h"
+#include "mg_dlds.h"
+#include "mg_kslab.h"
+
+namespace mg {
+
+// ---- configuration table ---------------------------------------------------
+// One row per compiled tile shape.  The table is static: rows are chosen by
+// shape class in select_config(), which an offline sweep tunes; there is no
+// run-time search.
+// Each row has a general kernel (register-staged loads, any K and N) and,
+// where BK = 64, a direct-to-LDS fast kernel used when K % 64 == 0 and
+// N % 8 == 0.
+using Cfg0 = TileCfg<256, 256, 64, 2, 4>;  // large square problems, eight waves (two per SIMD)
+using Cfg1 = TileCfg<128, 128, 64, 2, 2>;  // mid-size, grouped
+using Cfg2 = TileCfg<64, 64, 64, 2, 2>;    // small problems: enough tiles to fill 256 CUs
+using Cfg3 = TileCfg<128, 256, 64, 2, 2>;
+using Cfg4 = TileCfg<256, 128, 64, 2, 2>;
+using Cfg5 = TileCfg<128, 128, 32, 2, 2>;
+using Cfg6 = TileCfg<256, 256, 64, 2, 4>;  // general fallback keeps eight waves
+// fast kernels: <BM, BN, waves M, waves N, K slice, LDS ring slots>
+using Fast0 = DldsCfg<256, 256, 2, 4, 32, 5>;
+using Fast1 = DldsCfg<128, 128, 2, 2, 64, 3>;
+using Fast2 = DldsCfg<64, 64, 2, 2, 64, 6>;
+using Fast3 = DldsCfg<128, 256, 2, 2, 32, 4>;
+using Fast4 = DldsCfg<256, 128, 2, 2, 32, 4>;
+using Fast6 = DldsCfg<256, 256, 2, 2, 32, 5>;
+using Cfg7 = TileCfg<64, 64, 64, 2, 2>;
+using Fast7 = SlabCfg<64, 64, 4, 32, 4>;  // K split over the 4 waves of the workgroup
+
+inline constexpr int kNumConfigs = 8;
+inline constexpr int kGroupM = 8;
+
+template <class F>
+struct is_slab : std::false_type {};
+template <int BM, int BN, int NW, int BK, int RW>
+struct is_slab<SlabCfg<BM, BN, NW, BK, RW>> : std::true_type {};
+
+// Launch row `cfg` (0 .. kNumConfigs-1) on stream s; defined one per row in
+// mg_row<cfg>.hip so that the rows compile in parallel.
+#define MG_DECLARE_ROW(n)                                                                                   \
+    mg_status launch_row##n(int dt, bool epi, int mode, const KArgs& a, int64_t grid, hipStream_t s)
+MG_DECLARE_ROW(0);
+MG_DECLARE_ROW(1);
+MG_DECLARE_ROW(2);
+MG_DECLARE_ROW(3);
+MG_DECLARE_ROW(4);
+MG_DECLARE_ROW(5);
+MG_DECLARE_ROW(6);
+MG_DECLARE_ROW(7);
+
+}  // namespace mg
