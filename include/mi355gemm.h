@@ -42,7 +42,8 @@ typedef enum {
     MG_OK = 0,
     MG_ERR_INVALID_ARG = 1,        /* null pointer with a nonzero extent, negative size, bad count */
     MG_ERR_UNSUPPORTED_DTYPE = 2,  /* dtype not fp16/bf16, or input and output types differ        */
-    MG_ERR_UNSUPPORTED_LAYOUT = 3, /* inner stride != 1, or leading stride shorter than a row       */
+    MG_ERR_UNSUPPORTED_LAYOUT = 3, /* no unit stride, leading stride shorter than a row, or a
+                                      transposed operand on a shape the direct kernels cannot take  */
     MG_ERR_MISALIGNED = 4,         /* base pointer not 16-byte aligned or leading stride % 8 != 0   */
     MG_ERR_HIP = 5,                /* the HIP runtime reported an error when launching               */
     MG_ERR_BAD_CONFIG = 6          /* unknown configuration id, or a BK the configuration cannot use */
@@ -59,9 +60,20 @@ const char* mg_status_string(mg_status status);
  * The tiled product of the pages' minimal kernel ("Using Triton to optimise
  * GEMM across chips", section 2.1; Gluon matmul example): the output is cut
  * into BM x BN tiles, each tile accumulates BK-wide slices of A and B.
- * A: M x K, row stride stride_am, inner stride stride_ak (must be 1).
- * B: K x N, row stride stride_bk, inner stride stride_bn (must be 1).
+ * A: M x K, element (m, k) at A + m*stride_am + k*stride_ak: either
+ *    stride_ak == 1 (row-major) or stride_am == 1 (A given transposed,
+ *    stored K x M with row stride stride_ak).
+ * B: K x N, element (k, n) at B + k*stride_bk + n*stride_bn: either
+ *    stride_bn == 1 (row-major) or stride_bk == 1 (B given transposed,
+ *    stored N x K with row stride stride_bn).
  * C: M x N, row stride stride_cm, inner stride stride_cn (must be 1).
+ * Strides are in elements; a transposed view is a swap of the two strides
+ * (the strided 2-D view of "Triton study notes", section 1.2).  The stored
+ * row stride of each operand must be a multiple of 8 and at least its row
+ * length; any other stride pattern is MG_ERR_UNSUPPORTED_LAYOUT.  A
+ * transposed operand is supported on the direct-to-LDS kernels only, i.e.
+ * when K is a multiple of the chosen row's K slice, N % 8 == 0 and, for a
+ * transposed A, M % 8 == 0; otherwise MG_ERR_UNSUPPORTED_LAYOUT.
  */
 mg_status mg_gemm(const void* A, const void* B, void* C,
                   int64_t M, int64_t N, int64_t K,

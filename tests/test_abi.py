@@ -62,9 +62,24 @@ def test_status_strings(L):
     (dict(sam=32), LAYOUT), (dict(sbk=8), LAYOUT),
     (dict(A=P + 2), MISALIGNED), (dict(B=P + 8), MISALIGNED), (dict(C=P + 4), MISALIGNED),
     (dict(sam=68), MISALIGNED), (dict(scm=100), MISALIGNED),
+    # transposed operands (unit stride along M for A, along K for B)
+    (dict(sam=1, sak=32), LAYOUT), (dict(sam=1, sak=68), MISALIGNED), (dict(sbk=1, sbn=32), LAYOUT),
+    (dict(sbk=1, sbn=68), MISALIGNED), (dict(sam=1, sak=64, M=60), LAYOUT),
+    (dict(sam=1, sak=64, K=40), LAYOUT), (dict(sbk=1, sbn=64, K=40, sam=40), LAYOUT),
 ])
 def test_gemm_rejects_bad_arguments(L, kw, status):
     assert gemm(L, **kw) == status
+
+
+def test_transposed_operands_need_a_direct_row(L):
+    # rows without a direct-to-LDS kernel (general-only, K split) refuse transposed operands
+    for cid in (5, 7):
+        assert L.mg_set_config(cid) == OK
+        try:
+            assert gemm(L, sam=1, sak=64) == LAYOUT
+            assert gemm(L, sbk=1, sbn=64) == LAYOUT
+        finally:
+            assert L.mg_set_config(-1) == OK
 
 
 def test_zero_sized_problems_are_noops(L):

@@ -206,6 +206,95 @@ def test_large_ragged_edges_sampled(orc, integer):
         assert_tolerance(got[rows, cols], ref, dt, c.name)
 
 
+# Transposed operands (strides swapped, "Triton study notes" section 1.2):
+# shapes the direct-to-LDS rows take (K a multiple of 64, N and M multiples
+# of 8), with ragged tile edges, on every row that has such a kernel.
+TRANSPOSED = [(64, 64, 64), (8, 8, 64), (72, 200, 128), (264, 136, 320), (520, 512, 256), (128, 264, 192)]
+DIRECT_ROWS = [0, 1, 2, 3, 4, 6]
+
+
+def stored_transposed(bits, dt):
+    """bits ([R,C]) handed over as the transposed view of its transpose,
+    stored [C,R] with the row stride rounded up to a multiple of 8."""
+    R, C = bits.shape
+    ld = (R + 7) // 8 * 8
+    full = np.zeros((C, ld), dtype=np.uint16)
+    full[:, :R] = bits.T
+    return to_dev(full, dt)[:, :R].t()
+
+
+def run_transposed(case, ta, tb, cfg=-1):
+    """Run a dense case with A and/or B handed over as transposed views of
+    their transposes (stored [K,M] / [N,K]); returns (bits, guards intact)."""
+    import torch
+
+    dt = case.dtype
+    A = stored_transposed(case.A, dt) if ta else to_dev(case.A, dt)
+    B = stored_transposed(case.B, dt) if tb else to_dev(case.B, dt)
+    assert (A.stride(0) == 1) == bool(ta) or case.M == 1 or case.K == 1
+    out = Guarded(case.M, case.N, dt)
+    mg.mg_set_config(cfg)
+    try:
+        if case.bias is not None:
+            mg.mg_gemm_bias_relu(A, B, to_dev(case.bias, dt), out=out.mat)
+        else:
+            mg.mg_gemm(A, B, out=out.mat)
+        torch.cuda.synchronize()
+    finally:
+        mg.mg_set_config(-1)
+    return out.result(), out.guards_intact()
+
+
+@pytest.mark.parametrize("cfg", DIRECT_ROWS)
+@pytest.mark.parametrize("ta,tb", [(1, 0), (0, 1), (1, 1)])
+def test_transposed_operands_every_direct_row(orc, cfg, ta, tb):
+    for i, (M, N, K) in enumerate(TRANSPOSED):
+        for dtype in (F16, BF16):
+            for integer in (True, False):
+                epi = (i + integer) % 2 == 1
+                seed = 5000 + 10 * i + 2 * integer + dtype
+                if integer:
+                    c = inputs.integer_dense(M, N, K, dtype, seed, epilogue=epi, name="transposed")
+                else:
+                    c = inputs.random_dense(M, N, K, dtype, seed, epilogue=epi, name="transposed")
+                announce("transposed ta=%d tb=%d cfg=%d M=%d N=%d K=%d dt=%d int=%s epi=%s" %
+                         (ta, tb, cfg, M, N, K, dtype, integer, epi))
+                got, guards = run_transposed(c, ta, tb, cfg)
+                assert guards, "write outside the output"
+                ref, ref_q = orc.gemm(c.A, c.B, dtype, bias=c.bias, relu=c.relu)
+                if integer:
+                    assert_bitexact(got, ref_q, dtype, c.name)
+                else:
+                    assert_tolerance(got, ref, dtype, c.name)
+
+
+def test_transposed_operands_outside_the_direct_kernels_are_refused():
+    # a transposed A needs M % 8 == 0; K must fill whole slices
+    for (M, N, K, ta, tb) in [(70, 64, 64, 1, 0), (64, 64, 40, 1, 0), (64, 64, 40, 0, 1)]:
+        c = inputs.integer_dense(M, N, K, F16, 7, name="refused")
+        announce("transposed refused M=%d N=%d K=%d ta=%d tb=%d" % (M, N, K, ta, tb))
+        with pytest.raises(RuntimeError, match="UNSUPPORTED_LAYOUT"):
+            run_transposed(c, ta, tb)
+
+
+@pytest.mark.parametrize("ta,tb", [(1, 0), (0, 1), (1, 1)])
+def test_transposed_large_sampled(orc, ta, tb):
+    """4096 x 4096 x 4096 bf16 on the 256x256 row with transposed operands:
+    sampled positions and the edge set against the oracle, Freivalds screen."""
+    M = N = K = 4096
+    c = inputs.random_dense(M, N, K, BF16, 6000 + 2 * ta + tb, name="transposed_large")
+    announce("transposed large ta=%d tb=%d" % (ta, tb))
+    got, guards = run_transposed(c, ta, tb)
+    assert guards
+    rows, cols = compare.sample_positions(M, N, 4096, 6100)
+    er, ec = compare.edge_positions(M, N)
+    rows, cols = np.concatenate([rows, er]), np.concatenate([cols, ec])
+    ref, _ = orc.gemm_sampled(c.A, c.B, BF16, rows, cols)
+    assert_tolerance(got[rows, cols], ref, BF16, c.name)
+    bad = compare.freivalds_rows(got, compare.to_f64(c.A, BF16), compare.to_f64(c.B, BF16), BF16, seed=7)
+    assert bad.size == 0, "Freivalds screen fails on rows %s" % bad[:10]
+
+
 def run_grouped(case):
     import torch
 

@@ -98,7 +98,7 @@ mg_status check_dtype(mg_dtype in, mg_dtype out) {
     } while (0)
 
 // ---- launch --------------------------------------------------------------------
-mg_status launch(int cfg, int dt, bool epi, int mode, KArgs& a, hipStream_t s) {
+mg_status launch(int cfg, int dt, bool epi, int mode, KArgs& a, hipStream_t s, int ta = 0, int tb = 0) {
     const mg_config_desc& d = kTable[cfg];
     a.tiles_n = (int32_t)cdiv(a.N, d.bn);
     int64_t grid;
@@ -115,14 +115,14 @@ mg_status launch(int cfg, int dt, bool epi, int mode, KArgs& a, hipStream_t s) {
     a.xcd_remap = d.xcd_remap;
     mg_status st;
     switch (cfg) {
-        case 0: st = launch_row0(dt, epi, mode, a, grid, s); break;
-        case 1: st = launch_row1(dt, epi, mode, a, grid, s); break;
-        case 2: st = launch_row2(dt, epi, mode, a, grid, s); break;
-        case 3: st = launch_row3(dt, epi, mode, a, grid, s); break;
-        case 4: st = launch_row4(dt, epi, mode, a, grid, s); break;
-        case 5: st = launch_row5(dt, epi, mode, a, grid, s); break;
-        case 6: st = launch_row6(dt, epi, mode, a, grid, s); break;
-        case 7: st = launch_row7(dt, epi, mode, a, grid, s); break;
+        case 0: st = launch_row0(dt, epi, mode, ta, tb, a, grid, s); break;
+        case 1: st = launch_row1(dt, epi, mode, ta, tb, a, grid, s); break;
+        case 2: st = launch_row2(dt, epi, mode, ta, tb, a, grid, s); break;
+        case 3: st = launch_row3(dt, epi, mode, ta, tb, a, grid, s); break;
+        case 4: st = launch_row4(dt, epi, mode, ta, tb, a, grid, s); break;
+        case 5: st = launch_row5(dt, epi, mode, ta, tb, a, grid, s); break;
+        case 6: st = launch_row6(dt, epi, mode, ta, tb, a, grid, s); break;
+        case 7: st = launch_row7(dt, epi, mode, ta, tb, a, grid, s); break;
         default: return MG_ERR_BAD_CONFIG;
     }
     if (st == MG_OK) g_last.store(cfg);
@@ -134,8 +134,15 @@ mg_status gemm_common(const void* A, const void* B, const void* bias, void* C, i
                       mg_dtype in_dtype, mg_dtype out_dtype, bool epi, hipStream_t stream) {
     if (M < 0 || N < 0 || K < 0) return MG_ERR_INVALID_ARG;
     MG_TRY(check_dtype(in_dtype, out_dtype));
-    MG_TRY(check_matrix(A, M, K, sam, sak));
-    MG_TRY(check_matrix(B, K, N, sbk, sbn));
+    // A is row-major (unit stride along K) or given transposed (unit stride
+    // along M, i.e. stored [K,M]); likewise B row-major (unit stride along N)
+    // or transposed (unit stride along K, stored [N,K]).  The row-major
+    // reading wins when both strides are 1 (a single row or column).
+    const int ta = (sak == 1 || K <= 1) ? 0 : ((sam == 1 || M <= 1) ? 1 : -1);
+    const int tb = (sbn == 1 || N <= 1) ? 0 : ((sbk == 1 || K <= 1) ? 1 : -1);
+    if (ta < 0 || tb < 0) return MG_ERR_UNSUPPORTED_LAYOUT;
+    MG_TRY(ta ? check_matrix(A, K, M, sak, sam) : check_matrix(A, M, K, sam, sak));
+    MG_TRY(tb ? check_matrix(B, N, K, sbn, sbk) : check_matrix(B, K, N, sbk, sbn));
     MG_TRY(check_matrix(C, M, N, scm, scn));
     if (epi && N > 0 && M > 0 && bias == nullptr) return MG_ERR_INVALID_ARG;
     if (M == 0 || N == 0) return MG_OK;
@@ -147,8 +154,10 @@ mg_status gemm_common(const void* A, const void* B, const void* bias, void* C, i
     a.C = (uint16_t*)C;
     a.bias = (const uint16_t*)bias;
     a.M = M; a.N = N; a.K = K;
-    a.lda = sam; a.ldb = sbk; a.ldc = scm;
-    return launch(cfg, (int)in_dtype, epi, MODE_DENSE, a, stream);
+    a.lda = ta ? sak : sam;  // stride between the stored rows
+    a.ldb = tb ? sbn : sbk;
+    a.ldc = scm;
+    return launch(cfg, (int)in_dtype, epi, MODE_DENSE, a, stream, ta, tb);
 }
 
 }  // namespace

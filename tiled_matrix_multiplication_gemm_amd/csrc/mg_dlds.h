@@ -100,6 +100,79 @@ __device__ __forceinline__ int swz_a(int row) {
 template <int BCH>
 __device__ __forceinline__ int swz_b(int krow) { return (4 * (krow & 3)) & (BCH - 1); }
 
+// The two operand layouts.  The MFMA wants, for each of 32 rows (of A) or
+// columns (of B), 8 consecutive k values per lane.
+//
+// K-major (A as stored row-major [M,K]; B given transposed, [N,K]): E lines
+// (rows of A or columns of B) whose K elements are contiguous, stored in LDS
+// as E lines of BK*2 bytes with swizzled 16-byte chunks; a fragment is one
+// ds_read_b128 of a chunk column over 32 lines.
+//
+// MN-major (B as stored row-major [K,N]; A given transposed, [K,M]): BK
+// k-rows whose E elements are contiguous, stored as k-rows of E*2 bytes; a
+// fragment is two transposing reads (ds_read_b64_tr_b16) per lane.
+//
+// Both give lane l the k values 16s + 8 (l / 32) + {0..7} of line l % 32 in
+// the same order, so any pairing of the two layouts feeds the MFMA.  A slice
+// is E*BK*2 bytes either way, loaded as 1 KB direct loads split over the NW
+// waves; lines (K-major) or 8-element chunks (MN-major) past the extent are
+// clamped to the last valid ones.
+template <int E, int BK, int NW>
+struct OpKM {
+    static constexpr int CH = BK / 8, LINE = BK * 2, BYTES = E * LINE, J = BYTES / 1024 / NW;
+    // byte offset (from the tile's first line of the slice) of load j of wave w, lane l
+    __device__ static uint32_t load_off(int w, int j, int lane, int64_t e0, int64_t ext, int64_t ld) {
+        const int q = w * J + j;
+        const int line = q * (1024 / LINE) + lane / CH;
+        const int c = (lane % CH) ^ swz_a<CH>(line);
+        const int64_t r = (e0 + line < ext ? line : ext - 1 - e0);
+        return (uint32_t)((r * ld + 8 * c) * 2);
+    }
+    __device__ static const char* tile_base(const uint16_t* p, int64_t e0, int64_t ld) {
+        return (const char*)(p + e0 * ld);
+    }
+    __device__ static int64_t slice_bytes(int64_t) { return (int64_t)BK * 2; }
+    // per-lane LDS offset of 32-line block b of a wave whose lines start at woff
+    __device__ static int frag_off(int woff, int b, int lane) { return (woff + b * 32 + (lane & 31)) * LINE; }
+    __device__ static u32x4 read(const char* part, int off, int woff, int b, int s, int lane) {
+        const int line = woff + b * 32 + (lane & 31);
+        const int c = (2 * s + (lane >> 5)) ^ swz_a<CH>(line);
+        return *(const lds_u32x4_t*)(part + off + c * 16);
+    }
+};
+
+template <int E, int BK, int NW>
+struct OpMN {
+    static constexpr int CH = E / 8, LINE = E * 2, BYTES = BK * LINE, J = BYTES / 1024 / NW;
+    __device__ static uint32_t load_off(int w, int j, int lane, int64_t e0, int64_t ext, int64_t ld) {
+        const int q = w * J + j;
+        const int krow = q * (512 / E) + (8 * lane) / E;
+        const int c = (lane % CH) ^ swz_b<CH>(krow);
+        const int64_t cn = (e0 + 8 * c <= ext - 8) ? 8 * c : ext - 8 - e0;
+        return (uint32_t)((krow * ld + cn) * 2);
+    }
+    __device__ static const char* tile_base(const uint16_t* p, int64_t e0, int64_t) { return (const char*)(p + e0); }
+    __device__ static int64_t slice_bytes(int64_t ld) { return (int64_t)BK * ld * 2; }
+    // lane l reads, through k-row 8 (g16 / 2) + t16 / 4, the piece of 4 lines
+    // 16 (g16 % 2) + 4 (t16 % 4) .. of the block (g16, t16: lane's group of
+    // 16 and index in it); the swizzle depends on the k-row modulo 4 only
+    __device__ static int frag_off(int woff, int b, int lane) {
+        const int g16 = lane >> 4, t16 = lane & 15;
+        const int n = woff + b * 32 + 16 * (g16 & 1) + 4 * (t16 & 3);
+        const int kr = 8 * (g16 >> 1) + (t16 >> 2);
+        return kr * LINE + ((n >> 3) ^ swz_b<CH>(kr)) * 16 + (n & 7) * 2;
+    }
+    __device__ static u32x4 read(const char* part, int off, int, int, int s, int) {
+        // k-rows 16s + {0..3} and 16s + {4..7} (+8 for the upper half-wave)
+        const i16x4 lo = lds_read_tr16(part + off + (16 * s) * LINE);
+        const i16x4 hi = lds_read_tr16(part + off + (16 * s + 4) * LINE);
+        return u32x4{__builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 0, 1)),
+                     __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 2, 3)),
+                     __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 0, 1)),
+                     __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 2, 3))};
+    }
+};
+
 // s_waitcnt vmcnt(N): wait until at most N vector memory operations of this
 // wave are outstanding.
 template <int N>
@@ -122,7 +195,7 @@ __device__ __forceinline__ void ring_barrier() {
 }
 
 // One LDS ring slot: a distinct shared-memory object per (slot index, kernel).
-template <class Cfg, int DT, bool EPI, int MODE>
+template <class Cfg, int DT, bool EPI, int MODE, bool TA, bool TB>
 struct DldsTag {};
 template <int BYTES, int I, class Tag>
 __device__ __forceinline__ char* lds_slot() {
@@ -130,16 +203,21 @@ __device__ __forceinline__ char* lds_slot() {
     return buf;
 }
 
-template <class Cfg, int DT, bool EPI, int MODE>
+// TA: A is given transposed (stored [K,M], lda = its k-row stride);
+// TB: B is given transposed (stored [N,K], ldb = its row stride).
+template <class Cfg, int DT, bool EPI, int MODE, bool TA = false, bool TB = false>
 __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;
-    constexpr int FM = Cfg::FM, FN = Cfg::FN, JA = Cfg::JA, JB = Cfg::JB, BCH = Cfg::BCH;
-    constexpr int ACH = Cfg::ACH, AROW = Cfg::AROW, STEPS = Cfg::STEPS, R = Cfg::R;
+    constexpr int FM = Cfg::FM, FN = Cfg::FN, JA = Cfg::JA, JB = Cfg::JB;
+    constexpr int STEPS = Cfg::STEPS, R = Cfg::R;
     // R ring slots of [A slice | B slice], each its own LDS object so that the
     // compiler can tell reads of one slot from direct loads landing in another
     // (a single array would make it wait for every load in flight before each
     // LDS read).
-    using Tag = DldsTag<Cfg, DT, EPI, MODE>;
+    using Tag = DldsTag<Cfg, DT, EPI, MODE, TA, TB>;
+    using OA = std::conditional_t<TA, OpMN<Cfg::BM, Cfg::BK, Cfg::NW>, OpKM<Cfg::BM, Cfg::BK, Cfg::NW>>;
+    using OB = std::conditional_t<TB, OpKM<Cfg::BN, Cfg::BK, Cfg::NW>, OpMN<Cfg::BN, Cfg::BK, Cfg::NW>>;
+    static_assert(OA::J == Cfg::JA && OB::J == Cfg::JB, "operand slices split like the ring");
     auto slot_ptr = [&](int i) -> char* {  // i is a compile-time constant at every use
         switch (i) {
             case 0: return lds_slot<Cfg::SLOT, 0, Tag>();
@@ -185,35 +263,21 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
     const int nk = (int)(K / BK);
 
     // ---- per-lane source offsets of the direct loads ---------------------
-    // Offsets are 32-bit byte offsets from a workgroup-uniform base that
-    // advances by one k-slice per step (the host guarantees they fit).
-    // A: load q = wave*JA + j fills bytes [q KB, q KB + 1 KB) of a slice,
-    //    i.e. 1024/AROW rows; lane L lands in row q*1024/AROW + L/ACH, physical
-    //    chunk L%ACH, and therefore fetches logical chunk (L%ACH) ^ swz_a(row).
+    // 32-bit byte offsets from a workgroup-uniform base that advances by one
+    // k-slice per step (the host guarantees they fit).  Load q = wave*J + j
+    // of an operand fills bytes [q KB, q KB + 1 KB) of its part of the slot;
+    // lane L lands at 16 L in it and fetches the logical chunk whose
+    // swizzled position that is.
     uint32_t offA_g[JA];
 #pragma unroll
-    for (int j = 0; j < JA; ++j) {
-        const int q = wave * JA + j;
-        const int row = q * (1024 / AROW) + lane / ACH;
-        const int c = (lane % ACH) ^ swz_a<ACH>(row);
-        const int64_t r = (m0 + row < M ? row : M - 1 - m0);
-        offA_g[j] = (uint32_t)((r * args.lda + 8 * c) * 2);
-    }
-    // B: load q covers k-rows (512/BN) q .. ; lane L lands in k-row
-    //    q*512/BN + 8L/BN, physical chunk L % BCH.
+    for (int j = 0; j < JA; ++j) offA_g[j] = OA::load_off(wave, j, lane, m0, M, args.lda);
     uint32_t offB_g[JB];
 #pragma unroll
-    for (int j = 0; j < JB; ++j) {
-        const int q = wave * JB + j;
-        const int krow = q * (512 / BN) + (8 * lane) / BN;
-        const int c = (lane % BCH) ^ swz_b<BCH>(krow);
-        const int64_t cn = (n0 + 8 * c <= N - 8) ? 8 * c : N - 8 - n0;
-        offB_g[j] = (uint32_t)((krow * args.ldb + cn) * 2);
-    }
-    const char* baseA = (const char*)(Ag + m0 * args.lda);
-    const char* baseB = (const char*)(Bg + n0);
-    const int64_t stepA = (int64_t)BK * 2;              // bytes per k-slice
-    const int64_t stepB = (int64_t)BK * args.ldb * 2;
+    for (int j = 0; j < JB; ++j) offB_g[j] = OB::load_off(wave, j, lane, n0, N, args.ldb);
+    const char* baseA = OA::tile_base(Ag, m0, args.lda);
+    const char* baseB = OB::tile_base(Bg, n0, args.ldb);
+    const int64_t stepA = OA::slice_bytes(args.lda);  // bytes per k-slice
+    const int64_t stepB = OB::slice_bytes(args.ldb);
 
     // direct loads of k-slice kt into ring slot `slot` (a compile-time index)
     // (buffer resources rebased on the slice: offsets stay below 2^31)
@@ -237,19 +301,15 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     // ---- operand fragments ------------------------------------------------
-    // Fragments of one k16 step: FM A fragments (ds_read_b128 of one swizzled
-    // chunk of 32 rows) and FN B fragments (two transposing reads each).
-    // Two register sets alternate so that the reads of step s+1 are in flight
+    // Fragments of one k16 step: FM A fragments and FN B fragments (one
+    // ds_read_b128 each if K-major, two transposing reads if MN-major).  Two
+    // register sets alternate so that the reads of step s+1 are in flight
     // while the MFMAs of step s issue.
-    const int rowA0 = wm * Cfg::WTM + (lane & 31);
-    const int g16 = lane >> 4, t16 = lane & 15;
-    int offBj[FN];  // byte offset of this lane's B piece in k-row (t16 >> 2), per n fragment
+    int offAi[FM], offBj[FN];  // per-lane LDS offsets of the fragment blocks
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-        const int n = wn * Cfg::WTN + j * 32 + 16 * (g16 & 1) + 4 * (t16 & 3);
-        const int kr = 8 * (g16 >> 1) + (t16 >> 2);  // swizzle only depends on kr & 3
-        offBj[j] = kr * (2 * BN) + ((n >> 3) ^ swz_b<BCH>(kr)) * 16 + (n & 7) * 2;
-    }
+    for (int i = 0; i < FM; ++i) offAi[i] = OA::frag_off(wm * Cfg::WTM, i, lane);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) offBj[j] = OB::frag_off(wn * Cfg::WTN, j, lane);
     struct Frags {
         u32x4 a[FM], b[FN];
     };
@@ -262,21 +322,11 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
             if (i >= lv) break;
-            const int row = rowA0 + i * 32;
-            const int c = (2 * s + (lane >> 5)) ^ swz_a<ACH>(row);
-            f.a[i] = *(const lds_u32x4_t*)(sa + row * AROW + c * 16);
+            f.a[i] = OA::read(sa, offAi[i], wm * Cfg::WTM, i, s, lane);
         }
         if (lv == 0) return;
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            // k-rows 16s + {0..3} and 16s + {4..7} (+8 for the upper half-wave)
-            const i16x4 lo = lds_read_tr16(sb + offBj[j] + (16 * s) * (2 * BN));
-            const i16x4 hi = lds_read_tr16(sb + offBj[j] + (16 * s + 4) * (2 * BN));
-            f.b[j] = u32x4{__builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 0, 1)),
-                           __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 2, 3)),
-                           __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 0, 1)),
-                           __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 2, 3))};
-        }
+        for (int j = 0; j < FN; ++j) f.b[j] = OB::read(sb, offBj[j], wn * Cfg::WTN, j, s, lane);
     };
     auto mfma_step = [&](const Frags& f, auto lv) {
 #pragma unroll

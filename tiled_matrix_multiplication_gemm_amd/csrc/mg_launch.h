@@ -14,11 +14,21 @@ mg_status launch_cfg(const KArgs& a, int64_t grid, hipStream_t stream) {
     return hipGetLastError() == hipSuccess ? MG_OK : MG_ERR_HIP;
 }
 
-template <class F, int DT, bool EPI, int MODE>
+template <class F, int DT, bool EPI, int MODE, bool TA = false, bool TB = false>
 mg_status launch_fast(const KArgs& a, int64_t grid, hipStream_t stream) {
     (void)hipGetLastError();
-    hipLaunchKernelGGL((gemm_dlds_kernel<F, DT, EPI, MODE>), dim3((unsigned)grid), dim3(F::NT), 0, stream, a);
+    hipLaunchKernelGGL((gemm_dlds_kernel<F, DT, EPI, MODE, TA, TB>), dim3((unsigned)grid), dim3(F::NT), 0, stream,
+                       a);
     return hipGetLastError() == hipSuccess ? MG_OK : MG_ERR_HIP;
+}
+
+// dense GEMM on the direct-to-LDS kernel with A and/or B given transposed
+template <class F, int DT, bool EPI>
+mg_status launch_fast_t(int ta, int tb, const KArgs& a, int64_t grid, hipStream_t s) {
+    if (ta && tb) return launch_fast<F, DT, EPI, MODE_DENSE, true, true>(a, grid, s);
+    if (ta) return launch_fast<F, DT, EPI, MODE_DENSE, true, false>(a, grid, s);
+    if (tb) return launch_fast<F, DT, EPI, MODE_DENSE, false, true>(a, grid, s);
+    return launch_fast<F, DT, EPI, MODE_DENSE>(a, grid, s);
 }
 
 template <class C, int DT>
@@ -36,28 +46,40 @@ mg_status launch_slab(const KArgs& a, int64_t grid, hipStream_t stream) {
 }
 
 template <class F, int DT>
-mg_status launch_direct(bool epi, int mode, const KArgs& a, int64_t grid, hipStream_t s) {
+mg_status launch_direct(bool epi, int mode, int ta, int tb, const KArgs& a, int64_t grid, hipStream_t s) {
     if constexpr (is_slab<F>::value) {
-        (void)mode;
+        (void)mode, (void)ta, (void)tb;
         return epi ? launch_slab<F, DT, true>(a, grid, s) : launch_slab<F, DT, false>(a, grid, s);
     } else {
         if (mode == MODE_GROUPED) return launch_fast<F, DT, false, MODE_GROUPED>(a, grid, s);
-        return epi ? launch_fast<F, DT, true, MODE_DENSE>(a, grid, s)
-                   : launch_fast<F, DT, false, MODE_DENSE>(a, grid, s);
+        return epi ? launch_fast_t<F, DT, true>(ta, tb, a, grid, s) : launch_fast_t<F, DT, false>(ta, tb, a, grid, s);
     }
 }
 
-// F = void: the row has no direct-to-LDS kernel.
+// Whether the direct-to-LDS kernel of row F takes this problem: K in whole
+// slices, N in whole 8-element chunks (and M too when A is given transposed,
+// its chunks then run along M), and every per-tile operand offset within
+// 31 bits (K-major operand: a tile's lines; MN-major: a slice's k-rows).
+template <class F>
+bool direct_fits(int mode, int ta, int tb, const KArgs& a) {
+    constexpr int64_t LIM = (int64_t)1 << 31;
+    if (mode == MODE_PACKED_A || (is_slab<F>::value && (mode == MODE_GROUPED || ta || tb))) return false;
+    if (a.K % F::BK != 0 || a.N % 8 != 0 || (ta && a.M % 8 != 0)) return false;
+    const int64_t a_span = ta ? 64 * a.lda * 2 : (int64_t)F::BM * a.lda * 2;
+    const int64_t b_span = tb ? (int64_t)F::BN * a.ldb * 2 : 64 * a.ldb * 2;
+    return a_span < LIM && b_span < LIM;
+}
+
+// F = void: the row has no direct-to-LDS kernel.  Transposed operands exist
+// on the direct-to-LDS kernel only.
 template <class C, class F>
-mg_status launch_dt(int dt, bool epi, int mode, const KArgs& a, int64_t grid, hipStream_t s) {
+mg_status launch_dt(int dt, bool epi, int mode, int ta, int tb, const KArgs& a, int64_t grid, hipStream_t s) {
     if constexpr (!std::is_void<F>::value) {
-        const bool direct = mode != MODE_PACKED_A && !(is_slab<F>::value && mode == MODE_GROUPED) &&
-                            a.K % F::BK == 0 && a.N % 8 == 0 &&
-                            (int64_t)F::BM * a.lda * 2 < (int64_t)1 << 31 && 64 * a.ldb * 2 < (int64_t)1 << 31;
-        if (direct)
-            return dt == DT_F16 ? launch_direct<F, DT_F16>(epi, mode, a, grid, s)
-                                : launch_direct<F, DT_BF16>(epi, mode, a, grid, s);
+        if (direct_fits<F>(mode, ta, tb, a))
+            return dt == DT_F16 ? launch_direct<F, DT_F16>(epi, mode, ta, tb, a, grid, s)
+                                : launch_direct<F, DT_BF16>(epi, mode, ta, tb, a, grid, s);
     }
+    if (ta || tb) return MG_ERR_UNSUPPORTED_LAYOUT;
     return dt == DT_F16 ? launch_general<C, DT_F16>(epi, mode, a, grid, s)
                         : launch_general<C, DT_BF16>(epi, mode, a, grid, s);
 }
@@ -66,5 +88,5 @@ mg_status launch_dt(int dt, bool epi, int mode, const KArgs& a, int64_t grid, hi
 
 #define MG_DEFINE_ROW(n, C, F)                                                                      \
     namespace mg {                                                                                  \
-    MG_DECLARE_ROW(n) { return launch_dt<C, F>(dt, epi, mode, a, grid, s); }                       \
+    MG_DECLARE_ROW(n) { return launch_dt<C, F>(dt, epi, mode, ta, tb, a, grid, s); }               \
     }

@@ -46,10 +46,12 @@ struct is_slab : std::false_type {};
 template <int BM, int BN, int NW, int BK, int RW>
 struct is_slab<SlabCfg<BM, BN, NW, BK, RW>> : std::true_type {};
 
-// Launch row `cfg` (0 .. kNumConfigs-1) on stream s; defined one per row in
-// mg_row<cfg>.hip so that the rows compile in parallel.
+// Launch row `cfg` (0 .. kNumConfigs-1) on stream s; ta / tb: A / B given
+// transposed.  Defined one per row in mg_row<cfg>.hip so that the rows
+// compile in parallel.
 #define MG_DECLARE_ROW(n)                                                                                   \
-    mg_status launch_row##n(int dt, bool epi, int mode, const KArgs& a, int64_t grid, hipStream_t s)
+    mg_status launch_row##n(int dt, bool epi, int mode, int ta, int tb, const KArgs& a, int64_t grid,     \
+                            hipStream_t s)
 MG_DECLARE_ROW(0);
 MG_DECLARE_ROW(1);
 MG_DECLARE_ROW(2);
