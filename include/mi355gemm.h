@@ -99,6 +99,26 @@ mg_status mg_gemm_bias_relu(const void* A, const void* B, const void* bias, void
                             mg_dtype in_dtype, mg_dtype out_dtype, hipStream_t stream);
 
 /*
+ * Batched GEMM in one launch: C_b = A_b * B_b for b = 0 .. batch-1, where
+ * entry b of each operand starts batch_stride_{a,b,c} elements after entry
+ * b-1 (the batched shapes of "Using Triton to optimise GEMM across chips",
+ * section 4.3).  Every entry has the layout mg_gemm() accepts, transposed
+ * operands included.  A stride of 0 repeats one A or B for every entry; C
+ * entries must not overlap (batch_stride_c >= M * stride_cm), otherwise
+ * MG_ERR_UNSUPPORTED_LAYOUT.  Batch strides are multiples of 8 (16-byte
+ * aligned entries), else MG_ERR_MISALIGNED; batch < 0 is MG_ERR_INVALID_ARG,
+ * batch == 0 does nothing.  Workgroups take the tiles of one entry after
+ * another, so one launch fills the GPU with many small products.
+ */
+mg_status mg_gemm_batched(const void* A, const void* B, void* C, int64_t batch,
+                          int64_t M, int64_t N, int64_t K,
+                          int64_t stride_am, int64_t stride_ak,
+                          int64_t stride_bk, int64_t stride_bn,
+                          int64_t stride_cm, int64_t stride_cn,
+                          int64_t batch_stride_a, int64_t batch_stride_b, int64_t batch_stride_c,
+                          mg_dtype in_dtype, mg_dtype out_dtype, hipStream_t stream);
+
+/*
  * Grouped GEMM for the expert layer of a mixture-of-experts model, in one
  * launch: for every expert e,
  *     Y[o_e : o_{e+1}, :] = X[o_e : o_{e+1}, :] * W[e]

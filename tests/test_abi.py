@@ -82,6 +82,25 @@ def test_transposed_operands_need_a_direct_row(L):
             assert L.mg_set_config(-1) == OK
 
 
+def gemm_batched(L, batch=2, A=P, B=P, C=P, M=64, N=64, K=64, sam=64, sak=1, sbk=64, sbn=1, scm=64, scn=1,
+                 sab=4096, sbb=4096, scb=4096, din=F16, dout=F16):
+    return L.mg_gemm_batched(A, B, C, batch, M, N, K, sam, sak, sbk, sbn, scm, scn, sab, sbb, scb, din, dout, S)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=-1), INVALID), (dict(sab=-8), INVALID), (dict(scb=-4096), INVALID),
+    (dict(scb=64 * 63), LAYOUT), (dict(sab=4100), MISALIGNED), (dict(sbb=12), MISALIGNED),
+    (dict(scb=4100), MISALIGNED), (dict(sak=2), LAYOUT), (dict(A=None), INVALID),
+])
+def test_gemm_batched_rejects_bad_arguments(L, kw, status):
+    assert gemm_batched(L, **kw) == status
+
+
+def test_gemm_batched_empty_batches_are_noops(L):
+    assert gemm_batched(L, batch=0, A=None, B=None, C=None) == OK
+    assert gemm_batched(L, M=0, A=None, C=None) == OK
+
+
 def test_zero_sized_problems_are_noops(L):
     # M == 0 or N == 0: nothing to compute, null pointers are fine
     assert gemm(L, A=None, C=None, M=0) == OK

@@ -295,6 +295,74 @@ def test_transposed_large_sampled(orc, ta, tb):
     assert bad.size == 0, "Freivalds screen fails on rows %s" % bad[:10]
 
 
+# Batched GEMM: one launch over all entries, each entry checked against the
+# dense oracle.  All rows (general, direct, K-split), ragged entries, a
+# repeated (stride-0) B, and transposed entries on a direct row.
+BATCHED = [(3, 70, 72, 96), (5, 64, 64, 64), (2, 300, 264, 192), (4, 129, 136, 64)]
+
+
+def run_batched(cases, cfg=-1, broadcast_b=False, ta=0, tb=0):
+    import torch
+
+    dt = cases[0].dtype
+    if ta:
+        A = torch.stack([stored_transposed(c.A, dt) for c in cases])
+    else:
+        A = to_dev(np.stack([c.A for c in cases]), dt)
+    if broadcast_b:
+        B = to_dev(cases[0].B, dt).unsqueeze(0).expand(len(cases), -1, -1)
+    elif tb:
+        B = torch.stack([stored_transposed(c.B, dt) for c in cases])
+    else:
+        B = to_dev(np.stack([c.B for c in cases]), dt)
+    if ta:  # torch.stack copies: rebuild the transposed strides of each entry
+        A = A.transpose(1, 2).contiguous().transpose(1, 2)
+    if tb:
+        B = B.transpose(1, 2).contiguous().transpose(1, 2)
+    M, N = cases[0].M, cases[0].N
+    out = Guarded(len(cases) * M, N, dt)
+    mg.mg_set_config(cfg)
+    try:
+        mg.mg_gemm_batched(A, B, out=out.mat.view(len(cases), M, N))
+        torch.cuda.synchronize()
+    finally:
+        mg.mg_set_config(-1)
+    return out.result().reshape(len(cases), M, N), out.guards_intact()
+
+
+@pytest.mark.parametrize("cfg", range(NUM_CONFIGS))
+def test_batched_every_config(orc, cfg):
+    for i, (nb, M, N, K) in enumerate(BATCHED):
+        for dtype in (F16, BF16):
+            for integer in (True, False):
+                gen = inputs.integer_dense if integer else inputs.random_dense
+                cases = [gen(M, N, K, dtype, 7000 + 100 * i + 10 * b + 2 * integer + dtype, name="batched")
+                         for b in range(nb)]
+                bcast = (i + integer) % 2 == 1
+                announce("batched cfg=%d b=%d M=%d N=%d K=%d dt=%d int=%s bcastB=%s" %
+                         (cfg, nb, M, N, K, dtype, integer, bcast))
+                got, guards = run_batched(cases, cfg, broadcast_b=bcast)
+                assert guards, "write outside the output"
+                for b, c in enumerate(cases):
+                    ref, ref_q = orc.gemm(c.A, cases[0].B if bcast else c.B, dtype)
+                    if integer:
+                        assert_bitexact(got[b], ref_q, dtype, "batched entry %d" % b)
+                    else:
+                        assert_tolerance(got[b], ref, dtype, "batched entry %d" % b)
+
+
+@pytest.mark.parametrize("ta,tb", [(1, 0), (0, 1), (1, 1)])
+def test_batched_transposed_entries(orc, ta, tb):
+    nb, M, N, K = 3, 264, 136, 192
+    cases = [inputs.integer_dense(M, N, K, BF16, 7500 + 10 * b + 2 * ta + tb, name="batched_t") for b in range(nb)]
+    announce("batched transposed ta=%d tb=%d" % (ta, tb))
+    got, guards = run_batched(cases, ta=ta, tb=tb)
+    assert guards
+    for b, c in enumerate(cases):
+        _, ref_q = orc.gemm(c.A, c.B, BF16)
+        assert_bitexact(got[b], ref_q, BF16, "batched transposed entry %d" % b)
+
+
 def run_grouped(case):
     import torch
 

@@ -38,7 +38,7 @@ class ConfigDesc(ctypes.Structure):
 
 
 EXPORTED = (
-    "mg_status_string", "mg_gemm", "mg_gemm_bias_relu", "mg_grouped_gemm", "mg_prepacked_bytes",
+    "mg_status_string", "mg_gemm", "mg_gemm_bias_relu", "mg_gemm_batched", "mg_grouped_gemm", "mg_prepacked_bytes",
     "mg_prepack_a", "mg_config_bk", "mg_gemm_prepacked", "mg_num_configs", "mg_config_info",
     "mg_set_config", "mg_last_config", "mg_select_config",
 )
@@ -64,6 +64,8 @@ def lib() -> ctypes.CDLL:
         L.mg_gemm.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, i64, cint, cint, vp]
         L.mg_gemm_bias_relu.restype = cint
         L.mg_gemm_bias_relu.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, i64, cint, cint, vp]
+        L.mg_gemm_batched.restype = cint
+        L.mg_gemm_batched.argtypes = [vp, vp, vp] + [i64] * 13 + [cint, cint, vp]
         L.mg_grouped_gemm.restype = cint
         L.mg_grouped_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, cint, vp]
         L.mg_prepacked_bytes.restype = ctypes.c_size_t
@@ -155,6 +157,26 @@ def mg_gemm_bias_relu(a, b, bias, out=None):
     return out
 
 
+def mg_gemm_batched(a, b, out=None):
+    """out[i] = a[i] @ b[i] for every batch entry i, in one launch.
+
+    a: [batch, M, K], b: [batch, K, N] (either may be an expanded view with
+    batch stride 0; each entry row-major or transposed as for mg_gemm)."""
+    import torch
+
+    _require_gpu(a, b)
+    if a.dim() != 3 or b.dim() != 3 or a.shape[0] != b.shape[0] or a.shape[2] != b.shape[1]:
+        raise RuntimeError("MG_ERR_INVALID_ARG: a[batch,M,K] and b[batch,K,N] expected")
+    batch, M, K = a.shape
+    N = b.shape[2]
+    if out is None:
+        out = torch.empty((batch, M, N), dtype=a.dtype, device=a.device)
+    _check(lib().mg_gemm_batched(a.data_ptr(), b.data_ptr(), out.data_ptr(), batch, M, N, K, a.stride(1),
+                                 a.stride(2), b.stride(1), b.stride(2), out.stride(1), out.stride(2), a.stride(0),
+                                 b.stride(0), out.stride(0), _dtype_code(a), _dtype_code(out), _stream(a)))
+    return out
+
+
 def mg_grouped_gemm(x, w, offsets, out=None):
     """out[o_e:o_{e+1}] = x[o_e:o_{e+1}] @ w[e] for every expert e (one launch).
 
@@ -243,6 +265,7 @@ def mg_select_config(M: int, N: int, K: int, dtype: int = MG_F16, grouped: bool 
 # short names
 gemm = mg_gemm
 gemm_bias_relu = mg_gemm_bias_relu
+gemm_batched = mg_gemm_batched
 grouped_gemm = mg_grouped_gemm
 prepack_a = mg_prepack_a
 gemm_prepacked = mg_gemm_prepacked

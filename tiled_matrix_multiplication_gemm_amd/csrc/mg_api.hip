@@ -107,7 +107,7 @@ mg_status launch(int cfg, int dt, bool epi, int mode, KArgs& a, hipStream_t s, i
         grid = (cdiv(a.M, d.bm) + a.E) * a.tiles_n;
     } else {
         a.tiles_m = (int32_t)cdiv(a.M, d.bm);
-        grid = (int64_t)a.tiles_m * a.tiles_n;
+        grid = (int64_t)a.tiles_m * a.tiles_n * (a.batch > 1 ? a.batch : 1);
     }
     if (grid <= 0) return MG_OK;
     if (grid > 0x7fffffff) return MG_ERR_INVALID_ARG;
@@ -131,8 +131,16 @@ mg_status launch(int cfg, int dt, bool epi, int mode, KArgs& a, hipStream_t s, i
 
 mg_status gemm_common(const void* A, const void* B, const void* bias, void* C, int64_t M, int64_t N, int64_t K,
                       int64_t sam, int64_t sak, int64_t sbk, int64_t sbn, int64_t scm, int64_t scn,
-                      mg_dtype in_dtype, mg_dtype out_dtype, bool epi, hipStream_t stream) {
-    if (M < 0 || N < 0 || K < 0) return MG_ERR_INVALID_ARG;
+                      mg_dtype in_dtype, mg_dtype out_dtype, bool epi, hipStream_t stream, int64_t batch = 1,
+                      int64_t sab = 0, int64_t sbb = 0, int64_t scb = 0) {
+    if (M < 0 || N < 0 || K < 0 || batch < 0) return MG_ERR_INVALID_ARG;
+    if (batch == 0) return check_dtype(in_dtype, out_dtype);  // no entries: pointers never used
+    if (batch > 1) {
+        // entries of A and B may repeat (stride 0); entries of C may not overlap
+        if (sab < 0 || sbb < 0 || scb < 0) return MG_ERR_INVALID_ARG;
+        if (M > 0 && N > 0 && scb < M * scm) return MG_ERR_UNSUPPORTED_LAYOUT;
+        if (sab % 8 != 0 || sbb % 8 != 0 || scb % 8 != 0) return MG_ERR_MISALIGNED;
+    }
     MG_TRY(check_dtype(in_dtype, out_dtype));
     // A is row-major (unit stride along K) or given transposed (unit stride
     // along M, i.e. stored [K,M]); likewise B row-major (unit stride along N)
@@ -145,7 +153,7 @@ mg_status gemm_common(const void* A, const void* B, const void* bias, void* C, i
     MG_TRY(tb ? check_matrix(B, N, K, sbn, sbk) : check_matrix(B, K, N, sbk, sbn));
     MG_TRY(check_matrix(C, M, N, scm, scn));
     if (epi && N > 0 && M > 0 && bias == nullptr) return MG_ERR_INVALID_ARG;
-    if (M == 0 || N == 0) return MG_OK;
+    if (M == 0 || N == 0 || batch == 0) return MG_OK;
     const int cfg = select_config(M, N, K, 0);
     if (cfg < 0 || cfg >= kNumConfigs) return MG_ERR_BAD_CONFIG;
     KArgs a{};
@@ -157,6 +165,9 @@ mg_status gemm_common(const void* A, const void* B, const void* bias, void* C, i
     a.lda = ta ? sak : sam;  // stride between the stored rows
     a.ldb = tb ? sbn : sbk;
     a.ldc = scm;
+    a.batch = (int32_t)(batch > 1 ? batch : 1);
+    if (batch > 0x7fffffff) return MG_ERR_INVALID_ARG;
+    a.sab = sab; a.sbb = sbb; a.scb = scb;
     return launch(cfg, (int)in_dtype, epi, MODE_DENSE, a, stream, ta, tb);
 }
 
@@ -190,6 +201,14 @@ mg_status mg_gemm_bias_relu(const void* A, const void* B, const void* bias, void
                             hipStream_t stream) {
     return gemm_common(A, B, bias, C, M, N, K, stride_am, stride_ak, stride_bk, stride_bn, stride_cm, stride_cn,
                        in_dtype, out_dtype, true, stream);
+}
+
+mg_status mg_gemm_batched(const void* A, const void* B, void* C, int64_t batch, int64_t M, int64_t N, int64_t K,
+                          int64_t stride_am, int64_t stride_ak, int64_t stride_bk, int64_t stride_bn,
+                          int64_t stride_cm, int64_t stride_cn, int64_t batch_stride_a, int64_t batch_stride_b,
+                          int64_t batch_stride_c, mg_dtype in_dtype, mg_dtype out_dtype, hipStream_t stream) {
+    return gemm_common(A, B, nullptr, C, M, N, K, stride_am, stride_ak, stride_bk, stride_bn, stride_cm, stride_cn,
+                       in_dtype, out_dtype, false, stream, batch, batch_stride_a, batch_stride_b, batch_stride_c);
 }
 
 mg_status mg_grouped_gemm(const void* X, const void* W, void* Y, const int32_t* expert_offsets, int64_t E, int64_t T,

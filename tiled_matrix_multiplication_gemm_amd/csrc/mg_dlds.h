@@ -256,6 +256,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
         Bg += (int64_t)e * args.stride_we;
         Cg += (int64_t)r0 * args.ldc;
     } else {
+        if constexpr (MODE == MODE_DENSE) batch_entry(args, logical, Ag, Bg, Cg);
         grouped_order(logical, args.tiles_m, args.tiles_n, args.group_m, pm, pn);
     }
     const int64_t N = args.N, K = args.K;

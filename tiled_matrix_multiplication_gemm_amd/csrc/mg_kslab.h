@@ -73,6 +73,10 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_kslab_kernel(const KArgs args) {
     const int wave = tid >> 6;
 
     int logical = args.xcd_remap ? xcd_logical(blockIdx.x, gridDim.x) : (int)blockIdx.x;
+    const uint16_t* Ag = args.A;
+    const uint16_t* Bg = args.B;
+    uint16_t* Cg = args.C;
+    batch_entry(args, logical, Ag, Bg, Cg);
     int pm, pn;
     grouped_order(logical, args.tiles_m, args.tiles_n, args.group_m, pm, pn);
     const int64_t M = args.M, N = args.N, K = args.K;
@@ -97,8 +101,8 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_kslab_kernel(const KArgs args) {
         const int64_t cn = (n0 + 8 * c <= N - 8) ? 8 * c : N - 8 - n0;
         offB_g[j] = (uint32_t)((krow * args.ldb + cn) * 2);
     }
-    const char* baseA = (const char*)(args.A + m0 * args.lda);
-    const char* baseB = (const char*)(args.B + n0);
+    const char* baseA = (const char*)(Ag + m0 * args.lda);
+    const char* baseB = (const char*)(Bg + n0);
     const int64_t stepA = (int64_t)BK * 2;
     const int64_t stepB = (int64_t)BK * args.ldb * 2;
 
@@ -212,7 +216,6 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_kslab_kernel(const KArgs args) {
                     float4{acc[i][j][4 * r4], acc[i][j][4 * r4 + 1], acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]};
         }
     __syncthreads();
-    uint16_t* Cg = args.C;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll

@@ -40,6 +40,8 @@ struct KArgs {
     int64_t stride_we;       // grouped: elements between experts' weights
     int32_t E;
     int32_t tiles_m, tiles_n;
+    int32_t batch;           // dense: batch entries (1 for a single GEMM)
+    int64_t sab, sbb, scb;   // dense: elements between batch entries of A, B, C
     int32_t group_m;
     int32_t xcd_remap;
 };
@@ -167,6 +169,20 @@ __device__ __forceinline__ int xcd_logical(int b, int total) {
     return (xcd < r) ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
 }
 
+// Dense and batched GEMM: batch entry of workgroup `logical`, whose tile index
+// within the entry is returned in `logical`; the operands are advanced to
+// the entry.  Entries are contiguous ranges of workgroups, so each XCD works
+// on whole tiles of few entries.
+__device__ __forceinline__ void batch_entry(const KArgs& args, int& logical, const uint16_t*& A, const uint16_t*& B,
+                                            uint16_t*& C) {
+    const int per = args.tiles_m * args.tiles_n;
+    const int b = logical / per;
+    logical -= b * per;
+    A += (int64_t)b * args.sab;
+    B += (int64_t)b * args.sbb;
+    C += (int64_t)b * args.scb;
+}
+
 // Grouped tile order: GROUP_M tile rows at a time, column by column within
 // the group (the Gluon matmul example's program-id mapping).
 __device__ __forceinline__ void grouped_order(int pid, int tiles_m, int tiles_n, int group_m, int& pm, int& pn) {
@@ -212,6 +228,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_tile_kernel(const KArgs args) {
         Bg += (int64_t)e * args.stride_we;
         Cg += (int64_t)r0 * args.ldc;
     } else {
+        if constexpr (MODE == MODE_DENSE) batch_entry(args, logical, Ag, Bg, Cg);
         grouped_order(logical, args.tiles_m, args.tiles_n, args.group_m, pm, pn);
     }
     const int64_t N = args.N, K = args.K;
