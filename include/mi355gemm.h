@@ -119,6 +119,29 @@ mg_status mg_gemm_batched(const void* A, const void* B, void* C, int64_t batch,
                           mg_dtype in_dtype, mg_dtype out_dtype, hipStream_t stream);
 
 /*
+ * Split-K GEMM for outputs too small to fill the GPU (tall-skinny or large-K
+ * shapes, "Using Triton to optimise GEMM across chips", section 4.3): the K
+ * slices are cut into `splits` contiguous runs, one set of output tiles per
+ * run writes fp32 partial products to the caller's workspace
+ * ([splits][M][N] fp32, mg_splitk_workspace_bytes() bytes, 16-byte aligned,
+ * device memory the call only writes and reads), and a second kernel adds
+ * the partials in split order (deterministic) and rounds once into C.  Both
+ * kernels run on `stream`; the workspace must not be used by another call
+ * until they have finished.  Operands as for mg_gemm(), transposed ones
+ * included; the shape must suit the direct-to-LDS kernels (K in whole
+ * slices of the chosen row, N % 8 == 0, M % 8 == 0 for a transposed A),
+ * else MG_ERR_UNSUPPORTED_LAYOUT.  splits in [1, 4096]; a workspace that is
+ * null or too small is MG_ERR_INVALID_ARG.
+ */
+size_t mg_splitk_workspace_bytes(int64_t M, int64_t N, int64_t splits);
+mg_status mg_gemm_splitk(const void* A, const void* B, void* C, void* workspace, size_t workspace_bytes,
+                         int64_t splits, int64_t M, int64_t N, int64_t K,
+                         int64_t stride_am, int64_t stride_ak,
+                         int64_t stride_bk, int64_t stride_bn,
+                         int64_t stride_cm, int64_t stride_cn,
+                         mg_dtype in_dtype, mg_dtype out_dtype, hipStream_t stream);
+
+/*
  * Grouped GEMM for the expert layer of a mixture-of-experts model, in one
  * launch: for every expert e,
  *     Y[o_e : o_{e+1}, :] = X[o_e : o_{e+1}, :] * W[e]

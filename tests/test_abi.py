@@ -101,6 +101,33 @@ def test_gemm_batched_empty_batches_are_noops(L):
     assert gemm_batched(L, M=0, A=None, C=None) == OK
 
 
+def test_splitk_workspace_and_arguments(L):
+    assert L.mg_splitk_workspace_bytes(64, 32, 4) == 4 * 64 * 32 * 4
+    assert L.mg_splitk_workspace_bytes(0, 32, 4) == 0
+    assert L.mg_splitk_workspace_bytes(64, 32, 0) == 0
+    W = P + 4096 * 1024
+
+    def splitk(ws=W, nbytes=1 << 20, splits=2, **kw):
+        a = dict(M=64, N=64, K=64, sam=64, sak=1, sbk=64, sbn=1, scm=64, scn=1)
+        a.update(kw)
+        return L.mg_gemm_splitk(P, P, P, ws, nbytes, splits, a["M"], a["N"], a["K"], a["sam"], a["sak"], a["sbk"],
+                                a["sbn"], a["scm"], a["scn"], F16, F16, S)
+
+    assert splitk(splits=0) == INVALID
+    assert splitk(splits=5000) == INVALID
+    assert splitk(ws=None) == INVALID
+    assert splitk(nbytes=2 * 64 * 64 * 4 - 1) == INVALID
+    assert splitk(ws=W + 8) == MISALIGNED
+    assert splitk(sak=2) == LAYOUT
+    assert splitk(M=0) == OK
+    for cid in (5, 7):  # rows without a direct-to-LDS kernel cannot split
+        assert L.mg_set_config(cid) == OK
+        try:
+            assert splitk() == LAYOUT
+        finally:
+            assert L.mg_set_config(-1) == OK
+
+
 def test_zero_sized_problems_are_noops(L):
     # M == 0 or N == 0: nothing to compute, null pointers are fine
     assert gemm(L, A=None, C=None, M=0) == OK

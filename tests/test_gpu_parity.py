@@ -363,6 +363,78 @@ def test_batched_transposed_entries(orc, ta, tb):
         assert_bitexact(got[b], ref_q, BF16, "batched transposed entry %d" % b)
 
 
+# Split-K: partial products per K run in a caller workspace, summed in split
+# order.  Integer inputs stay exact (every partial sum is an integer below
+# 2^24), so the bit-exact gate applies unchanged.
+SPLITK = [(64, 64, 4096, 2), (64, 64, 4096, 8), (128, 264, 8192, 4), (520, 512, 2048, 3), (1024, 1024, 2048, 2),
+          (64, 64, 128, 8), (72, 200, 1024, 5)]
+
+
+def run_splitk(case, splits, cfg=-1, ta=0, tb=0):
+    import torch
+
+    dt = case.dtype
+    A = stored_transposed(case.A, dt) if ta else to_dev(case.A, dt)
+    B = stored_transposed(case.B, dt) if tb else to_dev(case.B, dt)
+    out = Guarded(case.M, case.N, dt)
+    ws = torch.full((mg.mg_splitk_workspace_bytes(case.M, case.N, splits) // 4,), float("nan"), device="cuda")
+    mg.mg_set_config(cfg)
+    try:
+        mg.mg_gemm_splitk(A, B, splits, workspace=ws, out=out.mat)
+        torch.cuda.synchronize()
+    finally:
+        mg.mg_set_config(-1)
+    return out.result(), out.guards_intact()
+
+
+@pytest.mark.parametrize("cfg", [-1, 0, 1, 2])
+def test_splitk_every_row(orc, cfg):
+    for i, (M, N, K, splits) in enumerate(SPLITK):
+        for dtype in (F16, BF16):
+            for integer in (True, False):
+                gen = inputs.integer_dense if integer else inputs.random_dense
+                c = gen(M, N, K, dtype, 8000 + 10 * i + 2 * integer + dtype, name="splitk")
+                announce("splitk cfg=%d M=%d N=%d K=%d splits=%d dt=%d int=%s" % (cfg, M, N, K, splits, dtype, integer))
+                got, guards = run_splitk(c, splits, cfg)
+                assert guards, "write outside the output"
+                ref, ref_q = orc.gemm(c.A, c.B, dtype)
+                if integer:
+                    assert_bitexact(got, ref_q, dtype, c.name)
+                else:
+                    assert_tolerance(got, ref, dtype, c.name)
+
+
+@pytest.mark.parametrize("ta,tb", [(1, 0), (0, 1), (1, 1)])
+def test_splitk_transposed_and_deterministic(orc, ta, tb):
+    M, N, K, splits = 264, 136, 4096, 6
+    c = inputs.random_dense(M, N, K, BF16, 8500 + 2 * ta + tb, name="splitk_t")
+    announce("splitk transposed ta=%d tb=%d" % (ta, tb))
+    got, guards = run_splitk(c, splits, ta=ta, tb=tb)
+    got2, _ = run_splitk(c, splits, ta=ta, tb=tb)
+    assert guards
+    assert np.array_equal(got, got2), "split-K result differs between two calls"
+    ref, _ = orc.gemm(c.A, c.B, BF16)
+    assert_tolerance(got, ref, BF16, c.name)
+
+
+def test_splitk_tall_skinny_large_k_sampled(orc):
+    """256 x 256 output with K = 65536: 16 tiles of 64x64 would occupy 16 of
+    256 CUs; cut into 16 K runs they fill the GPU."""
+    M, N, K, splits = 256, 256, 65536, 16
+    for integer in (True, False):
+        gen = inputs.integer_dense if integer else inputs.random_dense
+        c = gen(M, N, K, BF16, 8600 + integer, name="splitk_large_k")
+        announce("splitk tall-skinny int=%s" % integer)
+        got, guards = run_splitk(c, splits)
+        assert guards
+        rows, cols = compare.sample_positions(M, N, 4096, 8601)
+        ref, ref_q = orc.gemm_sampled(c.A, c.B, BF16, rows, cols)
+        if integer:
+            assert_bitexact(got[rows, cols], ref_q, BF16, c.name)
+        else:
+            assert_tolerance(got[rows, cols], ref, BF16, c.name)
+
+
 def run_grouped(case):
     import torch
 

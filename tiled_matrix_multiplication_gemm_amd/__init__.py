@@ -38,7 +38,8 @@ class ConfigDesc(ctypes.Structure):
 
 
 EXPORTED = (
-    "mg_status_string", "mg_gemm", "mg_gemm_bias_relu", "mg_gemm_batched", "mg_grouped_gemm", "mg_prepacked_bytes",
+    "mg_status_string", "mg_gemm", "mg_gemm_bias_relu", "mg_gemm_batched", "mg_gemm_splitk",
+    "mg_splitk_workspace_bytes", "mg_grouped_gemm", "mg_prepacked_bytes",
     "mg_prepack_a", "mg_config_bk", "mg_gemm_prepacked", "mg_num_configs", "mg_config_info",
     "mg_set_config", "mg_last_config", "mg_select_config",
 )
@@ -66,6 +67,10 @@ def lib() -> ctypes.CDLL:
         L.mg_gemm_bias_relu.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, i64, cint, cint, vp]
         L.mg_gemm_batched.restype = cint
         L.mg_gemm_batched.argtypes = [vp, vp, vp] + [i64] * 13 + [cint, cint, vp]
+        L.mg_splitk_workspace_bytes.restype = ctypes.c_size_t
+        L.mg_splitk_workspace_bytes.argtypes = [i64, i64, i64]
+        L.mg_gemm_splitk.restype = cint
+        L.mg_gemm_splitk.argtypes = [vp, vp, vp, vp, ctypes.c_size_t] + [i64] * 10 + [cint, cint, vp]
         L.mg_grouped_gemm.restype = cint
         L.mg_grouped_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, cint, vp]
         L.mg_prepacked_bytes.restype = ctypes.c_size_t
@@ -177,6 +182,33 @@ def mg_gemm_batched(a, b, out=None):
     return out
 
 
+def mg_splitk_workspace_bytes(M: int, N: int, splits: int) -> int:
+    return int(lib().mg_splitk_workspace_bytes(M, N, splits))
+
+
+def mg_gemm_splitk(a, b, splits: int, workspace=None, out=None):
+    """out = a @ b with K cut into `splits` runs (fp32 partials in `workspace`,
+    a device tensor of at least mg_splitk_workspace_bytes(M, N, splits)
+    bytes; allocated here through torch when not given)."""
+    import torch
+
+    _require_gpu(a, b)
+    M, K = a.shape
+    K2, N = b.shape
+    if K2 != K:
+        raise RuntimeError("MG_ERR_INVALID_ARG: inner dimensions differ (%d vs %d)" % (K, K2))
+    if out is None:
+        out = torch.empty((M, N), dtype=a.dtype, device=a.device)
+    need = mg_splitk_workspace_bytes(M, N, splits)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=a.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().mg_gemm_splitk(a.data_ptr(), b.data_ptr(), out.data_ptr(), workspace.data_ptr(), ws_bytes, splits,
+                                M, N, K, a.stride(0), a.stride(1), b.stride(0), b.stride(1), out.stride(0),
+                                out.stride(1), _dtype_code(a), _dtype_code(out), _stream(a)))
+    return out
+
+
 def mg_grouped_gemm(x, w, offsets, out=None):
     """out[o_e:o_{e+1}] = x[o_e:o_{e+1}] @ w[e] for every expert e (one launch).
 
@@ -266,6 +298,7 @@ def mg_select_config(M: int, N: int, K: int, dtype: int = MG_F16, grouped: bool 
 gemm = mg_gemm
 gemm_bias_relu = mg_gemm_bias_relu
 gemm_batched = mg_gemm_batched
+gemm_splitk = mg_gemm_splitk
 grouped_gemm = mg_grouped_gemm
 prepack_a = mg_prepack_a
 gemm_prepacked = mg_gemm_prepacked

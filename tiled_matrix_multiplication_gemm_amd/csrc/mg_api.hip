@@ -71,6 +71,31 @@ int select_config(int64_t M, int64_t N, int64_t K, int grouped) {
     return best;
 }
 
+// Split-K rows: those with a direct-to-LDS kernel for small and mid-size
+// tiles, chosen by the same rounds x tile-rate model with the tiles of every
+// split counted (each split runs K / splits of the product).
+int select_config_splitk(int64_t M, int64_t N, int64_t splits) {
+    int forced = g_forced.load();
+    if (forced >= 0) return forced;
+    struct Cand {
+        int id, bm, bn;
+        double rate;
+    };
+    static const Cand cands[] = {{0, 256, 256, 1.00}, {1, 128, 128, 0.49}, {2, 64, 64, 0.50}};
+    constexpr int64_t kCUs = 256;
+    int best = 2;
+    double best_t = 0.0;
+    for (const Cand& c : cands) {
+        const int64_t tiles = cdiv(M, c.bm) * cdiv(N, c.bn) * splits;
+        const double t = (double)cdiv(tiles, kCUs) * ((double)c.bm * c.bn / c.rate);
+        if (best_t == 0.0 || t < best_t) {
+            best_t = t;
+            best = c.id;
+        }
+    }
+    return best;
+}
+
 // ---- validation --------------------------------------------------------------
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -108,6 +133,7 @@ mg_status launch(int cfg, int dt, bool epi, int mode, KArgs& a, hipStream_t s, i
     } else {
         a.tiles_m = (int32_t)cdiv(a.M, d.bm);
         grid = (int64_t)a.tiles_m * a.tiles_n * (a.batch > 1 ? a.batch : 1);
+        if (mode == MODE_SPLITK) grid = (int64_t)a.tiles_m * a.tiles_n * a.splits;
     }
     if (grid <= 0) return MG_OK;
     if (grid > 0x7fffffff) return MG_ERR_INVALID_ARG;
@@ -209,6 +235,42 @@ mg_status mg_gemm_batched(const void* A, const void* B, void* C, int64_t batch, 
                           int64_t batch_stride_c, mg_dtype in_dtype, mg_dtype out_dtype, hipStream_t stream) {
     return gemm_common(A, B, nullptr, C, M, N, K, stride_am, stride_ak, stride_bk, stride_bn, stride_cm, stride_cn,
                        in_dtype, out_dtype, false, stream, batch, batch_stride_a, batch_stride_b, batch_stride_c);
+}
+
+size_t mg_splitk_workspace_bytes(int64_t M, int64_t N, int64_t splits) {
+    if (M <= 0 || N <= 0 || splits <= 0) return 0;
+    return (size_t)(splits * M * N) * sizeof(float);
+}
+
+mg_status mg_gemm_splitk(const void* A, const void* B, void* C, void* workspace, size_t workspace_bytes,
+                         int64_t splits, int64_t M, int64_t N, int64_t K, int64_t stride_am, int64_t stride_ak,
+                         int64_t stride_bk, int64_t stride_bn, int64_t stride_cm, int64_t stride_cn,
+                         mg_dtype in_dtype, mg_dtype out_dtype, hipStream_t stream) {
+    if (M < 0 || N < 0 || K < 0 || splits < 1 || splits > 4096) return MG_ERR_INVALID_ARG;
+    MG_TRY(check_dtype(in_dtype, out_dtype));
+    const int ta = (stride_ak == 1 || K <= 1) ? 0 : ((stride_am == 1 || M <= 1) ? 1 : -1);
+    const int tb = (stride_bn == 1 || N <= 1) ? 0 : ((stride_bk == 1 || K <= 1) ? 1 : -1);
+    if (ta < 0 || tb < 0) return MG_ERR_UNSUPPORTED_LAYOUT;
+    MG_TRY(ta ? check_matrix(A, K, M, stride_ak, stride_am) : check_matrix(A, M, K, stride_am, stride_ak));
+    MG_TRY(tb ? check_matrix(B, N, K, stride_bn, stride_bk) : check_matrix(B, K, N, stride_bk, stride_bn));
+    MG_TRY(check_matrix(C, M, N, stride_cm, stride_cn));
+    if (M == 0 || N == 0) return MG_OK;
+    if (workspace == nullptr || workspace_bytes < mg_splitk_workspace_bytes(M, N, splits))
+        return MG_ERR_INVALID_ARG;
+    if (!aligned16(workspace)) return MG_ERR_MISALIGNED;
+    const int cfg = select_config_splitk(M, N, splits);
+    if (cfg < 0 || cfg >= kNumConfigs) return MG_ERR_BAD_CONFIG;
+    KArgs a{};
+    a.A = (const uint16_t*)A;
+    a.B = (const uint16_t*)B;
+    a.C = (uint16_t*)C;
+    a.M = M; a.N = N; a.K = K;
+    a.lda = ta ? stride_ak : stride_am;
+    a.ldb = tb ? stride_bn : stride_bk;
+    a.ldc = stride_cm;
+    a.ws = (float*)workspace;
+    a.splits = (int32_t)splits;
+    return launch(cfg, (int)in_dtype, false, MODE_SPLITK, a, stream, ta, tb);
 }
 
 mg_status mg_grouped_gemm(const void* X, const void* W, void* Y, const int32_t* expert_offsets, int64_t E, int64_t T,

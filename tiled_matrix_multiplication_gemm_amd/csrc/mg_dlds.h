@@ -28,6 +28,7 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4_t;
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) u32x2 lds_u32x2_t;
 
 // One 16-byte direct load per lane: global memory -> LDS at
@@ -248,6 +249,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
     uint16_t* Cg = args.C;
     int64_t M = args.M;
     int pm, pn;
+    int split = 0;  // split-K: which K range (workgroups of one split are contiguous)
     if constexpr (MODE == MODE_GROUPED) {
         int e, r0, rows;
         if (!grouped_tile<BM>(args, logical, e, r0, rows, pm, pn)) return;
@@ -257,11 +259,22 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
         Cg += (int64_t)r0 * args.ldc;
     } else {
         if constexpr (MODE == MODE_DENSE) batch_entry(args, logical, Ag, Bg, Cg);
+        if constexpr (MODE == MODE_SPLITK) {
+            const int per = args.tiles_m * args.tiles_n;
+            split = logical / per;
+            logical -= split * per;
+        }
         grouped_order(logical, args.tiles_m, args.tiles_n, args.group_m, pm, pn);
     }
     const int64_t N = args.N, K = args.K;
     const int64_t m0 = (int64_t)pm * BM, n0 = (int64_t)pn * BN;
-    const int nk = (int)(K / BK);
+    int nk = (int)(K / BK);
+    int kt0 = 0;  // this workgroup's K slices are [kt0, kt0 + nk)
+    if constexpr (MODE == MODE_SPLITK) {
+        const int all = nk;
+        kt0 = (int)((int64_t)split * all / args.splits);
+        nk = (int)((int64_t)(split + 1) * all / args.splits) - kt0;
+    }
 
     // ---- per-lane source offsets of the direct loads ---------------------
     // 32-bit byte offsets from a workgroup-uniform base that advances by one
@@ -275,10 +288,10 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
     uint32_t offB_g[JB];
 #pragma unroll
     for (int j = 0; j < JB; ++j) offB_g[j] = OB::load_off(wave, j, lane, n0, N, args.ldb);
-    const char* baseA = OA::tile_base(Ag, m0, args.lda);
-    const char* baseB = OB::tile_base(Bg, n0, args.ldb);
     const int64_t stepA = OA::slice_bytes(args.lda);  // bytes per k-slice
     const int64_t stepB = OB::slice_bytes(args.ldb);
+    const char* baseA = OA::tile_base(Ag, m0, args.lda) + kt0 * stepA;
+    const char* baseB = OB::tile_base(Bg, n0, args.ldb) + kt0 * stepB;
 
     // direct loads of k-slice kt into ring slot `slot` (a compile-time index)
     // (buffer resources rebased on the slice: offsets stay below 2^31)
@@ -461,7 +474,26 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
         return u32x2{(uint32_t)from_float<DT>(v[0]) | ((uint32_t)from_float<DT>(v[1]) << 16),
                      (uint32_t)from_float<DT>(v[2]) | ((uint32_t)from_float<DT>(v[3]) << 16)};
     };
-    if constexpr (Cfg::STAGED) {
+    if constexpr (MODE == MODE_SPLITK) {
+        // fp32 partial tile of this split: 4 adjacent columns per lane and
+        // register group, one 16-byte store each
+        float* W = args.ws + (int64_t)split * M * N;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int64_t row = m0 + wm * Cfg::WTM + i * 32 + (lane & 31);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                __builtin_amdgcn_sched_barrier(0);
+                const int64_t col0 = n0 + wn * Cfg::WTN + j * 32 + 4 * (lane >> 5);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t col = col0 + 8 * q;
+                    const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                    if (row < M && col < N) *(f32x4*)(W + row * N + col) = v;
+                }
+            }
+        }
+    } else if constexpr (Cfg::STAGED) {
         constexpr int CH = Cfg::WTN / 8;  // 16-byte chunks per staged row
         constexpr int RB = Cfg::WTN * 2;  // bytes per staged row
         auto stage_swz = [](int row) { return (row ^ (row >> 3)) & (CH - 1); };
@@ -514,6 +546,30 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
                 }
             }
         }
+    }
+}
+
+// Split-K reduction: C = sum over splits of the fp32 partials, in split
+// order (deterministic), one rounding; 8 adjacent outputs per thread
+// (N % 8 == 0 on this path), 16-byte loads and stores.
+template <int DT>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* ws, uint16_t* C, int64_t M, int64_t N,
+                                                            int64_t ldc, int splits) {
+    const int64_t groups = M * (N / 8);
+    for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < groups; g += (int64_t)gridDim.x * 256) {
+        const int64_t row = g / (N / 8), col = (g % (N / 8)) * 8;
+        f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < splits; ++s) {
+            const float* p = ws + (int64_t)s * M * N + row * N + col;
+            lo += *(const f32x4*)p;
+            hi += *(const f32x4*)(p + 4);
+        }
+        u32x4 o;
+        o[0] = (uint32_t)from_float<DT>(lo[0]) | ((uint32_t)from_float<DT>(lo[1]) << 16);
+        o[1] = (uint32_t)from_float<DT>(lo[2]) | ((uint32_t)from_float<DT>(lo[3]) << 16);
+        o[2] = (uint32_t)from_float<DT>(hi[0]) | ((uint32_t)from_float<DT>(hi[1]) << 16);
+        o[3] = (uint32_t)from_float<DT>(hi[2]) | ((uint32_t)from_float<DT>(hi[3]) << 16);
+        *(u32x4*)(C + row * ldc + col) = o;
     }
 }
 

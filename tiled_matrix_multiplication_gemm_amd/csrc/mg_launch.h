@@ -45,12 +45,30 @@ mg_status launch_slab(const KArgs& a, int64_t grid, hipStream_t stream) {
     return hipGetLastError() == hipSuccess ? MG_OK : MG_ERR_HIP;
 }
 
+// split-K: partial products of every split into the workspace, then their
+// sum in split order into C (both on stream s)
+template <class F, int DT>
+mg_status launch_split(int ta, int tb, const KArgs& a, int64_t grid, hipStream_t s) {
+    mg_status st;
+    if (ta && tb) st = launch_fast<F, DT, false, MODE_SPLITK, true, true>(a, grid, s);
+    else if (ta) st = launch_fast<F, DT, false, MODE_SPLITK, true, false>(a, grid, s);
+    else if (tb) st = launch_fast<F, DT, false, MODE_SPLITK, false, true>(a, grid, s);
+    else st = launch_fast<F, DT, false, MODE_SPLITK>(a, grid, s);
+    if (st != MG_OK) return st;
+    const int64_t groups = a.M * (a.N / 8);
+    const int64_t blocks = (groups + 255) / 256 < 8192 ? (groups + 255) / 256 : 8192;
+    hipLaunchKernelGGL((splitk_reduce_kernel<DT>), dim3((unsigned)blocks), dim3(256), 0, s, (const float*)a.ws, a.C,
+                       a.M, a.N, a.ldc, a.splits);
+    return hipGetLastError() == hipSuccess ? MG_OK : MG_ERR_HIP;
+}
+
 template <class F, int DT>
 mg_status launch_direct(bool epi, int mode, int ta, int tb, const KArgs& a, int64_t grid, hipStream_t s) {
     if constexpr (is_slab<F>::value) {
         (void)mode, (void)ta, (void)tb;
         return epi ? launch_slab<F, DT, true>(a, grid, s) : launch_slab<F, DT, false>(a, grid, s);
     } else {
+        if (mode == MODE_SPLITK) return launch_split<F, DT>(ta, tb, a, grid, s);
         if (mode == MODE_GROUPED) return launch_fast<F, DT, false, MODE_GROUPED>(a, grid, s);
         return epi ? launch_fast_t<F, DT, true>(ta, tb, a, grid, s) : launch_fast_t<F, DT, false>(ta, tb, a, grid, s);
     }
@@ -63,7 +81,8 @@ mg_status launch_direct(bool epi, int mode, int ta, int tb, const KArgs& a, int6
 template <class F>
 bool direct_fits(int mode, int ta, int tb, const KArgs& a) {
     constexpr int64_t LIM = (int64_t)1 << 31;
-    if (mode == MODE_PACKED_A || (is_slab<F>::value && (mode == MODE_GROUPED || ta || tb))) return false;
+    if (mode == MODE_PACKED_A || (is_slab<F>::value && (mode == MODE_GROUPED || mode == MODE_SPLITK || ta || tb)))
+        return false;
     if (a.K % F::BK != 0 || a.N % 8 != 0 || (ta && a.M % 8 != 0)) return false;
     const int64_t a_span = ta ? 64 * a.lda * 2 : (int64_t)F::BM * a.lda * 2;
     const int64_t b_span = tb ? (int64_t)F::BN * a.ldb * 2 : 64 * a.ldb * 2;
@@ -79,7 +98,7 @@ mg_status launch_dt(int dt, bool epi, int mode, int ta, int tb, const KArgs& a, 
             return dt == DT_F16 ? launch_direct<F, DT_F16>(epi, mode, ta, tb, a, grid, s)
                                 : launch_direct<F, DT_BF16>(epi, mode, ta, tb, a, grid, s);
     }
-    if (ta || tb) return MG_ERR_UNSUPPORTED_LAYOUT;
+    if (ta || tb || mode == MODE_SPLITK) return MG_ERR_UNSUPPORTED_LAYOUT;
     return dt == DT_F16 ? launch_general<C, DT_F16>(epi, mode, a, grid, s)
                         : launch_general<C, DT_BF16>(epi, mode, a, grid, s);
 }

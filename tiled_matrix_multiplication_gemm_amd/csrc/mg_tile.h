@@ -27,7 +27,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 enum { DT_F16 = 0, DT_BF16 = 1 };
-enum { MODE_DENSE = 0, MODE_PACKED_A = 1, MODE_GROUPED = 2 };
+enum { MODE_DENSE = 0, MODE_PACKED_A = 1, MODE_GROUPED = 2, MODE_SPLITK = 3 };
 
 struct KArgs {
     const uint16_t* A;       // dense: A; packed: blocked A; grouped: X
@@ -42,6 +42,8 @@ struct KArgs {
     int32_t tiles_m, tiles_n;
     int32_t batch;           // dense: batch entries (1 for a single GEMM)
     int64_t sab, sbb, scb;   // dense: elements between batch entries of A, B, C
+    float* ws;               // split-K: fp32 partial products [splits][M][N]
+    int32_t splits;          // split-K: K ranges (contiguous runs of K slices)
     int32_t group_m;
     int32_t xcd_remap;
 };
