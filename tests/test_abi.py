@@ -128,6 +128,17 @@ def test_splitk_workspace_and_arguments(L):
             assert L.mg_set_config(-1) == OK
 
 
+def test_splitk_choice_model(L):
+    ch = L.mg_splitk_choose
+    # outputs that fill the GPU are not split; tall-skinny, large-K ones are
+    assert ch(8192, 8192, 8192) == 1 and ch(1024, 1024, 2048) == 1
+    assert ch(256, 256, 65536) >= 8 and ch(2048, 2048, 16384) >= 2
+    for shape in [(256, 256, 65536), (64, 64, 4096), (512, 512, 32768), (128, 4096, 16384)]:
+        s = ch(*shape)
+        assert s >= 1 and s & (s - 1) == 0 and (s == 1 or shape[2] // s >= 256)
+    assert ch(0, 8, 8) == 1 and ch(8, 8, 0) == 1
+
+
 def test_zero_sized_problems_are_noops(L):
     # M == 0 or N == 0: nothing to compute, null pointers are fine
     assert gemm(L, A=None, C=None, M=0) == OK

@@ -39,7 +39,7 @@ class ConfigDesc(ctypes.Structure):
 
 EXPORTED = (
     "mg_status_string", "mg_gemm", "mg_gemm_bias_relu", "mg_gemm_batched", "mg_gemm_splitk",
-    "mg_splitk_workspace_bytes", "mg_grouped_gemm", "mg_prepacked_bytes",
+    "mg_splitk_workspace_bytes", "mg_splitk_choose", "mg_grouped_gemm", "mg_prepacked_bytes",
     "mg_prepack_a", "mg_config_bk", "mg_gemm_prepacked", "mg_num_configs", "mg_config_info",
     "mg_set_config", "mg_last_config", "mg_select_config",
 )
@@ -69,6 +69,8 @@ def lib() -> ctypes.CDLL:
         L.mg_gemm_batched.argtypes = [vp, vp, vp] + [i64] * 13 + [cint, cint, vp]
         L.mg_splitk_workspace_bytes.restype = ctypes.c_size_t
         L.mg_splitk_workspace_bytes.argtypes = [i64, i64, i64]
+        L.mg_splitk_choose.restype = i64
+        L.mg_splitk_choose.argtypes = [i64, i64, i64]
         L.mg_gemm_splitk.restype = cint
         L.mg_gemm_splitk.argtypes = [vp, vp, vp, vp, ctypes.c_size_t] + [i64] * 10 + [cint, cint, vp]
         L.mg_grouped_gemm.restype = cint
@@ -186,10 +188,15 @@ def mg_splitk_workspace_bytes(M: int, N: int, splits: int) -> int:
     return int(lib().mg_splitk_workspace_bytes(M, N, splits))
 
 
-def mg_gemm_splitk(a, b, splits: int, workspace=None, out=None):
+def mg_splitk_choose(M: int, N: int, K: int) -> int:
+    return int(lib().mg_splitk_choose(M, N, K))
+
+
+def mg_gemm_splitk(a, b, splits: int | None = None, workspace=None, out=None):
     """out = a @ b with K cut into `splits` runs (fp32 partials in `workspace`,
     a device tensor of at least mg_splitk_workspace_bytes(M, N, splits)
-    bytes; allocated here through torch when not given)."""
+    bytes; allocated here through torch when not given).  splits=None takes
+    mg_splitk_choose()."""
     import torch
 
     _require_gpu(a, b)
@@ -199,6 +206,8 @@ def mg_gemm_splitk(a, b, splits: int, workspace=None, out=None):
         raise RuntimeError("MG_ERR_INVALID_ARG: inner dimensions differ (%d vs %d)" % (K, K2))
     if out is None:
         out = torch.empty((M, N), dtype=a.dtype, device=a.device)
+    if splits is None:
+        splits = mg_splitk_choose(M, N, K)
     need = mg_splitk_workspace_bytes(M, N, splits)
     if workspace is None:
         workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=a.device)

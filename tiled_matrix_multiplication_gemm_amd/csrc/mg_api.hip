@@ -237,6 +237,38 @@ mg_status mg_gemm_batched(const void* A, const void* B, void* C, int64_t batch, 
                        in_dtype, out_dtype, false, stream, batch, batch_stride_a, batch_stride_b, batch_stride_c);
 }
 
+int64_t mg_splitk_choose(int64_t M, int64_t N, int64_t K) {
+    // Time model per split count s (seconds): rounds of 256 tiles, each tile
+    // BM*BN*(K/s) outputs-times-k at the row's relative rate (a 256x256x8192
+    // tile takes 0.205 ms on MI355X) plus 3 us of fill and drain, and for
+    // s > 1 the partials written and read back at 4 TB/s plus a launch.
+    if (M <= 0 || N <= 0 || K <= 0) return 1;
+    struct Cand {
+        int bm, bn;
+        double rate;
+    };
+    static const Cand cands[] = {{256, 256, 1.00}, {128, 128, 0.49}, {64, 64, 0.50}};
+    const double per_elem_k = 0.205e-3 / (65536.0 * 8192.0);
+    int64_t best_s = 1;
+    double best_t = 0.0;
+    for (int64_t s = 1; s <= 64; s *= 2) {
+        if (s > 1 && K / s < 256) break;  // keep at least a few slices per run
+        double t = 0.0;
+        for (const Cand& c : cands) {
+            const int64_t tiles = cdiv(M, c.bm) * cdiv(N, c.bn) * s;
+            const double tt = (double)cdiv(tiles, 256) *
+                              ((double)c.bm * c.bn / c.rate * ((double)K / s) * per_elem_k + 3e-6);
+            if (t == 0.0 || tt < t) t = tt;
+        }
+        if (s > 1) t += 2.0 * s * M * N * 4.0 / 4e12 + 3e-6;
+        if (best_t == 0.0 || t < best_t * 0.95) {  // a split must win by 5 %
+            best_t = t;
+            best_s = s;
+        }
+    }
+    return best_s;
+}
+
 size_t mg_splitk_workspace_bytes(int64_t M, int64_t N, int64_t splits) {
     if (M <= 0 || N <= 0 || splits <= 0) return 0;
     return (size_t)(splits * M * N) * sizeof(float);
