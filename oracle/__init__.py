@@ -71,6 +71,19 @@ def _configure(lib):
                                      f64p, u16p, cint]
     lib.orc_grouped_gemm.restype = cint
     lib.orc_grouped_gemm.argtypes = [u16p, u16p, i32p, i64, i64, i64, i64, i64, i64, cint, f64p, u16p, cint]
+    u32p = ctypes.POINTER(ctypes.c_uint32)
+    lib.orc_decode32.restype = ctypes.c_double
+    lib.orc_decode32.argtypes = [ctypes.c_uint32]
+    lib.orc_encode32.restype = ctypes.c_uint32
+    lib.orc_encode32.argtypes = [ctypes.c_double]
+    lib.orc_decode32_array.restype = None
+    lib.orc_decode32_array.argtypes = [u32p, f64p, i64]
+    lib.orc_encode32_array.restype = None
+    lib.orc_encode32_array.argtypes = [f64p, u32p, i64]
+    lib.orc_gemm_d.restype = cint
+    lib.orc_gemm_d.argtypes = [f64p, f64p, i64, i64, i64, f64p]
+    lib.orc_gemm_d_sampled.restype = cint
+    lib.orc_gemm_d_sampled.argtypes = [f64p, f64p, i64, i64, i64p, i64p, i64, f64p]
     lib.orc_grouped_sampled.restype = cint
     lib.orc_grouped_sampled.argtypes = [u16p, u16p, i32p, i64, i64, i64, i64, i64, cint, i64p, i64p, i64,
                                         f64p, u16p]
@@ -230,3 +243,48 @@ def grouped_sampled(X, W, offsets, dtype: int, rows, cols):
     if rc != 0:
         raise ValueError("a sampled row lies in no expert")
     return ref, ref_q
+
+
+# ---- fp32 -------------------------------------------------------------------
+def decode32(bits) -> np.ndarray:
+    """Exact values (fp64) of fp32 bit patterns, from the IEEE field definitions."""
+    b = np.ascontiguousarray(bits, dtype=np.uint32)
+    out = np.empty(b.shape, dtype=np.float64)
+    _L().orc_decode32_array(_ptr(b, ctypes.c_uint32), _ptr(out, ctypes.c_double), b.size)
+    return out
+
+
+def encode32(x) -> np.ndarray:
+    """fp64 values rounded once to fp32 (ties to even), as bit patterns."""
+    a = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(a.shape, dtype=np.uint32)
+    _L().orc_encode32_array(_ptr(a, ctypes.c_double), _ptr(out, ctypes.c_uint32), a.size)
+    return out
+
+
+def gemm_f32(A, B):
+    """fp32 GEMM oracle: A [M,K], B [K,N] fp32 bit patterns (uint32).  Returns
+    (ref, ref_q): the k-ascending fp64 sum of the exact products and its
+    single RNE rounding to fp32 (bit patterns)."""
+    Ad, Bd = decode32(A), decode32(B)
+    M, K = Ad.shape
+    _, N = Bd.shape
+    ref = np.empty((M, N), dtype=np.float64)
+    if M and N:
+        _L().orc_gemm_d(_ptr(np.ascontiguousarray(Ad), ctypes.c_double), _ptr(np.ascontiguousarray(Bd), ctypes.c_double),
+                        M, N, K, _ptr(ref, ctypes.c_double))
+    return ref, encode32(ref)
+
+
+def gemm_f32_sampled(A, B, rows, cols):
+    Ad, Bd = np.ascontiguousarray(decode32(A)), np.ascontiguousarray(decode32(B))
+    M, K = Ad.shape
+    _, N = Bd.shape
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    if rows.size and (rows.min() < 0 or rows.max() >= M or cols.min() < 0 or cols.max() >= N):
+        raise IndexError("sample position outside the output")
+    ref = np.empty(rows.shape, dtype=np.float64)
+    _L().orc_gemm_d_sampled(_ptr(Ad, ctypes.c_double), _ptr(Bd, ctypes.c_double), N, K, _ptr(rows, ctypes.c_int64),
+                            _ptr(cols, ctypes.c_int64), rows.size, _ptr(ref, ctypes.c_double))
+    return ref, encode32(ref)

@@ -11,7 +11,7 @@
  *   C[i,j] = sum_{k=0..K-1} a(i,k) * b(k,j)             (k ascending, fp64)
  *   optionally  C[i,j] += bias[j]   then   C[i,j] = max(C[i,j], 0)
  *
- * where a, b and bias are the exact values of the fp16 / bf16 inputs.  The
+ * where a, b and bias are the exact values of the fp16 / bf16 (or fp32) inputs.  The
  * unrounded fp64 value is returned as `ref` (tolerance check) and the same
  * value rounded ONCE to the output type, IEEE round-to-nearest-even, as
  * `ref_q` (bit-exact check).
@@ -41,12 +41,14 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORC_F16 = 0, ORC_BF16 = 1 };
+enum { ORC_F16 = 0, ORC_BF16 = 1, ORC_F32 = 2 };
 
 /* ---------------------------------------------------------------------------
- * Binary16 / bfloat16 <-> double, from the IEEE 754 field definitions.
+ * Binary16 / bfloat16 / binary32 <-> double, from the IEEE 754 field
+ * definitions.
  *   fp16 : 1 sign, 5 exponent (bias 15), 10 fraction bits
  *   bf16 : 1 sign, 8 exponent (bias 127), 7 fraction bits
+ *   fp32 : 1 sign, 8 exponent (bias 127), 23 fraction bits
  * ------------------------------------------------------------------------- */
 typedef struct {
     int frac_bits; /* p  */
@@ -56,17 +58,17 @@ typedef struct {
 
 static orc_format fmt_of(int dtype) {
     orc_format f;
-    if (dtype == ORC_F16) { f.frac_bits = 10; f.exp_bits = 5; f.bias = 15; }
-    else                  { f.frac_bits = 7;  f.exp_bits = 8; f.bias = 127; }
+    if (dtype == ORC_F16)      { f.frac_bits = 10; f.exp_bits = 5; f.bias = 15; }
+    else if (dtype == ORC_F32) { f.frac_bits = 23; f.exp_bits = 8; f.bias = 127; }
+    else                       { f.frac_bits = 7;  f.exp_bits = 8; f.bias = 127; }
     return f;
 }
 
-double orc_decode(uint16_t bits, int dtype) {
-    orc_format f = fmt_of(dtype);
-    int sign = (bits >> 15) & 1;
-    int emask = (1 << f.exp_bits) - 1;
-    int e = (bits >> f.frac_bits) & emask;
-    int frac = bits & ((1 << f.frac_bits) - 1);
+static double decode_fmt(uint64_t bits, orc_format f) {
+    int sign = (int)((bits >> (f.frac_bits + f.exp_bits)) & 1u);
+    uint64_t emask = (1u << f.exp_bits) - 1u;
+    uint64_t e = (bits >> f.frac_bits) & emask;
+    uint64_t frac = bits & ((1ull << f.frac_bits) - 1u);
     double v;
     if (e == emask) {
         v = frac ? NAN : INFINITY;
@@ -74,7 +76,7 @@ double orc_decode(uint16_t bits, int dtype) {
         /* subnormal: frac * 2^(1 - bias - p) */
         v = ldexp((double)frac, 1 - f.bias - f.frac_bits);
     } else {
-        v = ldexp((double)((1 << f.frac_bits) + frac), e - f.bias - f.frac_bits);
+        v = ldexp((double)((1ull << f.frac_bits) + frac), (int)e - f.bias - f.frac_bits);
     }
     return sign ? -v : v;
 }
@@ -84,18 +86,17 @@ double orc_decode(uint16_t bits, int dtype) {
  * rounded with rint() (round-half-even under the default rounding mode) and
  * scaled back; both scalings are exact in double for every finite input of
  * the magnitudes reachable here. */
-uint16_t orc_encode(double x, int dtype) {
-    orc_format f = fmt_of(dtype);
+static uint64_t encode_fmt(double x, orc_format f) {
     int emax = f.bias;            /* largest unbiased exponent of a finite value */
     int emin = 1 - f.bias;        /* smallest normal exponent                   */
-    int emask = (1 << f.exp_bits) - 1;
-    uint16_t sign = signbit(x) ? 0x8000u : 0u;
+    uint64_t emask = (1u << f.exp_bits) - 1u;
+    uint64_t sign = signbit(x) ? (1ull << (f.frac_bits + f.exp_bits)) : 0u;
     if (isnan(x)) {
         /* quiet NaN: exponent all ones, top fraction bit set */
-        return (uint16_t)(sign | (emask << f.frac_bits) | (1u << (f.frac_bits - 1)));
+        return sign | (emask << f.frac_bits) | (1ull << (f.frac_bits - 1));
     }
     double a = fabs(x);
-    if (isinf(a)) return (uint16_t)(sign | (emask << f.frac_bits));
+    if (isinf(a)) return sign | (emask << f.frac_bits);
     if (a == 0.0) return sign;
 
     int e2;
@@ -107,17 +108,30 @@ uint16_t orc_encode(double x, int dtype) {
     double v = ldexp(n, (int)quantum_exp);        /* rounded magnitude        */
 
     if (v >= ldexp(1.0, emax + 1))                /* rounds past the largest finite */
-        return (uint16_t)(sign | (emask << f.frac_bits));
+        return sign | (emask << f.frac_bits);
 
     if (v < ldexp(1.0, emin)) {
         /* subnormal (or zero): fraction field = number of quanta at emin */
-        return (uint16_t)(sign | (uint16_t)n);
+        return sign | (uint64_t)n;
     }
     int ev;
     (void)frexp(v, &ev);
     int Ev = ev - 1;
     double frac = ldexp(v, f.frac_bits - Ev) - ldexp(1.0, f.frac_bits);
-    return (uint16_t)(sign | ((Ev + f.bias) << f.frac_bits) | (uint16_t)frac);
+    return sign | ((uint64_t)(Ev + f.bias) << f.frac_bits) | (uint64_t)frac;
+}
+
+double orc_decode(uint16_t bits, int dtype) { return decode_fmt(bits, fmt_of(dtype)); }
+uint16_t orc_encode(double x, int dtype) { return (uint16_t)encode_fmt(x, fmt_of(dtype)); }
+double orc_decode32(uint32_t bits) { return decode_fmt(bits, fmt_of(ORC_F32)); }
+uint32_t orc_encode32(double x) { return (uint32_t)encode_fmt(x, fmt_of(ORC_F32)); }
+
+void orc_decode32_array(const uint32_t* src, double* dst, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) dst[i] = orc_decode32(src[i]);
+}
+
+void orc_encode32_array(const double* src, uint32_t* dst, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) dst[i] = orc_encode32(src[i]);
 }
 
 void orc_decode_array(const uint16_t* src, double* dst, int64_t n, int dtype) {
@@ -306,6 +320,32 @@ int orc_grouped_sampled(const uint16_t* X, const uint16_t* W, const int32_t* off
             acc += orc_decode(X[i * ldx + k], dtype) * orc_decode(We[k * ldw + c], dtype);
         if (ref) ref[s] = acc;
         if (ref_q) ref_q[s] = orc_encode(acc, dtype);
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * GEMM of matrices already decoded to double (the fp32 path decodes with
+ * orc_decode32_array): C[i,j] = sum_{k ascending} A[i,k] * B[k,j] in fp64,
+ * A M x K, B K x N, both dense.  Full output, or the listed positions.
+ * ------------------------------------------------------------------------- */
+int orc_gemm_d(const double* A, const double* B, int64_t M, int64_t N, int64_t K, double* ref) {
+    for (int64_t i = 0; i < M; ++i) {
+        for (int64_t n = 0; n < N; ++n) ref[i * N + n] = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const double a = A[i * K + k];
+            for (int64_t n = 0; n < N; ++n) ref[i * N + n] += a * B[k * N + n];
+        }
+    }
+    return 0;
+}
+
+int orc_gemm_d_sampled(const double* A, const double* B, int64_t N, int64_t K, const int64_t* rows,
+                       const int64_t* cols, int64_t count, double* ref) {
+    for (int64_t s = 0; s < count; ++s) {
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; ++k) acc += A[rows[s] * K + k] * B[k * N + cols[s]];
+        ref[s] = acc;
     }
     return 0;
 }
