@@ -49,7 +49,7 @@ typedef enum {
     MG_ERR_BAD_CONFIG = 6          /* unknown configuration id, or a BK the configuration cannot use */
 } mg_status;
 
-typedef enum { MG_F16 = 0, MG_BF16 = 1 } mg_dtype;
+typedef enum { MG_F16 = 0, MG_BF16 = 1, MG_F32 = 2 } mg_dtype;
 
 /* Human-readable name of a status code (static storage). */
 const char* mg_status_string(mg_status status);

@@ -57,7 +57,9 @@ def test_status_strings(L):
 @pytest.mark.parametrize("kw,status", [
     (dict(A=None), INVALID), (dict(B=None), INVALID), (dict(C=None), INVALID),
     (dict(M=-1), INVALID), (dict(N=-5), INVALID), (dict(K=-1), INVALID),
-    (dict(din=2, dout=2), DTYPE), (dict(din=F16, dout=BF16), DTYPE), (dict(din=7, dout=F16), DTYPE),
+    (dict(din=3, dout=3), DTYPE), (dict(din=F16, dout=BF16), DTYPE), (dict(din=7, dout=F16), DTYPE),
+    (dict(din=2, dout=F16), DTYPE), (dict(din=2, dout=2, sam=66), MISALIGNED), (dict(din=2, dout=2, sak=2), LAYOUT),
+    (dict(din=2, dout=2, sam=1, sak=64), LAYOUT), (dict(din=2, dout=2, K=40), LAYOUT), (dict(din=2, dout=2, N=62, sbk=64, scm=64), LAYOUT),
     (dict(sak=2), LAYOUT), (dict(sbn=64), LAYOUT), (dict(scn=0), LAYOUT),
     (dict(sam=32), LAYOUT), (dict(sbk=8), LAYOUT),
     (dict(A=P + 2), MISALIGNED), (dict(B=P + 8), MISALIGNED), (dict(C=P + 4), MISALIGNED),
@@ -137,6 +139,13 @@ def test_splitk_choice_model(L):
         s = ch(*shape)
         assert s >= 1 and s & (s - 1) == 0 and (s == 1 or shape[2] // s >= 256)
     assert ch(0, 8, 8) == 1 and ch(8, 8, 0) == 1
+
+
+def test_f32_only_on_the_plain_gemm(L):
+    F32 = 2
+    assert gemm_batched(L, din=F32, dout=F32) == DTYPE
+    assert L.mg_gemm_splitk(P, P, P, P, 1 << 20, 2, 64, 64, 64, 64, 1, 64, 1, 64, 1, F32, F32, S) == DTYPE
+    assert L.mg_prepack_a(P, P, 64, 64, 64, 64, F32, S) == DTYPE
 
 
 def test_zero_sized_problems_are_noops(L):

@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 
 import tiled_matrix_multiplication_gemm_amd as mg
+import oracle
 from oracle import compare, layout
 from tiled_matrix_multiplication_gemm_amd import inputs
 from tests.gpu_util import (F16, BF16, Guarded, announce, assert_bitexact, assert_tolerance, to_dev, to_host)
@@ -433,6 +434,55 @@ def test_splitk_tall_skinny_large_k_sampled(orc):
             assert_bitexact(got[rows, cols], ref_q, BF16, c.name)
         else:
             assert_tolerance(got[rows, cols], ref, BF16, c.name)
+
+
+# fp32 GEMM on the fp32 matrix cores.  Integer-valued inputs: products and
+# partial sums are exact in fp32, so the single rounding of the oracle's
+# exact sum is the only correct result (bit-exact).  Random inputs: the fp32
+# accumulation error is at most K * 2^-24 * sum_k |a_k b_k| (one rounding per
+# fused step), plus the final rounding, and the gate is twice that.
+F32_SHAPES = [(64, 64, 64), (1, 4, 16), (130, 200, 64), (256, 132, 128), (513, 260, 48), (384, 384, 512)]
+
+
+def run_f32(case):
+    import torch
+
+    A = torch.from_numpy(np.ascontiguousarray(case.A).view(np.float32)).cuda()
+    B = torch.from_numpy(np.ascontiguousarray(case.B).view(np.float32)).cuda()
+    out = torch.full((case.M + 2, case.N), float("nan"), device="cuda")
+    C = out[1:-1]
+    if case.bias is not None:
+        bias = torch.from_numpy(np.ascontiguousarray(case.bias).view(np.float32)).cuda()
+        mg.mg_gemm_bias_relu(A, B, bias, out=C)
+    else:
+        mg.mg_gemm(A, B, out=C)
+    torch.cuda.synchronize()
+    full = out.cpu().numpy()
+    guards = np.isnan(full[0]).all() and np.isnan(full[-1]).all()
+    return full[1:-1].copy(), guards
+
+
+def test_f32_gemm(orc):
+    for i, (M, N, K) in enumerate(F32_SHAPES):
+        for integer in (True, False):
+            epi = (i + integer) % 2 == 1
+            c = inputs.dense_f32(M, N, K, 9000 + 10 * i + integer, integer=integer, epilogue=epi)
+            announce("f32 M=%d N=%d K=%d int=%s epi=%s" % (M, N, K, integer, epi))
+            got, guards = run_f32(c)
+            assert guards, "write outside the output"
+            ref, ref_q = oracle.gemm_f32(c.A, c.B)
+            if epi:
+                ref = np.maximum(ref + oracle.decode32(c.bias)[None, :], 0.0)
+                ref_q = oracle.encode32(ref)
+            if integer:
+                bad = np.argwhere(got.view(np.uint32) != ref_q)
+                assert bad.size == 0, "f32 integer mismatch at %s: got %r want %r" % (
+                    bad[:5].tolist(), got.view(np.uint32)[tuple(bad[0])], ref_q[tuple(bad[0])])
+            else:
+                absprod = np.abs(oracle.decode32(c.A)) @ np.abs(oracle.decode32(c.B))
+                tol = 2.0 * (K * 2.0 ** -24 * absprod + 2.0 ** -24 * np.abs(ref)) + 1e-30
+                err = np.abs(got.astype(np.float64) - ref)
+                assert np.all(err <= tol), "f32 error %g above bound %g" % (err.max(), tol[err.argmax() // N, err.argmax() % N])
 
 
 def run_grouped(case):

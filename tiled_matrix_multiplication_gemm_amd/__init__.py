@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(_PKG, "libmi355gemm.so")
 
 MG_F16 = 0
 MG_BF16 = 1
+MG_F32 = 2
 
 _lock = threading.Lock()
 _lib = None
@@ -109,7 +110,9 @@ def _dtype_code(t) -> int:
         return MG_F16
     if t.dtype == torch.bfloat16:
         return MG_BF16
-    raise RuntimeError("MG_ERR_UNSUPPORTED_DTYPE: tensor dtype %s is not float16/bfloat16" % t.dtype)
+    if t.dtype == torch.float32:
+        return MG_F32
+    raise RuntimeError("MG_ERR_UNSUPPORTED_DTYPE: tensor dtype %s is not float16/bfloat16/float32" % t.dtype)
 
 
 def _stream(t):

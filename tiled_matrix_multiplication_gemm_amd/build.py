@@ -21,7 +21,8 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 
 
 def sources():
-    return [os.path.join(CSRC, "mg_api.hip")] + sorted(glob.glob(os.path.join(CSRC, "mg_row*.hip")))
+    return [os.path.join(CSRC, "mg_api.hip"), os.path.join(CSRC, "mg_f32.hip")] + sorted(
+        glob.glob(os.path.join(CSRC, "mg_row*.hip")))
 
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

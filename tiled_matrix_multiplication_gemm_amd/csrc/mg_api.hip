@@ -100,14 +100,14 @@ int select_config_splitk(int64_t M, int64_t N, int64_t splits) {
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // A rows x cols matrix with row stride ld and inner stride inner.
-mg_status check_matrix(const void* p, int64_t rows, int64_t cols, int64_t ld, int64_t inner) {
+mg_status check_matrix(const void* p, int64_t rows, int64_t cols, int64_t ld, int64_t inner, int esize = 2) {
     if (rows < 0 || cols < 0) return MG_ERR_INVALID_ARG;
     if (rows == 0 || cols == 0) return MG_OK;  // no extent: never dereferenced
     if (p == nullptr) return MG_ERR_INVALID_ARG;
     if (cols > 1 && inner != 1) return MG_ERR_UNSUPPORTED_LAYOUT;
     if (rows > 1 && ld < cols) return MG_ERR_UNSUPPORTED_LAYOUT;
     if (!aligned16(p)) return MG_ERR_MISALIGNED;
-    if (rows > 1 && (ld % 8) != 0) return MG_ERR_MISALIGNED;
+    if (rows > 1 && (ld * esize) % 16 != 0) return MG_ERR_MISALIGNED;
     return MG_OK;
 }
 
@@ -155,11 +155,48 @@ mg_status launch(int cfg, int dt, bool epi, int mode, KArgs& a, hipStream_t s, i
     return st;
 }
 
+// fp32 GEMM (the fp32 matrix cores): row-major operands on the fp32 kernel,
+// which needs K in whole 16-element slices, N % 4 == 0 and 16-byte rows.
+mg_status gemm_f32(const void* A, const void* B, const void* bias, void* C, int64_t M, int64_t N, int64_t K,
+                   int64_t sam, int64_t sak, int64_t sbk, int64_t sbn, int64_t scm, int64_t scn, mg_dtype in_dtype,
+                   mg_dtype out_dtype, bool epi, hipStream_t stream) {
+    if (in_dtype != MG_F32 || out_dtype != MG_F32) return MG_ERR_UNSUPPORTED_DTYPE;
+    if (!(sak == 1 || K <= 1) || !(sbn == 1 || N <= 1)) return MG_ERR_UNSUPPORTED_LAYOUT;
+    MG_TRY(check_matrix(A, M, K, sam, sak, 4));
+    MG_TRY(check_matrix(B, K, N, sbk, sbn, 4));
+    MG_TRY(check_matrix(C, M, N, scm, scn, 4));
+    if (epi && N > 0 && M > 0 && bias == nullptr) return MG_ERR_INVALID_ARG;
+    if (M == 0 || N == 0) return MG_OK;
+    if (K % kF32SliceK != 0 || N % 4 != 0) return MG_ERR_UNSUPPORTED_LAYOUT;
+    const int64_t lim = (int64_t)1 << 31;
+    if ((int64_t)kF32TileM * sam * 4 >= lim || ((int64_t)kF32SliceK * sbk + kF32TileN) * 4 >= lim)
+        return MG_ERR_UNSUPPORTED_LAYOUT;
+    KArgs a{};
+    a.A = (const uint16_t*)A;  // the fp32 kernel reinterprets the pointers
+    a.B = (const uint16_t*)B;
+    a.C = (uint16_t*)C;
+    a.bias = (const uint16_t*)bias;
+    a.M = M; a.N = N; a.K = K;
+    a.lda = sam; a.ldb = sbk; a.ldc = scm;
+    a.tiles_m = (int32_t)cdiv(M, kF32TileM);
+    a.tiles_n = (int32_t)cdiv(N, kF32TileN);
+    a.group_m = kGroupM;
+    a.xcd_remap = 1;
+    a.batch = 1;
+    const int64_t grid = (int64_t)a.tiles_m * a.tiles_n;
+    if (grid > 0x7fffffff) return MG_ERR_INVALID_ARG;
+    return launch_f32(epi, a, grid, stream);
+}
+
 mg_status gemm_common(const void* A, const void* B, const void* bias, void* C, int64_t M, int64_t N, int64_t K,
                       int64_t sam, int64_t sak, int64_t sbk, int64_t sbn, int64_t scm, int64_t scn,
                       mg_dtype in_dtype, mg_dtype out_dtype, bool epi, hipStream_t stream, int64_t batch = 1,
                       int64_t sab = 0, int64_t sbb = 0, int64_t scb = 0) {
     if (M < 0 || N < 0 || K < 0 || batch < 0) return MG_ERR_INVALID_ARG;
+    if (in_dtype == MG_F32 || out_dtype == MG_F32) {
+        if (batch != 1) return MG_ERR_UNSUPPORTED_DTYPE;
+        return gemm_f32(A, B, bias, C, M, N, K, sam, sak, sbk, sbn, scm, scn, in_dtype, out_dtype, epi, stream);
+    }
     if (batch == 0) return check_dtype(in_dtype, out_dtype);  // no entries: pointers never used
     if (batch > 1) {
         // entries of A and B may repeat (stride 0); entries of C may not overlap

@@ -61,4 +61,8 @@ MG_DECLARE_ROW(5);
 MG_DECLARE_ROW(6);
 MG_DECLARE_ROW(7);
 
+// fp32 GEMM: one configuration (mg_f32.h), defined in mg_f32.hip
+inline constexpr int kF32TileM = 128, kF32TileN = 128, kF32SliceK = 16;
+mg_status launch_f32(bool epi, const KArgs& a, int64_t grid, hipStream_t s);
+
 }  // namespace mg

@@ -107,6 +107,23 @@ def integer_dense(M, N, K, dtype, seed, lo=-4, hi=4, epilogue=False, name="custo
                      None if bias is None else to_bits(bias, dtype), relu=epilogue, integer=True)
 
 
+def dense_f32(M, N, K, seed, integer=False, epilogue=False, name="f32"):
+    """fp32 inputs as uint32 bit patterns: N(0,1)/sqrt(K) values, or integers
+    on -4..4 (exact products and sums); bias N(0, 0.1) or integers."""
+    rng = np.random.default_rng(seed)
+    if integer:
+        A = rng.integers(-4, 5, size=(M, K)).astype(np.float32)
+        B = rng.integers(-4, 5, size=(K, N)).astype(np.float32)
+        bias = rng.integers(-4, 5, size=N).astype(np.float32) if epilogue else None
+    else:
+        s = 1.0 / np.sqrt(max(K, 1))
+        A = (rng.standard_normal(size=(M, K)) * s).astype(np.float32)
+        B = (rng.standard_normal(size=(K, N)) * s).astype(np.float32)
+        bias = (rng.standard_normal(size=N) * 0.1).astype(np.float32) if epilogue else None
+    return DenseCase(name, M, N, K, 2, A.view(np.uint32), B.view(np.uint32),
+                     None if bias is None else bias.view(np.uint32), relu=epilogue, integer=integer)
+
+
 def dense_workload(name: str, variant: str = "float") -> DenseCase:
     w = DENSE_WORKLOADS[name]
     if variant == "float":
