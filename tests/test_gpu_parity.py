@@ -441,7 +441,10 @@ def test_splitk_tall_skinny_large_k_sampled(orc):
 # exact sum is the only correct result (bit-exact).  Random inputs: the fp32
 # accumulation error is at most K * 2^-24 * sum_k |a_k b_k| (one rounding per
 # fused step), plus the final rounding, and the gate is twice that.
-F32_SHAPES = [(64, 64, 64), (1, 4, 16), (130, 200, 64), (256, 132, 128), (513, 260, 48), (384, 384, 512)]
+# The last shape takes the 128 x 128 tile with ragged edges; the others below
+# 4096 take 64 x 64.
+F32_SHAPES = [(64, 64, 64), (1, 4, 16), (130, 200, 64), (256, 132, 128), (513, 260, 48), (384, 384, 512),
+              (4095, 4092, 32)]
 
 
 def run_f32(case):

@@ -155,6 +155,19 @@ mg_status launch(int cfg, int dt, bool epi, int mode, KArgs& a, hipStream_t s, i
     return st;
 }
 
+// fp32 tile by how well each fills the chip's workgroup slots: 256 CUs hold
+// 2 workgroups of the 128 x 128 kernel or 3 of the 64 x 64 one.  Per CU the
+// two run at about the same rate with full rounds, and the small tile is
+// weighted 0.9 for its extra operand traffic (measured on 512..8192-sized
+// squares and 8192 x 1024).
+int f32_tile(int64_t M, int64_t N) {
+    const int64_t tl = cdiv(M, kF32TileM[0]) * cdiv(N, kF32TileN[0]);
+    const int64_t ts = cdiv(M, kF32TileM[1]) * cdiv(N, kF32TileN[1]);
+    const double fill_l = (double)tl / (double)(cdiv(tl, 512) * 512);
+    const double fill_s = 0.9 * (double)ts / (double)(cdiv(ts, 768) * 768);
+    return fill_l >= fill_s ? 0 : 1;
+}
+
 // fp32 GEMM (the fp32 matrix cores): row-major operands on the fp32 kernel,
 // which needs K in whole 16-element slices, N % 4 == 0 and 16-byte rows.
 mg_status gemm_f32(const void* A, const void* B, const void* bias, void* C, int64_t M, int64_t N, int64_t K,
@@ -168,8 +181,9 @@ mg_status gemm_f32(const void* A, const void* B, const void* bias, void* C, int6
     if (epi && N > 0 && M > 0 && bias == nullptr) return MG_ERR_INVALID_ARG;
     if (M == 0 || N == 0) return MG_OK;
     if (K % kF32SliceK != 0 || N % 4 != 0) return MG_ERR_UNSUPPORTED_LAYOUT;
+    const int tile = f32_tile(M, N);
     const int64_t lim = (int64_t)1 << 31;
-    if ((int64_t)kF32TileM * sam * 4 >= lim || ((int64_t)kF32SliceK * sbk + kF32TileN) * 4 >= lim)
+    if ((int64_t)kF32TileM[tile] * sam * 4 >= lim || ((int64_t)kF32SliceK * sbk + kF32TileN[tile]) * 4 >= lim)
         return MG_ERR_UNSUPPORTED_LAYOUT;
     KArgs a{};
     a.A = (const uint16_t*)A;  // the fp32 kernel reinterprets the pointers
@@ -178,14 +192,14 @@ mg_status gemm_f32(const void* A, const void* B, const void* bias, void* C, int6
     a.bias = (const uint16_t*)bias;
     a.M = M; a.N = N; a.K = K;
     a.lda = sam; a.ldb = sbk; a.ldc = scm;
-    a.tiles_m = (int32_t)cdiv(M, kF32TileM);
-    a.tiles_n = (int32_t)cdiv(N, kF32TileN);
+    a.tiles_m = (int32_t)cdiv(M, kF32TileM[tile]);
+    a.tiles_n = (int32_t)cdiv(N, kF32TileN[tile]);
     a.group_m = kGroupM;
     a.xcd_remap = 1;
     a.batch = 1;
     const int64_t grid = (int64_t)a.tiles_m * a.tiles_n;
     if (grid > 0x7fffffff) return MG_ERR_INVALID_ARG;
-    return launch_f32(epi, a, grid, stream);
+    return launch_f32(tile, epi, a, grid, stream);
 }
 
 mg_status gemm_common(const void* A, const void* B, const void* bias, void* C, int64_t M, int64_t N, int64_t K,

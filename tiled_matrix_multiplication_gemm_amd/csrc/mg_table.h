@@ -62,7 +62,10 @@ MG_DECLARE_ROW(6);
 MG_DECLARE_ROW(7);
 
 // fp32 GEMM: one configuration (mg_f32.h), defined in mg_f32.hip
-inline constexpr int kF32TileM = 128, kF32TileN = 128, kF32SliceK = 16;
-mg_status launch_f32(bool epi, const KArgs& a, int64_t grid, hipStream_t s);
+// fp32 kernel tiles: 0 = 128 x 128 (large outputs), 1 = 64 x 64 (outputs
+// that leave the CUs idle at 128 x 128).  K slices of 16 values.
+inline constexpr int kF32NumTiles = 2, kF32SliceK = 16;
+inline constexpr int kF32TileM[kF32NumTiles] = {128, 64}, kF32TileN[kF32NumTiles] = {128, 64};
+mg_status launch_f32(int tile, bool epi, const KArgs& a, int64_t grid, hipStream_t s);
 
 }  // namespace mg
