@@ -11,6 +11,11 @@ C[i,j] = sum_k a(i,k) b(k,j) over the exact input values in fp64, k ascending,
 then optional + bias[j] and ReLU, kept unrounded (``ref``) and rounded once
 round-to-nearest-even to the output type (``ref_q``).
 
+GEMM consumers (FlagOS cross-chip page, section 5.3): a 2-D convolution by
+its definition (NHWC input, [KH,KW,C,OC] weights, zero padding, stride,
+dilation), and attention scores Q K^T per head on the GEMM oracle.  im2col,
+pure data movement, sits in ``layout.py``.
+
 Parity pins: every public function here is pinned by ``tests/test_oracle_*``
 against values fixed by the pages or by mathematics (brute force, closed
 forms, identities, exhaustive rounding checks).  Performance has no pin.
@@ -26,6 +31,7 @@ import numpy as np
 
 F16 = 0
 BF16 = 1
+F32 = 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gemm_oracle.c")
@@ -85,6 +91,8 @@ def _configure(lib):
     lib.orc_gemm_d_sampled.restype = cint
     lib.orc_gemm_d_sampled.argtypes = [f64p, f64p, i64, i64, i64p, i64p, i64, f64p]
     lib.orc_grouped_sampled.restype = cint
+    lib.orc_conv2d_d.restype = cint
+    lib.orc_conv2d_d.argtypes = [f64p, f64p] + [i64] * 13 + [i64p, i64p, i64, f64p]
     lib.orc_grouped_sampled.argtypes = [u16p, u16p, i32p, i64, i64, i64, i64, i64, cint, i64p, i64p, i64,
                                         f64p, u16p]
     return lib
@@ -95,8 +103,8 @@ def _load():
     with _lock:
         if _lib is not None:
             return _lib
-        if not os.path.exists(_LIB_PATH):
-            build(force=False)
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build(force=True)
         _lib = _configure(ctypes.CDLL(_LIB_PATH))
         return _lib
 
@@ -288,3 +296,86 @@ def gemm_f32_sampled(A, B, rows, cols):
     _L().orc_gemm_d_sampled(_ptr(Ad, ctypes.c_double), _ptr(Bd, ctypes.c_double), N, K, _ptr(rows, ctypes.c_int64),
                             _ptr(cols, ctypes.c_int64), rows.size, _ptr(ref, ctypes.c_double))
     return ref, encode32(ref)
+
+
+# ---- GEMM consumers: 2-D convolution and attention scores -------------------
+def _decode_any(bits, dtype: int) -> np.ndarray:
+    return decode32(bits) if dtype == F32 else decode(bits, dtype)
+
+
+def _encode_any(x, dtype: int) -> np.ndarray:
+    return encode32(x) if dtype == F32 else encode(x, dtype)
+
+
+def conv_out_hw(H, W, KH, KW, stride=(1, 1), pad=(0, 0), dil=(1, 1)):
+    """Output height and width of a convolution: floor((H + 2p - d (KH - 1) - 1) / s) + 1."""
+    oh = (H + 2 * pad[0] - dil[0] * (KH - 1) - 1) // stride[0] + 1
+    ow = (W + 2 * pad[1] - dil[1] * (KW - 1) - 1) // stride[1] + 1
+    return oh, ow
+
+
+def conv2d(x, w, dtype: int, stride=(1, 1), pad=(0, 0), dil=(1, 1), bias=None, relu: bool = False,
+           rows=None, cols=None):
+    """2-D convolution oracle (cross-correlation with zero padding, the
+    definition in gemm_oracle.c).  x: NHWC [Nb,H,W,C] bit patterns, w: [KH,KW,C,OC]
+    bit patterns, dtype F16 / BF16 / F32.  Returns (ref, ref_q) of shape
+    [Nb,OH,OW,OC], or, with `rows` (output row m = (n OH + oh) OW + ow) and
+    `cols` (output channel), at those positions only.  Optional + bias[o], then
+    ReLU (to +0.0), before the single rounding."""
+    Nb, H, W, C = x.shape
+    KH, KW, C2, OC = w.shape
+    if C2 != C:
+        raise ValueError("channel mismatch")
+    xd = np.ascontiguousarray(_decode_any(x, dtype))
+    wd = np.ascontiguousarray(_decode_any(w, dtype))
+    OH, OW = conv_out_hw(H, W, KH, KW, stride, pad, dil)
+    if OH < 1 or OW < 1:
+        raise ValueError("empty output")
+    if rows is not None:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        cols = np.ascontiguousarray(cols, dtype=np.int64)
+        if rows.size and (rows.min() < 0 or rows.max() >= Nb * OH * OW or cols.min() < 0 or cols.max() >= OC):
+            raise IndexError("sample position outside the output")
+        ref = np.empty(rows.shape, dtype=np.float64)
+        rp, cp, count = _ptr(rows, ctypes.c_int64), _ptr(cols, ctypes.c_int64), rows.size
+        oc_of = cols
+    else:
+        ref = np.empty((Nb, OH, OW, OC), dtype=np.float64)
+        rp = cp = None
+        count = 0
+        oc_of = None
+    rc = _L().orc_conv2d_d(_ptr(xd, ctypes.c_double), _ptr(wd, ctypes.c_double), Nb, H, W, C, OC, KH, KW,
+                           stride[0], stride[1], pad[0], pad[1], dil[0], dil[1], rp, cp, count,
+                           _ptr(ref, ctypes.c_double))
+    if rc != 0:
+        raise ValueError("bad convolution parameters (code %d)" % rc)
+    if bias is not None:
+        bd = _decode_any(bias, dtype)
+        ref = ref + (bd[oc_of] if oc_of is not None else bd)
+    if relu:
+        ref = np.where(ref > 0.0, ref, 0.0)
+    return ref, _encode_any(ref, dtype)
+
+
+def attention_scores(Q, K, dtype: int):
+    """Attention scores S[h] = Q[h] K[h]^T for every head h (the QK^T product of
+    the FlagOS page, section 5.3), on the GEMM oracle with B = K[h]^T.
+    Q [BH,Lq,d], K [BH,Lk,d] 16-bit bit patterns.  Returns (ref, ref_q) [BH,Lq,Lk]."""
+    BH, Lq, d = Q.shape
+    _, Lk, _ = K.shape
+    ref = np.empty((BH, Lq, Lk), dtype=np.float64)
+    ref_q = np.empty((BH, Lq, Lk), dtype=np.uint16)
+    for h in range(BH):
+        ref[h], ref_q[h] = gemm(np.ascontiguousarray(Q[h]), np.ascontiguousarray(K[h].T), dtype)
+    return ref, ref_q
+
+
+def attention_scores_sampled(Q, K, dtype: int, heads, rows, cols):
+    """S[h,i,j] = sum_{t ascending} q(h,i,t) k(h,j,t) in fp64 at the listed positions."""
+    heads, rows, cols = (np.asarray(v, dtype=np.int64) for v in (heads, rows, cols))
+    q = decode(np.ascontiguousarray(Q[heads, rows]), dtype)
+    k = decode(np.ascontiguousarray(K[heads, cols]), dtype)
+    ref = np.zeros(heads.shape, dtype=np.float64)
+    for t in range(q.shape[1]):
+        ref += q[:, t] * k[:, t]
+    return ref, encode(ref, dtype)

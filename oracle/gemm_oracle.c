@@ -349,3 +349,59 @@ int orc_gemm_d_sampled(const double* A, const double* B, int64_t N, int64_t K, c
     }
     return 0;
 }
+
+/* ---------------------------------------------------------------------------
+ * 2-D convolution (a GEMM consumer: the FlagOS cross-chip page, section 5.3,
+ * lowers it to a GEMM through im2col).  The plain definition, cross-
+ * correlation as deep-learning frameworks define it, over values already
+ * decoded to double:
+ *
+ *   y[n,oh,ow,o] = sum_{kh, kw, c ascending} x[n, ih, iw, c] * w[kh, kw, c, o]
+ *   ih = oh*sh - ph + kh*dh,  iw = ow*sw - pw + kw*dw
+ *
+ * with x taken as 0 where ih or iw falls outside the image (zero padding).
+ * x is NHWC [Nb,H,W,C], w is [KH,KW,C,OC], y is [Nb,OH,OW,OC], all dense;
+ * OH = (H + 2 ph - dh (KH - 1) - 1) / sh + 1 (floor), OW likewise.
+ * Output rows are m = (n*OH + oh)*OW + ow; with `rows`/`cols` the listed
+ * (m, o) positions only (count of them), else the full output.
+ * ------------------------------------------------------------------------- */
+static double conv_point(const double* x, const double* w, int64_t H, int64_t W, int64_t C, int64_t OC,
+                         int64_t KH, int64_t KW, int64_t sh, int64_t sw, int64_t ph, int64_t pw, int64_t dh,
+                         int64_t dw, int64_t n, int64_t oh, int64_t ow, int64_t o) {
+    double acc = 0.0;
+    for (int64_t kh = 0; kh < KH; ++kh) {
+        const int64_t ih = oh * sh - ph + kh * dh;
+        for (int64_t kw = 0; kw < KW; ++kw) {
+            const int64_t iw = ow * sw - pw + kw * dw;
+            const int inside = ih >= 0 && ih < H && iw >= 0 && iw < W;
+            for (int64_t c = 0; c < C; ++c) {
+                const double xv = inside ? x[((n * H + ih) * W + iw) * C + c] : 0.0;
+                acc += xv * w[((kh * KW + kw) * C + c) * OC + o];
+            }
+        }
+    }
+    return acc;
+}
+
+int orc_conv2d_d(const double* x, const double* w, int64_t Nb, int64_t H, int64_t W, int64_t C, int64_t OC,
+                 int64_t KH, int64_t KW, int64_t sh, int64_t sw, int64_t ph, int64_t pw, int64_t dh, int64_t dw,
+                 const int64_t* rows, const int64_t* cols, int64_t count, double* y) {
+    if (sh < 1 || sw < 1 || dh < 1 || dw < 1 || ph < 0 || pw < 0 || KH < 1 || KW < 1) return 1;
+    const int64_t OH = (H + 2 * ph - dh * (KH - 1) - 1) / sh + 1;
+    const int64_t OW = (W + 2 * pw - dw * (KW - 1) - 1) / sw + 1;
+    if (H + 2 * ph - dh * (KH - 1) - 1 < 0 || W + 2 * pw - dw * (KW - 1) - 1 < 0) return 2;
+    if (rows) {
+        for (int64_t s = 0; s < count; ++s) {
+            const int64_t m = rows[s], n = m / (OH * OW), oh = (m / OW) % OH, ow = m % OW;
+            y[s] = conv_point(x, w, H, W, C, OC, KH, KW, sh, sw, ph, pw, dh, dw, n, oh, ow, cols[s]);
+        }
+        return 0;
+    }
+    for (int64_t n = 0; n < Nb; ++n)
+        for (int64_t oh = 0; oh < OH; ++oh)
+            for (int64_t ow = 0; ow < OW; ++ow)
+                for (int64_t o = 0; o < OC; ++o)
+                    y[((n * OH + oh) * OW + ow) * OC + o] =
+                        conv_point(x, w, H, W, C, OC, KH, KW, sh, sw, ph, pw, dh, dw, n, oh, ow, o);
+    return 0;
+}

@@ -9,7 +9,9 @@ arithmetic on values:
   Gluon/Triton portability page; explained in "Triton study notes", section
   2.3.7, with its 9x9 worked example);
 * the shared-memory budget of a tile configuration (FlagOS cross-chip page,
-  section 2.1).
+  section 2.1);
+* im2col, which turns a convolution into a GEMM (FlagOS cross-chip page,
+  section 5.3).
 
 None of this is imported by the library.
 """
@@ -87,3 +89,27 @@ def lds_bytes(BM: int, BN: int, BK: int, elem_bytes: int, stages: int) -> int:
     """Shared-memory footprint of one tile configuration: one A tile and one
     B tile per pipeline stage (FlagOS cross-chip page, section 2.1)."""
     return (BM * BK + BK * BN) * elem_bytes * stages
+
+
+def im2col(x, KH, KW, stride=(1, 1), pad=(0, 0), dil=(1, 1)):
+    """im2col of an NHWC image batch (FlagOS cross-chip page, section 5.3:
+    convolution becomes a GEMM).  Row m = (n OH + oh) OW + ow of the result
+    holds, at column k = (kh KW + kw) C + c, the input value x[n, ih, iw, c]
+    with ih = oh sh - ph + kh dh and iw = ow sw - pw + kw dw, or 0 where
+    (ih, iw) lies outside the image.  Pure data movement, any element type;
+    the zero is the all-zero bit pattern (+0.0)."""
+    Nb, H, W, C = x.shape
+    sh, sw = stride
+    ph, pw = pad
+    dh, dw = dil
+    OH = (H + 2 * ph - dh * (KH - 1) - 1) // sh + 1
+    OW = (W + 2 * pw - dw * (KW - 1) - 1) // sw + 1
+    xp = np.zeros((Nb, H + 2 * ph, W + 2 * pw, C), dtype=x.dtype)
+    xp[:, ph:ph + H, pw:pw + W, :] = x
+    out = np.zeros((Nb, OH, OW, KH, KW, C), dtype=x.dtype)
+    for kh in range(KH):
+        for kw in range(KW):
+            # padded row index of (oh, kh) is oh sh + kh dh
+            out[:, :, :, kh, kw, :] = xp[:, kh * dh: kh * dh + sh * (OH - 1) + 1: sh,
+                                         kw * dw: kw * dw + sw * (OW - 1) + 1: sw, :]
+    return out.reshape(Nb * OH * OW, KH * KW * C)

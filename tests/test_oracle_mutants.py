@@ -3,7 +3,8 @@
 Each case compiles a copy of oracle/gemm_oracle.c with one deliberate,
 plausible mistake (a dropped term, a wrong index, a wrong sign, ties rounded
 away from zero, a signed-zero ReLU, a wrong subnormal scale, a wrong expert
-weight) into a temporary directory, binds the oracle's Python functions to
+weight; in the convolution a dropped dilation, a padding sign, swapped kernel
+axes, non-zero padding) into a temporary directory, binds the oracle's Python functions to
 it, and checks that at least one pin fails.  The real oracle is rebound
 afterwards.  CPU only; nothing here touches the GPU path.
 """
@@ -14,6 +15,7 @@ import pytest
 
 import oracle
 from tests import test_oracle_gemm as G
+from tests import test_oracle_consumers as CV
 from tests import test_oracle_rounding as R
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "gemm_oracle.c")
@@ -33,6 +35,14 @@ MUTANTS = {
                                            "double* Wd = decode_matrix(W + (e > 0 ? e - 1 : 0) * stride_we, K, N, ldw, dtype);"),
     "accumulates in single precision": ("for (int64_t n = 0; n < j->N; ++n) acc[n] += a * brow[n];",
                                         "for (int64_t n = 0; n < j->N; ++n) acc[n] = (float)(acc[n] + (float)(a * brow[n]));"),
+    "convolution ignores the dilation": ("const int64_t ih = oh * sh - ph + kh * dh;",
+                                         "const int64_t ih = oh * sh - ph + kh;"),
+    "convolution pads on the wrong side": ("const int64_t iw = ow * sw - pw + kw * dw;",
+                                           "const int64_t iw = ow * sw + pw + kw * dw;"),
+    "convolution swaps kh and kw in the weights": ("acc += xv * w[((kh * KW + kw) * C + c) * OC + o];",
+                                                   "acc += xv * w[((kw * KH + kh) * C + c) * OC + o];"),
+    "convolution pads with ones": ("const double xv = inside ? x[((n * H + ih) * W + iw) * C + c] : 0.0;",
+                                   "const double xv = inside ? x[((n * H + ih) * W + iw) * C + c] : 1.0;"),
 }
 
 PINS = [
@@ -45,6 +55,9 @@ PINS = [
     lambda o: R.test_decode_all_patterns_match_numpy(o, 0),
     lambda o: R.test_encode_midpoints_ties_to_even(o, 0),
     lambda o: R.test_encode_midpoints_ties_to_even(o, 1),
+    lambda o: CV.test_conv_worked_examples(o),
+    lambda o: CV.test_conv_matches_torch_float64(o, CV.CONV_PARAMS[3], 0),
+    lambda o: CV.test_conv_matches_torch_float64(o, CV.CONV_PARAMS[4], 0),
 ]
 
 
