@@ -12,11 +12,13 @@
  *  - Element types: fp16 or bf16 in, the same type out.  Products are exact
  *    and are accumulated in fp32 ("Triton study notes", section 2.1: always
  *    accumulate in fp32); the fp32 result is rounded once, to nearest even,
- *    to the output type.
- *  - Layout: row-major matrices with a unit inner stride.  Leading strides
- *    are in elements, must be >= the row length and a multiple of 8 (so
- *    every row starts on a 16-byte boundary); base pointers must be 16-byte
- *    aligned.  Transposed operands (inner stride != 1) are rejected.
+ *    to the output type.  mg_gemm, mg_gemm_bias_relu and mg_conv2d also
+ *    take fp32 (MG_F32 in and out, see mg_gemm).
+ *  - Layout: matrices with one unit stride.  Leading strides are in
+ *    elements, must be >= the row length and span 16 bytes a whole number
+ *    of times (a multiple of 8 for 16-bit types, of 4 for fp32), so every
+ *    row starts on a 16-byte boundary; base pointers must be 16-byte
+ *    aligned.  Where a transposed operand is accepted, the entry point says.
  *  - Ownership: the caller owns every buffer.  Outputs must not overlap
  *    inputs.  Buffers must stay valid until the enqueued work has finished.
  *  - Errors: a non-MG_OK status means nothing was enqueued, except
@@ -74,6 +76,13 @@ const char* mg_status_string(mg_status status);
  * transposed operand is supported on the direct-to-LDS kernels only, i.e.
  * when K is a multiple of the chosen row's K slice, N % 8 == 0 and, for a
  * transposed A, M % 8 == 0; otherwise MG_ERR_UNSUPPORTED_LAYOUT.
+ *
+ * fp32 (in_dtype == out_dtype == MG_F32; the 4096^3 fp32 row of the FlagOS
+ * cross-chip page's benchmark table, section 3.4): fp32 inputs on the fp32
+ * matrix cores, fp32 accumulation and output.  Row-major A and B only,
+ * K % 16 == 0 and N % 4 == 0, else MG_ERR_UNSUPPORTED_LAYOUT; leading
+ * strides multiples of 4.  Not available in the batched, split-K, grouped
+ * or prepacked entry points (MG_ERR_UNSUPPORTED_DTYPE there).
  */
 mg_status mg_gemm(const void* A, const void* B, void* C,
                   int64_t M, int64_t N, int64_t K,
@@ -188,6 +197,87 @@ mg_status mg_gemm_prepacked(const void* Ap, int64_t BK, const void* B, void* C,
                             int64_t stride_bk, int64_t stride_bn,
                             int64_t stride_cm, int64_t stride_cn,
                             mg_dtype dtype, hipStream_t stream);
+
+/* ---- GEMM consumers ------------------------------------------------------- */
+
+/*
+ * Shape of a 2-D convolution (cross-correlation with zero padding, as deep-
+ * learning frameworks define it).  Input NHWC [batch, height, width,
+ * in_channels]; output NHWC [batch, OH, OW, out_channels] with
+ *     OH = (height + 2*pad_h - dilation_h*(kernel_h - 1) - 1) / stride_h + 1
+ * (floor) and OW likewise.
+ */
+typedef struct {
+    int64_t batch, height, width, in_channels, out_channels;
+    int64_t kernel_h, kernel_w;
+    int64_t stride_h, stride_w;
+    int64_t pad_h, pad_w;
+    int64_t dilation_h, dilation_w;
+} mg_conv2d_shape;
+
+/* Output height and width of `shape`; MG_ERR_INVALID_ARG for a negative size,
+ * a stride, dilation or kernel extent below 1, or an empty output. */
+mg_status mg_conv2d_output_hw(const mg_conv2d_shape* shape, int64_t* out_h, int64_t* out_w);
+
+/*
+ * im2col (FlagOS cross-chip page, section 5.3: a convolution becomes a GEMM
+ * through im2col): cols is [M = batch*OH*OW, ld_cols] row-major; row
+ * m = (n*OH + oh)*OW + ow holds at column k = (kh*kernel_w + kw)*in_channels
+ * + c the input element x[n, oh*stride_h - pad_h + kh*dilation_h,
+ * ow*stride_w - pad_w + kw*dilation_w, c], or zero where that position is
+ * outside the image.  Columns K = kernel_h*kernel_w*in_channels ..
+ * ld_cols-1 are written as zero.  x: dense NHWC, 16-byte aligned.  ld_cols
+ * >= K and a whole number of 16-byte chunks (else MG_ERR_UNSUPPORTED_LAYOUT
+ * / MG_ERR_MISALIGNED).  Bit copies: any of the three dtypes.  Limits (else
+ * MG_ERR_UNSUPPORTED_LAYOUT): M < 2^31, ld_cols < 2^27, kernel_h*kernel_w
+ * <= 65535, height + 2*pad_h and width + 2*pad_w < 2^30.
+ */
+mg_status mg_im2col(const mg_conv2d_shape* shape, const void* x, void* cols, int64_t ld_cols,
+                    mg_dtype dtype, hipStream_t stream);
+
+/*
+ * Workspace that mg_conv2d needs for `shape`: the im2col matrix
+ * [batch*OH*OW, ld] with ld = K rounded up to whole 16-byte chunks, or 0 for
+ * a 1x1 kernel with unit stride and no padding whose channel rows are whole
+ * 16-byte chunks (the input itself is then the GEMM's A).  0 also for an
+ * invalid shape.
+ */
+size_t mg_conv2d_workspace_bytes(const mg_conv2d_shape* shape, mg_dtype dtype);
+
+/*
+ * 2-D convolution as im2col + GEMM (FlagOS cross-chip page, section 5.3):
+ *     y[n,oh,ow,o] = sum_{kh,kw,c} x[n, ih, iw, c] * w(k = (kh*kernel_w + kw)*in_channels + c, o)
+ * then, when bias is not null, ReLU(y + bias[o]) (the fused epilogue of
+ * mg_gemm_bias_relu).  x: dense NHWC, 16-byte aligned.  w: the K x
+ * out_channels GEMM operand, element (k, o) at w + k*stride_wk +
+ * o*stride_wn: HWIO weights ([kh][kw][c][o], stride_wk = out_channels,
+ * stride_wn = 1) or OHWI weights ([o][kh][kw][c], stride_wk = 1, stride_wn
+ * = K; the transposed-B layout of mg_gemm, 16-bit types only).  y: dense
+ * NHWC; its row length out_channels must span whole 16-byte chunks.
+ * workspace: at least mg_conv2d_workspace_bytes() bytes of device memory,
+ * 16-byte aligned (may be null when that is 0), used by this call's kernels
+ * only until they finish.  The im2col kernel and the GEMM run in order on
+ * `stream`.  Errors as mg_im2col and mg_gemm; a short workspace is
+ * MG_ERR_INVALID_ARG.  batch == 0 or out_channels == 0 does nothing.
+ */
+mg_status mg_conv2d(const mg_conv2d_shape* shape, const void* x, const void* w, int64_t stride_wk,
+                     int64_t stride_wn, const void* bias, void* y, void* workspace, size_t workspace_bytes,
+                     mg_dtype dtype, hipStream_t stream);
+
+/*
+ * Attention scores S_h = Q_h * K_h^T for every head h in one launch (FlagOS
+ * cross-chip page, section 5.3: the QK^T of attention is a GEMM; scaling and
+ * softmax are not part of it).  Q_h: Lq x d rows (row stride stride_qm,
+ * head stride stride_qh), K_h: Lk x d rows (stride_kn, stride_kh), S_h: Lq x
+ * Lk (stride_sm, stride_sh).  The batched GEMM with K_h as a transposed B
+ * operand; fp16 or bf16; d must be a whole number of the chosen tile's K
+ * slices (a multiple of 64 always is) and Lk % 8 == 0, else
+ * MG_ERR_UNSUPPORTED_LAYOUT; strides multiples of 8.
+ */
+mg_status mg_attention_scores(const void* Q, const void* K, void* S, int64_t heads, int64_t Lq, int64_t Lk,
+                              int64_t d, int64_t stride_qh, int64_t stride_qm, int64_t stride_kh,
+                              int64_t stride_kn, int64_t stride_sh, int64_t stride_sm, mg_dtype dtype,
+                              hipStream_t stream);
 
 /* ---- configuration table (offline-tuned; read-only) ---------------------- */
 

@@ -24,7 +24,7 @@ S = ctypes.c_void_p(0)
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(mg_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(mg_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -38,7 +38,7 @@ def test_header_and_exports_agree(L):
     names = declared_functions()
     assert set(names) == set(mg.EXPORTED)
     out = subprocess.run(["nm", "-D", "--defined-only", mg.LIB_PATH], capture_output=True, text=True, check=True)
-    exported = set(re.findall(r"\bT (mg_[a-z_]+)\b", out.stdout))
+    exported = set(re.findall(r"\bT (mg_[a-z0-9_]+)\b", out.stdout))
     for n in names:
         assert n in exported, n
         assert hasattr(L, n)
@@ -231,3 +231,99 @@ def test_table_selection_for_the_workloads(L):
         assert L.mg_set_config(cid) == OK
         assert L.mg_select_config(8192, 8192, 8192, BF16, 0) == cid
     assert L.mg_set_config(-1) == OK
+
+
+# ---- GEMM consumers: convolution, im2col, attention scores -------------------
+def shape(**kw):
+    d = dict(batch=2, height=16, width=16, in_channels=64, out_channels=64, kernel_h=3, kernel_w=3, stride_h=1,
+             stride_w=1, pad_h=1, pad_w=1, dilation_h=1, dilation_w=1)
+    d.update(kw)
+    return mg.Conv2dShape(**d)
+
+
+def test_conv_output_size(L):
+    oh, ow = ctypes.c_int64(), ctypes.c_int64()
+    for kw, want in [(dict(), (16, 16)), (dict(stride_h=2, stride_w=2), (8, 8)), (dict(pad_h=0, pad_w=0), (14, 14)),
+                     (dict(dilation_h=2, pad_w=0), (14, 14)), (dict(kernel_h=7, kernel_w=1, pad_h=3, pad_w=0), (16, 16)),
+                     (dict(height=5, width=6, stride_h=3, stride_w=3, pad_h=0, pad_w=0), (1, 2))]:
+        assert L.mg_conv2d_output_hw(ctypes.byref(shape(**kw)), ctypes.byref(oh), ctypes.byref(ow)) == OK
+        assert (oh.value, ow.value) == want
+    for kw, status in [(dict(kernel_h=0), INVALID), (dict(stride_w=0), INVALID), (dict(dilation_h=0), INVALID),
+                       (dict(pad_h=-1), INVALID), (dict(batch=-1), INVALID), (dict(in_channels=-2), INVALID),
+                       (dict(height=2, pad_h=0), INVALID),  # a 3-tall kernel does not fit a 2-tall image
+                       (dict(height=1 << 30), LAYOUT), (dict(kernel_h=300, kernel_w=300, height=400, width=400), LAYOUT),
+                       (dict(batch=1 << 20, height=4096, width=4096), LAYOUT)]:
+        assert L.mg_conv2d_output_hw(ctypes.byref(shape(**kw)), None, None) == status, kw
+    assert L.mg_conv2d_output_hw(None, None, None) == INVALID
+
+
+def test_conv_workspace_bytes(L):
+    M = 2 * 16 * 16
+    assert L.mg_conv2d_workspace_bytes(ctypes.byref(shape()), F16) == M * 576 * 2
+    assert L.mg_conv2d_workspace_bytes(ctypes.byref(shape()), 2) == M * 576 * 4
+    assert L.mg_conv2d_workspace_bytes(ctypes.byref(shape(in_channels=3)), F16) == M * 32 * 2  # 27 -> 32
+    assert L.mg_conv2d_workspace_bytes(ctypes.byref(shape(in_channels=3)), 2) == M * 28 * 4  # 27 -> 28
+    one = dict(kernel_h=1, kernel_w=1, pad_h=0, pad_w=0)
+    assert L.mg_conv2d_workspace_bytes(ctypes.byref(shape(**one)), F16) == 0  # the input is the GEMM's A
+    assert L.mg_conv2d_workspace_bytes(ctypes.byref(shape(in_channels=12, **one)), F16) == M * 16 * 2
+    assert L.mg_conv2d_workspace_bytes(ctypes.byref(shape(stride_h=2, **one)), F16) == 2 * 8 * 16 * 64 * 2
+    assert L.mg_conv2d_workspace_bytes(ctypes.byref(shape(kernel_h=0)), F16) == 0
+    assert L.mg_conv2d_workspace_bytes(ctypes.byref(shape()), 7) == 0
+
+
+def im2col(L, s=None, x=P, cols=P, ld=576, dt=F16):
+    return L.mg_im2col(ctypes.byref(s or shape()), x, cols, ld, dt, S)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=5), DTYPE), (dict(ld=568), LAYOUT), (dict(ld=580), MISALIGNED), (dict(ld=1 << 27), LAYOUT),
+    (dict(x=None), INVALID), (dict(x=P + 8), MISALIGNED), (dict(cols=None), INVALID), (dict(cols=P + 2), MISALIGNED),
+    (dict(s=shape(kernel_w=0)), INVALID), (dict(s=shape(batch=0), x=None, cols=None), OK),
+    (dict(dt=2, ld=578), MISALIGNED),
+])
+def test_im2col_rejects_bad_arguments(L, kw, status):
+    assert im2col(L, **kw) == status
+
+
+def conv(L, s=None, x=P, w=P, swk=64, swn=1, bias=None, y=P, ws=P, ws_bytes=1 << 30, dt=F16):
+    return L.mg_conv2d(ctypes.byref(s or shape()), x, w, swk, swn, bias, y, ws, ws_bytes, dt, S)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=9), DTYPE), (dict(x=None), INVALID), (dict(x=P + 4), MISALIGNED), (dict(w=None), INVALID),
+    (dict(y=None), INVALID), (dict(ws=None), INVALID), (dict(ws_bytes=2 * 256 * 576 * 2 - 1), INVALID),
+    (dict(ws=P + 8), MISALIGNED), (dict(swk=64, swn=2), LAYOUT), (dict(swk=70, swn=1), MISALIGNED),
+    (dict(s=shape(out_channels=4), swk=4), MISALIGNED),  # NHWC rows of 4 fp16 are not 16-byte rows
+    (dict(s=shape(in_channels=3), swk=1, swn=27), MISALIGNED),  # OHWI rows of 27 fp16
+    (dict(s=shape(in_channels=8), swk=1, swn=72), LAYOUT),  # OHWI needs K in whole slices (72 is not)
+    (dict(dt=2, swk=1, swn=576), LAYOUT),  # fp32 takes HWIO weights only
+    (dict(dt=2, s=shape(in_channels=3)), LAYOUT),  # fp32 K = 27 is not a multiple of 16
+    (dict(s=shape(batch=0), x=None, w=None, y=None, ws=None), OK),
+    (dict(s=shape(out_channels=0), w=None, y=None, ws=None), OK),
+    (dict(s=shape(stride_h=0)), INVALID),
+])
+def test_conv_rejects_bad_arguments(L, kw, status):
+    assert conv(L, **kw) == status
+
+
+def test_conv_1x1_needs_no_workspace_but_validates_the_gemm(L):
+    one = shape(kernel_h=1, kernel_w=1, pad_h=0, pad_w=0)
+    # no workspace is needed, so a null one is fine; the GEMM's checks still apply
+    assert conv(L, s=one, ws=None, ws_bytes=0, y=None) == INVALID
+    assert conv(L, s=one, ws=None, ws_bytes=0, x=P + 8) == MISALIGNED
+
+
+def attn(L, Q=P, K=P, Sx=P, heads=4, Lq=128, Lk=128, d=64, sqh=128 * 64, sqm=64, skh=128 * 64, skn=64,
+         ssh=128 * 128, ssm=128, dt=F16):
+    return L.mg_attention_scores(Q, K, Sx, heads, Lq, Lk, d, sqh, sqm, skh, skn, ssh, ssm, dt, S)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=2), DTYPE), (dict(dt=4), DTYPE), (dict(heads=-1), INVALID), (dict(Q=None), INVALID),
+    (dict(K=None), INVALID), (dict(Sx=None), INVALID), (dict(d=40, sqm=40, skn=40), LAYOUT),
+    (dict(Lk=60, ssm=64), LAYOUT), (dict(sqm=72, sqh=128 * 72 + 4), MISALIGNED), (dict(skn=66), MISALIGNED),
+    (dict(ssh=100 * 128), LAYOUT),  # score entries of different heads would overlap
+    (dict(heads=0, Q=None, K=None, Sx=None), OK), (dict(Lq=0), OK),
+])
+def test_attention_scores_rejects_bad_arguments(L, kw, status):
+    assert attn(L, **kw) == status

@@ -1,0 +1,255 @@
+"""GPU parity of the GEMM consumers (im2col, convolution as im2col + GEMM,
+attention scores Q K^T) through the C ABI, against the CPU oracle.
+
+Gates as for the GEMM: bit-exact on integer inputs; |got - ref| <= 1e-2 +
+1e-2 |ref| for random 16-bit inputs; for fp32, twice the fp32 accumulation
+bound K 2^-24 sum|x||w| + 2^-24 |ref|.  im2col is pure data movement and is
+bit-exact on every input.  Outputs sit between canary-filled guard bands.
+The timed workloads (a 56x56x64 -> 64 3x3 convolution at batch 32, and
+128 heads x 2048 x 2048 scores with d = 128) are checked on a seeded
+4096-element sample plus edges.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import tiled_matrix_multiplication_gemm_amd as mg
+from oracle import compare, layout
+from tiled_matrix_multiplication_gemm_amd import inputs
+from tests.gpu_util import F16, BF16, CANARY, announce, assert_bitexact, assert_tolerance, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+F32 = 2
+GUARD = 4096
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    mg.lib()
+
+
+def dev(bits, dtype):
+    import torch
+
+    if dtype == F32:
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.float32)).cuda()
+    return to_dev(bits, dtype)
+
+
+def host(t, dtype):
+    import torch
+
+    if dtype == F32:
+        return t.contiguous().cpu().numpy().view(np.uint32)
+    return to_host(t)
+
+
+def guarded(shape, dtype):
+    """(buffer, view): a tensor of `shape` between canary guard bands."""
+    import torch
+
+    n = int(np.prod(shape))
+    if dtype == F32:
+        buf = torch.full((GUARD + n + GUARD,), float("nan"), device="cuda")
+        return buf, buf[GUARD:GUARD + n].view(*shape)
+    buf = torch.full((GUARD + n + GUARD,), CANARY, dtype=torch.int16, device="cuda")
+    t = buf.view(torch.float16 if dtype == F16 else torch.bfloat16)
+    return buf, t[GUARD:GUARD + n].view(*shape)
+
+
+def guards_intact(buf, dtype):
+    h = buf.cpu().numpy()
+    if dtype == F32:
+        return bool(np.isnan(h[:GUARD]).all() and np.isnan(h[-GUARD:]).all())
+    return bool((h[:GUARD].view(np.uint16) == CANARY).all() and (h[-GUARD:].view(np.uint16) == CANARY).all())
+
+
+def check(got, ref, ref_q, dtype, integer, label, absref=None, K=None):
+    if integer:
+        if dtype == F32:
+            bad = np.flatnonzero((got != ref_q) & ~(((got & 0x7FFFFFFF) == 0) & ((ref_q & 0x7FFFFFFF) == 0)))
+            assert bad.size == 0, "%s: %d bit mismatches" % (label, bad.size)
+        else:
+            assert_bitexact(got, ref_q, dtype, label)
+    elif dtype == F32:
+        g = got.view(np.float32).astype(np.float64)
+        tol = 2.0 * (K * 2.0 ** -24 * absref + 2.0 ** -24 * np.abs(ref)) + 1e-30
+        assert np.all(np.isfinite(g)) and np.all(np.abs(g - ref) <= tol), label
+    else:
+        assert_tolerance(got, ref, dtype, label)
+
+
+# ---- im2col ------------------------------------------------------------------
+IM2COL_CASES = [
+    # (Nb, H, W, C, KH, KW, stride, pad, dil, dtype, extra ld)
+    (2, 9, 11, 64, 3, 3, (1, 1), (1, 1), (1, 1), F16, 0),   # one tap per launch column
+    (1, 10, 7, 16, 3, 2, (2, 1), (2, 0), (1, 2), BF16, 0),
+    (2, 8, 8, 8, 1, 1, (2, 2), (0, 0), (1, 1), F16, 0),
+    (1, 13, 13, 3, 7, 7, (2, 2), (3, 3), (1, 1), F16, 0),   # C = 3: element path, ld 147 -> 152
+    (1, 6, 5, 12, 3, 3, (1, 1), (1, 1), (1, 1), F16, 16),   # C % 8 != 0, wider ld
+    (2, 7, 7, 64, 3, 3, (1, 1), (0, 0), (1, 1), F16, 8),    # C % 8 == 0 but ld > K: element path
+    (1, 9, 9, 8, 3, 3, (1, 1), (1, 1), (2, 2), F32, 0),
+    (1, 5, 6, 6, 2, 2, (1, 1), (1, 1), (1, 1), F32, 4),
+]
+
+
+@pytest.mark.parametrize("case", IM2COL_CASES)
+def test_im2col_bit_exact(case):
+    import torch
+
+    Nb, H, W, C, KH, KW, stride, pad, dil, dt, extra = case
+    announce("im2col %s" % (case,))
+    c = inputs.conv_case(Nb, H, W, C, 1, KH, KW, dt, seed=31, stride=stride, pad=pad, dil=dil)
+    want = layout.im2col(c.x, KH, KW, stride, pad, dil)
+    M, K = want.shape
+    v = 16 // (4 if dt == F32 else 2)
+    ld = (K + v - 1) // v * v + extra
+    buf, out = guarded((M, ld), dt)
+    mg.mg_im2col(dev(c.x, dt), (KH, KW), stride, pad, dil, ld=ld, out=out)
+    torch.cuda.synchronize()
+    got = host(out, dt)
+    assert guards_intact(buf, dt)
+    assert np.array_equal(got[:, :K], want)
+    assert np.all(got[:, K:] == 0)
+
+
+# ---- convolution -----------------------------------------------------------------
+CONV_CASES = [
+    # (Nb, H, W, C, OC, KH, KW, stride, pad, dil, dtype, weights)
+    (2, 17, 17, 64, 64, 3, 3, (1, 1), (1, 1), (1, 1), F16, "hwio"),     # K = 576: direct GEMM rows
+    (1, 20, 18, 32, 128, 3, 3, (2, 2), (1, 1), (1, 1), BF16, "hwio"),
+    (2, 15, 15, 3, 64, 7, 7, (2, 2), (3, 3), (1, 1), F16, "hwio"),      # K = 147: general GEMM row
+    (2, 9, 9, 64, 32, 1, 1, (1, 1), (0, 0), (1, 1), F16, "hwio"),       # 1x1: the input is A
+    (1, 12, 12, 16, 32, 1, 1, (2, 2), (0, 0), (1, 1), BF16, "hwio"),    # 1x1 stride 2: im2col
+    (1, 14, 13, 16, 16, 3, 3, (1, 1), (2, 2), (2, 2), F16, "hwio"),     # dilation
+    (2, 10, 10, 64, 64, 3, 3, (1, 1), (1, 1), (1, 1), F16, "ohwi"),     # transposed weights
+    (1, 12, 12, 16, 32, 3, 3, (1, 1), (1, 1), (1, 1), F32, "hwio"),     # fp32, K = 144
+]
+
+
+def run_conv(c, OC, weights, bias=None):
+    import torch
+
+    dt = c.dtype
+    KH, KW, C, _ = c.w.shape
+    w = c.w if weights == "hwio" else np.ascontiguousarray(c.w.transpose(3, 0, 1, 2))
+    oh, ow = oracle.conv_out_hw(c.x.shape[1], c.x.shape[2], KH, KW, c.stride, c.pad, c.dil)
+    buf, out = guarded((c.x.shape[0], oh, ow, OC), dt)
+    mg.mg_conv2d(dev(c.x, dt), dev(w, dt), c.stride, c.pad, c.dil,
+                 bias=None if bias is None else dev(bias, dt), weight_layout=weights, out=out)
+    torch.cuda.synchronize()
+    return host(out, dt), guards_intact(buf, dt)
+
+
+@pytest.mark.parametrize("case", CONV_CASES)
+def test_conv2d(case):
+    Nb, H, W, C, OC, KH, KW, stride, pad, dil, dt, weights = case
+    for integer in (True, False):
+        for with_bias in (False, True):
+            label = "conv %s int=%s bias=%s" % (case, integer, with_bias)
+            announce(label)
+            c = inputs.conv_case(Nb, H, W, C, OC, KH, KW, dt, seed=41 + integer, stride=stride, pad=pad, dil=dil,
+                                 integer=integer, bias=with_bias)
+            got, guards = run_conv(c, OC, weights, c.bias)
+            assert guards, label + ": write outside the output"
+            ref, ref_q = oracle.conv2d(c.x, c.w, dt, stride, pad, dil, bias=c.bias, relu=with_bias)
+            absref = None
+            if dt == F32 and not integer:
+                xa = np.abs(oracle.decode32(c.x)).astype(np.float32).view(np.uint32)
+                wa = np.abs(oracle.decode32(c.w)).astype(np.float32).view(np.uint32)
+                absref, _ = oracle.conv2d(xa, wa, F32, stride, pad, dil)
+            check(got, ref, ref_q, dt, integer, label, absref, KH * KW * C)
+
+
+def test_conv2d_repeat_is_deterministic():
+    c = inputs.conv_case(2, 17, 17, 64, 64, 3, 3, F16, seed=43, pad=(1, 1))
+    a, _ = run_conv(c, 64, "hwio")
+    b, _ = run_conv(c, 64, "hwio")
+    assert np.array_equal(a, b)
+
+
+def test_conv2d_workload_sampled():
+    """The timed convolution (batch 32, 56x56, 64 -> 64, 3x3, pad 1, fp16) on
+    its integer and float inputs: 4096 seeded samples plus row/column edges."""
+    w = inputs.CONV_WORKLOAD
+    for variant in ("int", "float"):
+        integer = variant == "int"
+        c = inputs.conv_case(w["Nb"], w["H"], w["W"], w["C"], w["OC"], w["KH"], w["KW"], w["dtype"],
+                             w["seed_int"] if integer else w["seed_float"], w["stride"], w["pad"], w["dil"],
+                             integer=integer)
+        announce("conv workload %s" % variant)
+        got, guards = run_conv(c, w["OC"], "hwio")
+        assert guards
+        M = got.shape[0] * got.shape[1] * got.shape[2]
+        rows, cols = compare.sample_positions(M, w["OC"], 4096, 308)
+        er, ec = compare.edge_positions(M, w["OC"], tile=256)
+        rows, cols = np.concatenate([rows, er]), np.concatenate([cols, ec])
+        ref, ref_q = oracle.conv2d(c.x, c.w, w["dtype"], w["stride"], w["pad"], w["dil"], rows=rows, cols=cols)
+        check(got.reshape(M, w["OC"])[rows, cols], ref, ref_q, w["dtype"], integer, "conv workload " + variant)
+
+
+# ---- attention scores ------------------------------------------------------------
+ATTN_CASES = [
+    (6, 130, 200, 64, F16),
+    (4, 256, 256, 128, BF16),
+    (2, 1, 8, 64, F16),
+    (3, 77, 64, 192, BF16),
+]
+
+
+def run_attention(a, packed=False):
+    import torch
+
+    dt = a.dtype
+    H, Lq, d = a.Q.shape
+    Lk = a.K.shape[1]
+    if packed:
+        # q and k as column slices of one fused [heads, L, 3d] projection output
+        qkv = np.zeros((H, max(Lq, Lk), 3 * d), dtype=np.uint16)
+        qkv[:, :Lq, :d] = a.Q
+        qkv[:, :Lk, d:2 * d] = a.K
+        t = dev(qkv, dt)
+        q, k = t[:, :Lq, :d], t[:, :Lk, d:2 * d]
+    else:
+        q, k = dev(a.Q, dt), dev(a.K, dt)
+    buf, out = guarded((H, Lq, Lk), dt)
+    mg.mg_attention_scores(q, k, out=out)
+    torch.cuda.synchronize()
+    return host(out, dt), guards_intact(buf, dt)
+
+
+@pytest.mark.parametrize("case", ATTN_CASES)
+def test_attention_scores(case):
+    H, Lq, Lk, d, dt = case
+    for integer in (True, False):
+        for packed in (False, True):
+            label = "attention %s int=%s packed=%s" % (case, integer, packed)
+            announce(label)
+            a = inputs.attention_case(H, Lq, Lk, d, dt, seed=51 + integer, integer=integer)
+            got, guards = run_attention(a, packed)
+            assert guards, label + ": write outside the output"
+            ref, ref_q = oracle.attention_scores(a.Q, a.K, dt)
+            check(got, ref, ref_q, dt, integer, label)
+
+
+def test_attention_workload_sampled():
+    """The timed scores (128 heads, 2048 x 2048, d = 128, bf16): 4096 seeded
+    samples plus the edges of every head's tile grid."""
+    w = inputs.ATTENTION_WORKLOAD
+    H, L, d, dt = w["heads"], w["L"], w["d"], w["dtype"]
+    for variant in ("int", "float"):
+        integer = variant == "int"
+        a = inputs.attention_case(H, L, L, d, dt, w["seed_int"] if integer else w["seed_float"], integer=integer)
+        announce("attention workload %s" % variant)
+        got, guards = run_attention(a)
+        assert guards
+        rows, cols = compare.sample_positions(H * L, L, 4096, 309)
+        er, ec = compare.edge_positions(H * L, L, tile=256)
+        rows, cols = np.concatenate([rows, er]), np.concatenate([cols, ec])
+        heads, rows_h = rows // L, rows % L
+        ref, ref_q = oracle.attention_scores_sampled(a.Q, a.K, dt, heads, rows_h, cols)
+        check(got.reshape(H * L, L)[rows, cols], ref, ref_q, dt, integer, "attention workload " + variant)

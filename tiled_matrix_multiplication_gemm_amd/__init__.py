@@ -42,8 +42,16 @@ EXPORTED = (
     "mg_status_string", "mg_gemm", "mg_gemm_bias_relu", "mg_gemm_batched", "mg_gemm_splitk",
     "mg_splitk_workspace_bytes", "mg_splitk_choose", "mg_grouped_gemm", "mg_prepacked_bytes",
     "mg_prepack_a", "mg_config_bk", "mg_gemm_prepacked", "mg_num_configs", "mg_config_info",
-    "mg_set_config", "mg_last_config", "mg_select_config",
+    "mg_set_config", "mg_last_config", "mg_select_config", "mg_conv2d_output_hw", "mg_im2col",
+    "mg_conv2d_workspace_bytes", "mg_conv2d", "mg_attention_scores",
 )
+
+
+class Conv2dShape(ctypes.Structure):
+    """mg_conv2d_shape of the C ABI."""
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "batch", "height", "width", "in_channels", "out_channels", "kernel_h", "kernel_w", "stride_h", "stride_w",
+        "pad_h", "pad_w", "dilation_h", "dilation_w")]
 
 
 def lib() -> ctypes.CDLL:
@@ -94,6 +102,17 @@ def lib() -> ctypes.CDLL:
         L.mg_last_config.argtypes = []
         L.mg_select_config.restype = cint
         L.mg_select_config.argtypes = [i64, i64, i64, cint, cint]
+        shp = ctypes.POINTER(Conv2dShape)
+        L.mg_conv2d_output_hw.restype = cint
+        L.mg_conv2d_output_hw.argtypes = [shp, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+        L.mg_im2col.restype = cint
+        L.mg_im2col.argtypes = [shp, vp, vp, i64, cint, vp]
+        L.mg_conv2d_workspace_bytes.restype = ctypes.c_size_t
+        L.mg_conv2d_workspace_bytes.argtypes = [shp, cint]
+        L.mg_conv2d.restype = cint
+        L.mg_conv2d.argtypes = [shp, vp, vp, i64, i64, vp, vp, vp, ctypes.c_size_t, cint, vp]
+        L.mg_attention_scores.restype = cint
+        L.mg_attention_scores.argtypes = [vp, vp, vp] + [i64] * 10 + [cint, vp]
         _lib = L
         return L
 
@@ -306,6 +325,118 @@ def mg_select_config(M: int, N: int, K: int, dtype: int = MG_F16, grouped: bool 
     return int(lib().mg_select_config(M, N, K, dtype, int(bool(grouped))))
 
 
+# ---- GEMM consumers --------------------------------------------------------
+def _pair(v):
+    return (int(v), int(v)) if isinstance(v, int) else (int(v[0]), int(v[1]))
+
+
+def conv2d_shape(x_shape, kernel, out_channels: int, stride=1, pad=0, dil=1) -> Conv2dShape:
+    """The C ABI's convolution shape for an NHWC input of shape x_shape."""
+    Nb, H, W, C = (int(v) for v in x_shape)
+    (kh, kw), (sh, sw), (ph, pw), (dh, dw) = _pair(kernel), _pair(stride), _pair(pad), _pair(dil)
+    return Conv2dShape(Nb, H, W, C, int(out_channels), kh, kw, sh, sw, ph, pw, dh, dw)
+
+
+def mg_conv2d_output_hw(shape: Conv2dShape):
+    oh, ow = ctypes.c_int64(0), ctypes.c_int64(0)
+    _check(lib().mg_conv2d_output_hw(ctypes.byref(shape), ctypes.byref(oh), ctypes.byref(ow)))
+    return oh.value, ow.value
+
+
+def mg_conv2d_workspace_bytes(shape: Conv2dShape, dtype: int = MG_F16) -> int:
+    return int(lib().mg_conv2d_workspace_bytes(ctypes.byref(shape), dtype))
+
+
+def mg_im2col(x, kernel, stride=1, pad=0, dil=1, ld: int | None = None, out=None):
+    """cols[Nb*OH*OW, ld] of an NHWC tensor x (zero where a tap falls outside
+    the image; columns past KH*KW*C zero).  ld defaults to KH*KW*C rounded up
+    to whole 16-byte chunks."""
+    import torch
+
+    _require_gpu(x)
+    if x.dim() != 4 or not x.is_contiguous():
+        raise RuntimeError("MG_ERR_UNSUPPORTED_LAYOUT: a contiguous NHWC tensor expected")
+    shape = conv2d_shape(x.shape, kernel, 0, stride, pad, dil)
+    oh, ow = mg_conv2d_output_hw(shape)
+    K = shape.kernel_h * shape.kernel_w * shape.in_channels
+    v = 16 // x.element_size()
+    if ld is None:
+        ld = (K + v - 1) // v * v
+    M = shape.batch * oh * ow
+    if out is None:
+        out = torch.empty((M, ld), dtype=x.dtype, device=x.device)
+    if out.shape != (M, ld) or not out.is_contiguous():
+        raise RuntimeError("MG_ERR_INVALID_ARG: out must be a contiguous [%d, %d] tensor" % (M, ld))
+    _check(lib().mg_im2col(ctypes.byref(shape), x.data_ptr(), out.data_ptr(), ld, _dtype_code(x), _stream(x)))
+    return out
+
+
+def mg_conv2d(x, w, stride=1, pad=0, dil=1, bias=None, weight_layout: str = "hwio", workspace=None, out=None):
+    """y = conv2d(x, w) as im2col + GEMM (then ReLU(y + bias) when bias is given).
+
+    x: contiguous NHWC [Nb,H,W,C]; w: contiguous [KH,KW,C,OC] ("hwio") or
+    [OC,KH,KW,C] ("ohwi"); returns NHWC [Nb,OH,OW,OC].  workspace: a device
+    tensor of at least mg_conv2d_workspace_bytes() bytes, allocated here
+    through torch when not given."""
+    import torch
+
+    _require_gpu(x, w)
+    if x.dim() != 4 or w.dim() != 4 or not x.is_contiguous() or not w.is_contiguous():
+        raise RuntimeError("MG_ERR_UNSUPPORTED_LAYOUT: contiguous NHWC x and 4-D weights expected")
+    if weight_layout == "hwio":
+        KH, KW, C, OC = w.shape
+    elif weight_layout == "ohwi":
+        OC, KH, KW, C = w.shape
+    else:
+        raise RuntimeError("MG_ERR_INVALID_ARG: weight_layout must be 'hwio' or 'ohwi'")
+    if C != x.shape[3] or w.dtype != x.dtype:
+        raise RuntimeError("MG_ERR_INVALID_ARG: channel count or dtype of w does not match x")
+    shape = conv2d_shape(x.shape, (KH, KW), OC, stride, pad, dil)
+    oh, ow = mg_conv2d_output_hw(shape)
+    K = KH * KW * C
+    swk, swn = (OC, 1) if weight_layout == "hwio" else (1, K)
+    if bias is not None:
+        _require_gpu(bias)
+        if bias.shape != (OC,) or bias.dtype != x.dtype or (OC > 1 and bias.stride(0) != 1):
+            raise RuntimeError("MG_ERR_INVALID_ARG: contiguous bias[OC] of x's dtype expected")
+    if out is None:
+        out = torch.empty((shape.batch, oh, ow, OC), dtype=x.dtype, device=x.device)
+    if tuple(out.shape) != (shape.batch, oh, ow, OC) or not out.is_contiguous():
+        raise RuntimeError("MG_ERR_INVALID_ARG: out must be a contiguous [%d, %d, %d, %d] tensor"
+                           % (shape.batch, oh, ow, OC))
+    need = mg_conv2d_workspace_bytes(shape, _dtype_code(x))
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=x.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().mg_conv2d(ctypes.byref(shape), x.data_ptr(), w.data_ptr(), swk, swn,
+                           bias.data_ptr() if bias is not None else None, out.data_ptr(), ws_ptr, ws_bytes,
+                           _dtype_code(x), _stream(x)))
+    return out
+
+
+def mg_attention_scores(q, k, out=None):
+    """out[h] = q[h] @ k[h]^T for every head h in one launch.
+
+    q: [heads, Lq, d], k: [heads, Lk, d] with unit stride along d (fp16/bf16);
+    returns [heads, Lq, Lk]."""
+    import torch
+
+    _require_gpu(q, k)
+    if q.dim() != 3 or k.dim() != 3 or q.shape[0] != k.shape[0] or q.shape[2] != k.shape[2]:
+        raise RuntimeError("MG_ERR_INVALID_ARG: q[heads,Lq,d] and k[heads,Lk,d] expected")
+    H, Lq, d = q.shape
+    Lk = k.shape[1]
+    if (d > 1 and (q.stride(2) != 1 or k.stride(2) != 1)) or k.dtype != q.dtype:
+        raise RuntimeError("MG_ERR_UNSUPPORTED_LAYOUT: unit stride along d and one dtype required")
+    if out is None:
+        out = torch.empty((H, Lq, Lk), dtype=q.dtype, device=q.device)
+    _check(lib().mg_attention_scores(q.data_ptr(), k.data_ptr(), out.data_ptr(), H, Lq, Lk, d, q.stride(0),
+                                     q.stride(1), k.stride(0), k.stride(1), out.stride(0), out.stride(1),
+                                     _dtype_code(q), _stream(q)))
+    return out
+
+
 # short names
 gemm = mg_gemm
 gemm_bias_relu = mg_gemm_bias_relu
@@ -314,3 +445,6 @@ gemm_splitk = mg_gemm_splitk
 grouped_gemm = mg_grouped_gemm
 prepack_a = mg_prepack_a
 gemm_prepacked = mg_gemm_prepacked
+conv2d = mg_conv2d
+im2col = mg_im2col
+attention_scores = mg_attention_scores

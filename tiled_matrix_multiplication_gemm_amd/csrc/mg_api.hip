@@ -8,6 +8,7 @@
 #include <stdint.h>
 
 #include "mi355gemm.h"
+#include "mg_im2col.h"
 #include "mg_table.h"
 
 namespace {
@@ -151,7 +152,7 @@ mg_status launch(int cfg, int dt, bool epi, int mode, KArgs& a, hipStream_t s, i
         case 7: st = launch_row7(dt, epi, mode, ta, tb, a, grid, s); break;
         default: return MG_ERR_BAD_CONFIG;
     }
-    if (st == MG_OK) g_last.store(cfg);
+    if (st == MG_OK && !a.dry) g_last.store(cfg);
     return st;
 }
 
@@ -172,7 +173,7 @@ int f32_tile(int64_t M, int64_t N) {
 // which needs K in whole 16-element slices, N % 4 == 0 and 16-byte rows.
 mg_status gemm_f32(const void* A, const void* B, const void* bias, void* C, int64_t M, int64_t N, int64_t K,
                    int64_t sam, int64_t sak, int64_t sbk, int64_t sbn, int64_t scm, int64_t scn, mg_dtype in_dtype,
-                   mg_dtype out_dtype, bool epi, hipStream_t stream) {
+                   mg_dtype out_dtype, bool epi, hipStream_t stream, bool dry = false) {
     if (in_dtype != MG_F32 || out_dtype != MG_F32) return MG_ERR_UNSUPPORTED_DTYPE;
     if (!(sak == 1 || K <= 1) || !(sbn == 1 || N <= 1)) return MG_ERR_UNSUPPORTED_LAYOUT;
     MG_TRY(check_matrix(A, M, K, sam, sak, 4));
@@ -199,17 +200,18 @@ mg_status gemm_f32(const void* A, const void* B, const void* bias, void* C, int6
     a.batch = 1;
     const int64_t grid = (int64_t)a.tiles_m * a.tiles_n;
     if (grid > 0x7fffffff) return MG_ERR_INVALID_ARG;
+    if (dry) return MG_OK;
     return launch_f32(tile, epi, a, grid, stream);
 }
 
 mg_status gemm_common(const void* A, const void* B, const void* bias, void* C, int64_t M, int64_t N, int64_t K,
                       int64_t sam, int64_t sak, int64_t sbk, int64_t sbn, int64_t scm, int64_t scn,
                       mg_dtype in_dtype, mg_dtype out_dtype, bool epi, hipStream_t stream, int64_t batch = 1,
-                      int64_t sab = 0, int64_t sbb = 0, int64_t scb = 0) {
+                      int64_t sab = 0, int64_t sbb = 0, int64_t scb = 0, bool dry = false) {
     if (M < 0 || N < 0 || K < 0 || batch < 0) return MG_ERR_INVALID_ARG;
     if (in_dtype == MG_F32 || out_dtype == MG_F32) {
         if (batch != 1) return MG_ERR_UNSUPPORTED_DTYPE;
-        return gemm_f32(A, B, bias, C, M, N, K, sam, sak, sbk, sbn, scm, scn, in_dtype, out_dtype, epi, stream);
+        return gemm_f32(A, B, bias, C, M, N, K, sam, sak, sbk, sbn, scm, scn, in_dtype, out_dtype, epi, stream, dry);
     }
     if (batch == 0) return check_dtype(in_dtype, out_dtype);  // no entries: pointers never used
     if (batch > 1) {
@@ -245,7 +247,96 @@ mg_status gemm_common(const void* A, const void* B, const void* bias, void* C, i
     a.batch = (int32_t)(batch > 1 ? batch : 1);
     if (batch > 0x7fffffff) return MG_ERR_INVALID_ARG;
     a.sab = sab; a.sbb = sbb; a.scb = scb;
+    a.dry = dry ? 1 : 0;
     return launch(cfg, (int)in_dtype, epi, MODE_DENSE, a, stream, ta, tb);
+}
+
+// ---- convolution geometry and im2col -----------------------------------------
+struct ConvGeom {
+    int64_t OH, OW, M, K, taps;
+};
+
+int elem_bytes(mg_dtype dt) { return dt == MG_F16 || dt == MG_BF16 ? 2 : (dt == MG_F32 ? 4 : 0); }
+
+// Checks the shape and derives the output size; the limits keep every index
+// of the im2col kernels (32-bit row and column decodes) in range.
+mg_status conv_geom(const mg_conv2d_shape* s, ConvGeom& g) {
+    if (s == nullptr) return MG_ERR_INVALID_ARG;
+    if (s->batch < 0 || s->height < 0 || s->width < 0 || s->in_channels < 0 || s->out_channels < 0)
+        return MG_ERR_INVALID_ARG;
+    if (s->kernel_h < 1 || s->kernel_w < 1 || s->stride_h < 1 || s->stride_w < 1 || s->dilation_h < 1 ||
+        s->dilation_w < 1 || s->pad_h < 0 || s->pad_w < 0)
+        return MG_ERR_INVALID_ARG;
+    const int64_t lim30 = (int64_t)1 << 30;
+    if (s->height >= lim30 || s->width >= lim30 || s->pad_h >= lim30 || s->pad_w >= lim30 ||
+        s->kernel_h >= lim30 || s->kernel_w >= lim30 || s->dilation_h >= lim30 || s->dilation_w >= lim30 ||
+        s->stride_h >= lim30 || s->stride_w >= lim30 || s->height + 2 * s->pad_h >= lim30 ||
+        s->width + 2 * s->pad_w >= lim30)
+        return MG_ERR_UNSUPPORTED_LAYOUT;
+    const int64_t eh = s->height + 2 * s->pad_h - s->dilation_h * (s->kernel_h - 1) - 1;
+    const int64_t ew = s->width + 2 * s->pad_w - s->dilation_w * (s->kernel_w - 1) - 1;
+    if (eh < 0 || ew < 0) return MG_ERR_INVALID_ARG;  // the kernel does not fit: empty output
+    g.OH = eh / s->stride_h + 1;
+    g.OW = ew / s->stride_w + 1;
+    const int64_t lim31 = ((int64_t)1 << 31) - 1;
+    const int64_t ohw = g.OH * g.OW;  // both < 2^30
+    if (ohw > lim31 || (s->batch > 0 && ohw > lim31 / s->batch)) return MG_ERR_UNSUPPORTED_LAYOUT;
+    g.M = s->batch * ohw;
+    if (s->kernel_h * s->kernel_w > 65535) return MG_ERR_UNSUPPORTED_LAYOUT;
+    g.taps = s->kernel_h * s->kernel_w;
+    if (s->in_channels >= ((int64_t)1 << 27) / g.taps) return MG_ERR_UNSUPPORTED_LAYOUT;
+    g.K = g.taps * s->in_channels;
+    return MG_OK;
+}
+
+int64_t im2col_ld(int64_t K, int es) {
+    const int64_t v = 16 / es;
+    return (K + v - 1) / v * v;
+}
+
+// The input itself is the GEMM's A for a 1x1 kernel with unit stride and no
+// padding, when its channel rows span whole 16-byte chunks.
+bool conv_zero_copy(const mg_conv2d_shape* s, int es) {
+    return s->kernel_h == 1 && s->kernel_w == 1 && s->stride_h == 1 && s->stride_w == 1 && s->pad_h == 0 &&
+           s->pad_w == 0 && (s->in_channels * es) % 16 == 0;
+}
+
+// Validated arguments; enqueues the im2col kernel.
+mg_status launch_im2col(const mg_conv2d_shape* s, const ConvGeom& g, const void* x, void* cols, int64_t ld, int es,
+                        hipStream_t stream) {
+    if (g.M == 0 || ld == 0) return MG_OK;
+    Im2colArgs a{};
+    a.x = (const char*)x;
+    a.cols = (char*)cols;
+    a.H = s->height; a.W = s->width; a.C = s->in_channels;
+    a.M = g.M; a.K = g.K; a.ld = ld;
+    a.KH = (int32_t)s->kernel_h; a.KW = (int32_t)s->kernel_w;
+    a.sh = (int32_t)s->stride_h; a.sw = (int32_t)s->stride_w;
+    a.ph = (int32_t)s->pad_h; a.pw = (int32_t)s->pad_w;
+    a.dh = (int32_t)s->dilation_h; a.dw = (int32_t)s->dilation_w;
+    a.OH = (int32_t)g.OH; a.OW = (int32_t)g.OW;
+    const int64_t v = 16 / es;
+    const bool tap = g.K > 0 && ld == g.K && s->in_channels % v == 0;
+    const int64_t per_row = tap ? s->in_channels / v : ld / v;  // 16-byte chunks per row of one launch
+    int64_t rows = 2048 / per_row;
+    rows = rows < 1 ? 1 : (rows > kIm2colMaxRows ? kIm2colMaxRows : rows);
+    a.rows_per_block = (int32_t)rows;
+    const dim3 grid((unsigned)cdiv(g.M, rows), tap ? (unsigned)g.taps : 1u);
+    (void)hipGetLastError();
+    if (tap) {
+        if (es == 2) hipLaunchKernelGGL(im2col_tap_kernel<2>, grid, dim3(kIm2colThreads), 0, stream, a);
+        else hipLaunchKernelGGL(im2col_tap_kernel<4>, grid, dim3(kIm2colThreads), 0, stream, a);
+    } else {
+        if (es == 2) hipLaunchKernelGGL(im2col_elem_kernel<2>, grid, dim3(kIm2colThreads), 0, stream, a);
+        else hipLaunchKernelGGL(im2col_elem_kernel<4>, grid, dim3(kIm2colThreads), 0, stream, a);
+    }
+    return hipGetLastError() == hipSuccess ? MG_OK : MG_ERR_HIP;
+}
+
+mg_status check_image(const mg_conv2d_shape* s, const void* x) {
+    if (s->batch * s->height * s->width * s->in_channels == 0) return MG_OK;  // no extent
+    if (x == nullptr) return MG_ERR_INVALID_ARG;
+    return aligned16(x) ? MG_OK : MG_ERR_MISALIGNED;
 }
 
 }  // namespace
@@ -464,6 +555,72 @@ int mg_last_config(void) { return g_last.load(); }
 int mg_select_config(int64_t M, int64_t N, int64_t K, mg_dtype dtype, int grouped) {
     (void)dtype;
     return select_config(M, N, K, grouped);
+}
+
+mg_status mg_conv2d_output_hw(const mg_conv2d_shape* shape, int64_t* out_h, int64_t* out_w) {
+    ConvGeom g{};
+    MG_TRY(conv_geom(shape, g));
+    if (out_h) *out_h = g.OH;
+    if (out_w) *out_w = g.OW;
+    return MG_OK;
+}
+
+mg_status mg_im2col(const mg_conv2d_shape* shape, const void* x, void* cols, int64_t ld_cols, mg_dtype dtype,
+                    hipStream_t stream) {
+    ConvGeom g{};
+    MG_TRY(conv_geom(shape, g));
+    const int es = elem_bytes(dtype);
+    if (es == 0) return MG_ERR_UNSUPPORTED_DTYPE;
+    if (ld_cols < g.K || ld_cols >= ((int64_t)1 << 27)) return MG_ERR_UNSUPPORTED_LAYOUT;
+    if ((ld_cols * es) % 16 != 0) return MG_ERR_MISALIGNED;
+    MG_TRY(check_image(shape, x));
+    if (g.M == 0 || ld_cols == 0) return MG_OK;
+    if (cols == nullptr) return MG_ERR_INVALID_ARG;
+    if (!aligned16(cols)) return MG_ERR_MISALIGNED;
+    return launch_im2col(shape, g, x, cols, ld_cols, es, stream);
+}
+
+size_t mg_conv2d_workspace_bytes(const mg_conv2d_shape* shape, mg_dtype dtype) {
+    ConvGeom g{};
+    const int es = elem_bytes(dtype);
+    if (es == 0 || conv_geom(shape, g) != MG_OK || conv_zero_copy(shape, es)) return 0;
+    return (size_t)(g.M * im2col_ld(g.K, es) * es);
+}
+
+mg_status mg_conv2d(const mg_conv2d_shape* shape, const void* x, const void* w, int64_t stride_wk, int64_t stride_wn,
+                    const void* bias, void* y, void* workspace, size_t workspace_bytes, mg_dtype dtype,
+                    hipStream_t stream) {
+    ConvGeom g{};
+    MG_TRY(conv_geom(shape, g));
+    const int es = elem_bytes(dtype);
+    if (es == 0) return MG_ERR_UNSUPPORTED_DTYPE;
+    MG_TRY(check_image(shape, x));
+    if (g.M == 0 || shape->out_channels == 0) return MG_OK;
+    const bool direct = conv_zero_copy(shape, es);
+    const int64_t ld = direct ? shape->in_channels : im2col_ld(g.K, es);
+    const void* A = direct ? x : workspace;
+    if (!direct && g.K > 0) {
+        if (workspace == nullptr || workspace_bytes < (size_t)(g.M * ld * es)) return MG_ERR_INVALID_ARG;
+        if (!aligned16(workspace)) return MG_ERR_MISALIGNED;
+    }
+    const int64_t N = shape->out_channels;
+    // The GEMM y[M, OC] = cols[M, K] * w[K, OC] (+ bias, ReLU), validated in
+    // full before anything is enqueued.
+    MG_TRY(gemm_common(A, w, bias, y, g.M, N, g.K, ld, 1, stride_wk, stride_wn, N, 1, dtype, dtype,
+                       bias != nullptr, stream, 1, 0, 0, 0, /*dry=*/true));
+    if (!direct && g.K > 0) MG_TRY(launch_im2col(shape, g, x, workspace, ld, es, stream));
+    return gemm_common(A, w, bias, y, g.M, N, g.K, ld, 1, stride_wk, stride_wn, N, 1, dtype, dtype, bias != nullptr,
+                       stream);
+}
+
+mg_status mg_attention_scores(const void* Q, const void* K, void* S, int64_t heads, int64_t Lq, int64_t Lk, int64_t d,
+                              int64_t stride_qh, int64_t stride_qm, int64_t stride_kh, int64_t stride_kn,
+                              int64_t stride_sh, int64_t stride_sm, mg_dtype dtype, hipStream_t stream) {
+    if (dtype == MG_F32) return MG_ERR_UNSUPPORTED_DTYPE;
+    // S_h[Lq, Lk] = Q_h[Lq, d] * B with B = K_h^T: element (t, j) of B is
+    // K_h[j, t], i.e. unit stride along t and stride_kn along j.
+    return gemm_common(Q, K, nullptr, S, Lq, Lk, d, stride_qm, 1, 1, stride_kn, stride_sm, 1, dtype, dtype, false,
+                       stream, heads, stride_qh, stride_kh, stride_sh);
 }
 
 }  // extern "C"

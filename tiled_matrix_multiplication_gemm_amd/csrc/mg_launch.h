@@ -94,11 +94,14 @@ bool direct_fits(int mode, int ta, int tb, const KArgs& a) {
 template <class C, class F>
 mg_status launch_dt(int dt, bool epi, int mode, int ta, int tb, const KArgs& a, int64_t grid, hipStream_t s) {
     if constexpr (!std::is_void<F>::value) {
-        if (direct_fits<F>(mode, ta, tb, a))
+        if (direct_fits<F>(mode, ta, tb, a)) {
+            if (a.dry) return MG_OK;
             return dt == DT_F16 ? launch_direct<F, DT_F16>(epi, mode, ta, tb, a, grid, s)
                                 : launch_direct<F, DT_BF16>(epi, mode, ta, tb, a, grid, s);
+        }
     }
     if (ta || tb || mode == MODE_SPLITK) return MG_ERR_UNSUPPORTED_LAYOUT;
+    if (a.dry) return MG_OK;
     return dt == DT_F16 ? launch_general<C, DT_F16>(epi, mode, a, grid, s)
                         : launch_general<C, DT_BF16>(epi, mode, a, grid, s);
 }

@@ -46,6 +46,7 @@ struct KArgs {
     int32_t splits;          // split-K: K ranges (contiguous runs of K slices)
     int32_t group_m;
     int32_t xcd_remap;
+    int32_t dry;             // host only: 1 = validate the launch, enqueue nothing
 };
 
 // Grouped GEMM: which tile workgroup `logical` computes.  Tiles run expert by

@@ -170,3 +170,78 @@ def grouped_workload(name: str, variant: str = "float", counts=None) -> GroupedC
     seed = w["seed_float"] if variant == "float" else w["seed_int"]
     return random_grouped(w["E"], w["T"], w["K"], w["N"], w["dtype"], seed, w["w_sigma"], counts=counts,
                           integer=(variant == "int"), name=name)
+
+
+# ---- GEMM consumers ------------------------------------------------------------
+# The pages name no convolution or attention workload; the shapes below are a
+# mid-network 3x3 convolution stage and one attention layer's scores, with
+# He-style weight scaling so that outputs are O(1).
+F32 = 2
+
+
+def _store(x: np.ndarray, dtype: int) -> np.ndarray:
+    if dtype == F32:
+        return np.ascontiguousarray(x, dtype=np.float64).astype(np.float32).view(np.uint32)
+    return to_bits(x, dtype)
+
+
+@dataclass
+class ConvCase:
+    name: str
+    x: np.ndarray          # NHWC [Nb,H,W,C] bit patterns
+    w: np.ndarray          # [KH,KW,C,OC] bit patterns
+    bias: np.ndarray | None
+    dtype: int
+    stride: tuple
+    pad: tuple
+    dil: tuple
+    integer: bool
+
+
+def conv_case(Nb, H, W, C, OC, KH, KW, dtype, seed, stride=(1, 1), pad=(0, 0), dil=(1, 1), integer=False,
+              bias=False, name="conv") -> ConvCase:
+    """x ~ N(0,1), w ~ N(0,1)/sqrt(KH KW C), bias ~ N(0, 0.1); or integers on
+    -4..4 (exact sums).  Drawn in the order x, w, bias."""
+    rng = np.random.default_rng(seed)
+    K = KH * KW * C
+    if integer:
+        x = rng.integers(-4, 5, size=(Nb, H, W, C)).astype(np.float64)
+        w = rng.integers(-4, 5, size=(KH, KW, C, OC)).astype(np.float64)
+        b = rng.integers(-4, 5, size=OC).astype(np.float64) if bias else None
+    else:
+        x = rng.standard_normal(size=(Nb, H, W, C))
+        w = rng.standard_normal(size=(KH, KW, C, OC)) / np.sqrt(max(K, 1))
+        b = rng.standard_normal(size=OC) * 0.1 if bias else None
+    return ConvCase(name, _store(x, dtype), _store(w, dtype), None if b is None else _store(b, dtype), dtype,
+                    tuple(stride), tuple(pad), tuple(dil), integer)
+
+
+@dataclass
+class AttentionCase:
+    name: str
+    Q: np.ndarray  # [heads, Lq, d] bit patterns
+    K: np.ndarray  # [heads, Lk, d] bit patterns
+    dtype: int
+    integer: bool
+
+
+def attention_case(heads, Lq, Lk, d, dtype, seed, integer=False, name="attention") -> AttentionCase:
+    """Q, K ~ N(0,1) / d^(1/4) each (scores of unit variance); or integers on
+    -4..4.  Drawn in the order Q, K."""
+    rng = np.random.default_rng(seed)
+    if integer:
+        q = rng.integers(-4, 5, size=(heads, Lq, d)).astype(np.float64)
+        k = rng.integers(-4, 5, size=(heads, Lk, d)).astype(np.float64)
+    else:
+        s = float(d) ** -0.25
+        q = rng.standard_normal(size=(heads, Lq, d)) * s
+        k = rng.standard_normal(size=(heads, Lk, d)) * s
+    return AttentionCase(name, _store(q, dtype), _store(k, dtype), dtype, integer)
+
+
+# Timed consumer workloads: a 3x3 convolution stage at batch 32 (56x56, 64 ->
+# 64 channels) and the scores of one attention layer (batch 8 x 16 heads,
+# 2048 tokens, head dimension 128).
+CONV_WORKLOAD = dict(Nb=32, H=56, W=56, C=64, OC=64, KH=3, KW=3, stride=(1, 1), pad=(1, 1), dil=(1, 1),
+                     dtype=F16, seed_float=106, seed_int=206)
+ATTENTION_WORKLOAD = dict(heads=128, L=2048, d=128, dtype=BF16, seed_float=107, seed_int=207)
