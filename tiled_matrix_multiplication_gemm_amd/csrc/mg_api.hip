@@ -46,8 +46,9 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // rate relative to 256x256 tiles (offline sweep on MI355X, 8192^3 bf16).
 // Large outputs get 256x256 tiles, outputs too small to give every CU one of
 // them get smaller tiles (1024 x 1024 -> 64x64).  Grouped GEMMs use the
-// 256x256 row (each expert's weight slab is read by one or two tiles).
-int select_config(int64_t M, int64_t N, int64_t K, int grouped) {
+// 256x256 row (each expert's weight slab is read by one or two tiles).  A
+// batched product counts the tiles of every entry.
+int select_config(int64_t M, int64_t N, int64_t K, int grouped, int64_t batch = 1) {
     (void)K;
     int forced = g_forced.load();
     if (forced >= 0) return forced;
@@ -62,7 +63,7 @@ int select_config(int64_t M, int64_t N, int64_t K, int grouped) {
     int best = 0;
     double best_t = 0.0;
     for (const Cand& c : cands) {
-        const int64_t tiles = cdiv(M, c.bm) * cdiv(N, c.bn);
+        const int64_t tiles = cdiv(M, c.bm) * cdiv(N, c.bn) * (batch > 1 ? batch : 1);
         const double t = (double)cdiv(tiles, kCUs) * ((double)c.bm * c.bn / c.rate);
         if (best_t == 0.0 || t < best_t) {
             best_t = t;
@@ -233,7 +234,7 @@ mg_status gemm_common(const void* A, const void* B, const void* bias, void* C, i
     MG_TRY(check_matrix(C, M, N, scm, scn));
     if (epi && N > 0 && M > 0 && bias == nullptr) return MG_ERR_INVALID_ARG;
     if (M == 0 || N == 0 || batch == 0) return MG_OK;
-    const int cfg = select_config(M, N, K, 0);
+    const int cfg = select_config(M, N, K, 0, batch);
     if (cfg < 0 || cfg >= kNumConfigs) return MG_ERR_BAD_CONFIG;
     KArgs a{};
     a.A = (const uint16_t*)A;
