@@ -237,15 +237,24 @@ mg_status mg_im2col(const mg_conv2d_shape* shape, const void* x, void* cols, int
 
 /*
  * Workspace that mg_conv2d needs for `shape`: the im2col matrix
- * [batch*OH*OW, ld] with ld = K rounded up to whole 16-byte chunks, or 0 for
- * a 1x1 kernel with unit stride and no padding whose channel rows are whole
- * 16-byte chunks (the input itself is then the GEMM's A).  0 also for an
- * invalid shape.
+ * [batch*OH*OW, ld] with ld = K rounded up to whole 16-byte chunks, or 0
+ * when the convolution runs without one:
+ *  - a 1x1 kernel with unit stride and no padding whose channel rows are
+ *    whole 16-byte chunks (the input itself is then the GEMM's A);
+ *  - implicit GEMM: fp16/bf16, an image batch below 2^31 bytes and an
+ *    in_channels count that the selected configuration's K slice divides
+ *    (every multiple of 64 qualifies).  The GEMM kernel then gathers each
+ *    slice of its A operand straight from the image, zero-filling taps
+ *    outside it, and im2col never reaches memory.
+ * 0 also for an invalid shape.  The answer depends on the configuration
+ * table, so an mg_set_config() override applies to it as to mg_conv2d.
  */
 size_t mg_conv2d_workspace_bytes(const mg_conv2d_shape* shape, mg_dtype dtype);
 
 /*
- * 2-D convolution as im2col + GEMM (FlagOS cross-chip page, section 5.3):
+ * 2-D convolution as a GEMM over the im2col matrix (FlagOS cross-chip page,
+ * section 5.3), gathered by the GEMM's loads (implicit GEMM) or written by
+ * the im2col kernel into the workspace first (see mg_conv2d_workspace_bytes):
  *     y[n,oh,ow,o] = sum_{kh,kw,c} x[n, ih, iw, c] * w(k = (kh*kernel_w + kw)*in_channels + c, o)
  * then, when bias is not null, ReLU(y + bias[o]) (the fused epilogue of
  * mg_gemm_bias_relu).  x: dense NHWC, 16-byte aligned.  w: the K x
@@ -256,8 +265,7 @@ size_t mg_conv2d_workspace_bytes(const mg_conv2d_shape* shape, mg_dtype dtype);
  * NHWC; its row length out_channels must span whole 16-byte chunks.
  * workspace: at least mg_conv2d_workspace_bytes() bytes of device memory,
  * 16-byte aligned (may be null when that is 0), used by this call's kernels
- * only until they finish.  The im2col kernel and the GEMM run in order on
- * `stream`.  Errors as mg_im2col and mg_gemm; a short workspace is
+ * only until they finish.  The kernels run in order on `stream`.  Errors as mg_im2col and mg_gemm; a short workspace is
  * MG_ERR_INVALID_ARG.  batch == 0 or out_channels == 0 does nothing.
  */
 mg_status mg_conv2d(const mg_conv2d_shape* shape, const void* x, const void* w, int64_t stride_wk,

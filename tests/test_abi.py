@@ -259,14 +259,17 @@ def test_conv_output_size(L):
 
 def test_conv_workspace_bytes(L):
     M = 2 * 16 * 16
-    assert L.mg_conv2d_workspace_bytes(ctypes.byref(shape()), F16) == M * 576 * 2
-    assert L.mg_conv2d_workspace_bytes(ctypes.byref(shape()), 2) == M * 576 * 4
+    assert L.mg_conv2d_workspace_bytes(ctypes.byref(shape()), F16) == 0  # the GEMM gathers from the image
+    assert L.mg_conv2d_workspace_bytes(ctypes.byref(shape(in_channels=128)), BF16) == 0
+    assert L.mg_conv2d_workspace_bytes(ctypes.byref(shape(in_channels=16)), F16) == M * 144 * 2
+    assert L.mg_conv2d_workspace_bytes(ctypes.byref(shape()), 2) == M * 576 * 4  # fp32: im2col + GEMM
     assert L.mg_conv2d_workspace_bytes(ctypes.byref(shape(in_channels=3)), F16) == M * 32 * 2  # 27 -> 32
     assert L.mg_conv2d_workspace_bytes(ctypes.byref(shape(in_channels=3)), 2) == M * 28 * 4  # 27 -> 28
     one = dict(kernel_h=1, kernel_w=1, pad_h=0, pad_w=0)
     assert L.mg_conv2d_workspace_bytes(ctypes.byref(shape(**one)), F16) == 0  # the input is the GEMM's A
     assert L.mg_conv2d_workspace_bytes(ctypes.byref(shape(in_channels=12, **one)), F16) == M * 16 * 2
-    assert L.mg_conv2d_workspace_bytes(ctypes.byref(shape(stride_h=2, **one)), F16) == 2 * 8 * 16 * 64 * 2
+    assert L.mg_conv2d_workspace_bytes(ctypes.byref(shape(stride_h=2, **one)), F16) == 0  # gathered
+    assert L.mg_conv2d_workspace_bytes(ctypes.byref(shape(stride_h=2, in_channels=16, **one)), F16) == 2 * 8 * 16 * 16 * 2
     assert L.mg_conv2d_workspace_bytes(ctypes.byref(shape(kernel_h=0)), F16) == 0
     assert L.mg_conv2d_workspace_bytes(ctypes.byref(shape()), 7) == 0
 
@@ -289,10 +292,13 @@ def conv(L, s=None, x=P, w=P, swk=64, swn=1, bias=None, y=P, ws=P, ws_bytes=1 <<
     return L.mg_conv2d(ctypes.byref(s or shape()), x, w, swk, swn, bias, y, ws, ws_bytes, dt, S)
 
 
+C16 = shape(in_channels=16)  # 16 channels: never gathered by the GEMM, so im2col needs a workspace
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(dt=9), DTYPE), (dict(x=None), INVALID), (dict(x=P + 4), MISALIGNED), (dict(w=None), INVALID),
-    (dict(y=None), INVALID), (dict(ws=None), INVALID), (dict(ws_bytes=2 * 256 * 576 * 2 - 1), INVALID),
-    (dict(ws=P + 8), MISALIGNED), (dict(swk=64, swn=2), LAYOUT), (dict(swk=70, swn=1), MISALIGNED),
+    (dict(y=None), INVALID), (dict(s=C16, ws=None), INVALID), (dict(s=C16, ws_bytes=2 * 256 * 144 * 2 - 1), INVALID),
+    (dict(s=C16, ws=P + 8), MISALIGNED), (dict(swk=64, swn=2), LAYOUT), (dict(swk=70, swn=1), MISALIGNED),
     (dict(s=shape(out_channels=4), swk=4), MISALIGNED),  # NHWC rows of 4 fp16 are not 16-byte rows
     (dict(s=shape(in_channels=3), swk=1, swn=27), MISALIGNED),  # OHWI rows of 27 fp16
     (dict(s=shape(in_channels=8), swk=1, swn=72), LAYOUT),  # OHWI needs K in whole slices (72 is not)
@@ -327,3 +333,14 @@ def attn(L, Q=P, K=P, Sx=P, heads=4, Lq=128, Lk=128, d=64, sqh=128 * 64, sqm=64,
 ])
 def test_attention_scores_rejects_bad_arguments(L, kw, status):
     assert attn(L, **kw) == status
+
+
+def test_conv_workspace_follows_a_forced_row(L):
+    # the general-only row cannot gather: the convolution then needs the im2col workspace
+    assert L.mg_set_config(5) == OK
+    try:
+        assert L.mg_conv2d_workspace_bytes(ctypes.byref(shape()), F16) == 2 * 256 * 576 * 2
+        assert conv(L, ws=None) == INVALID
+    finally:
+        L.mg_set_config(-1)
+    assert L.mg_conv2d_workspace_bytes(ctypes.byref(shape()), F16) == 0

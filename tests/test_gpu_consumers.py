@@ -128,6 +128,11 @@ CONV_CASES = [
     (1, 14, 13, 16, 16, 3, 3, (1, 1), (2, 2), (2, 2), F16, "hwio"),     # dilation
     (2, 10, 10, 64, 64, 3, 3, (1, 1), (1, 1), (1, 1), F16, "ohwi"),     # transposed weights
     (1, 12, 12, 16, 32, 3, 3, (1, 1), (1, 1), (1, 1), F32, "hwio"),     # fp32, K = 144
+    # C % 64 == 0: the GEMM gathers A from the image (implicit GEMM)
+    (2, 13, 11, 64, 96, 3, 5, (2, 1), (1, 2), (1, 1), F16, "hwio"),     # KH != KW, uneven stride / pad
+    (1, 16, 16, 128, 64, 3, 3, (1, 1), (2, 2), (2, 2), BF16, "ohwi"),   # dilation, OHWI weights
+    (3, 7, 9, 64, 64, 1, 1, (2, 2), (0, 0), (1, 1), F16, "hwio"),       # 1x1 stride 2
+    (1, 5, 5, 64, 32, 5, 5, (1, 1), (0, 0), (1, 1), BF16, "hwio"),      # one output row
 ]
 
 
@@ -163,6 +168,22 @@ def test_conv2d(case):
                 wa = np.abs(oracle.decode32(c.w)).astype(np.float32).view(np.uint32)
                 absref, _ = oracle.conv2d(xa, wa, F32, stride, pad, dil)
             check(got, ref, ref_q, dt, integer, label, absref, KH * KW * C)
+
+
+def test_conv2d_every_row():
+    """The gathering kernel of every table row (K slices of 32 and 64), and the
+    im2col + GEMM fallback of the general-only and K-split rows."""
+    c = inputs.conv_case(2, 17, 15, 64, 64, 3, 3, F16, seed=45, stride=(1, 2), pad=(1, 1), integer=True, bias=True)
+    ref, ref_q = oracle.conv2d(c.x, c.w, F16, c.stride, c.pad, c.dil, bias=c.bias, relu=True)
+    try:
+        for cfg in range(mg.mg_num_configs()):
+            announce("conv forced row %d" % cfg)
+            mg.mg_set_config(cfg)
+            got, guards = run_conv(c, 64, "hwio", c.bias)
+            assert guards
+            assert_bitexact(got, ref_q, F16, "conv row %d" % cfg)
+    finally:
+        mg.mg_set_config(-1)
 
 
 def test_conv2d_repeat_is_deterministic():

@@ -302,6 +302,48 @@ bool conv_zero_copy(const mg_conv2d_shape* s, int es) {
            s->pad_w == 0 && (s->in_channels * es) % 16 == 0;
 }
 
+// The GEMM gathers its A operand from the image itself (MODE_CONV): 16-bit
+// types, an image batch below 2^31 bytes (32-bit load offsets), and a table
+// row (the selected or the forced one) with a direct-to-LDS kernel whose K
+// slice divides the channel count, so that a slice lies within one tap.
+bool conv_implicit(const mg_conv2d_shape* s, const ConvGeom& g, int es) {
+    if (es != 2 || s->in_channels <= 0 || s->out_channels <= 0 || g.M <= 0) return false;
+    const int64_t lim = ((int64_t)1 << 31) / (2 * s->in_channels);  // pixels that fit
+    const int64_t px = s->height * s->width;                           // both < 2^30, batch > 0 here
+    if (px > lim || s->batch > lim / px) return false;
+    const int cfg = select_config(g.M, s->out_channels, g.K, 0);
+    if (cfg < 0 || cfg >= kNumConfigs) return false;
+    const mg_config_desc& d = kTable[cfg];
+    return d.direct_lds == 1 && d.direct_ksplit == 1 && s->in_channels % d.direct_bk == 0;
+}
+
+// Implicit-GEMM convolution: one launch of the selected row's gathering kernel.
+mg_status conv_implicit_launch(const mg_conv2d_shape* s, const ConvGeom& g, const void* x, const void* w,
+                               int64_t swk, int64_t swn, const void* bias, void* y, mg_dtype dtype,
+                               hipStream_t stream) {
+    const int64_t N = s->out_channels, K = g.K;
+    const int tb = (swn == 1 || N <= 1) ? 0 : ((swk == 1 || K <= 1) ? 1 : -1);
+    if (tb < 0) return MG_ERR_UNSUPPORTED_LAYOUT;
+    MG_TRY(tb ? check_matrix(w, N, K, swn, swk) : check_matrix(w, K, N, swk, swn));
+    MG_TRY(check_matrix(y, g.M, N, N, 1));
+    const int cfg = select_config(g.M, N, K, 0);
+    if (cfg < 0 || cfg >= kNumConfigs) return MG_ERR_BAD_CONFIG;
+    KArgs a{};
+    a.A = (const uint16_t*)x;
+    a.B = (const uint16_t*)w;
+    a.C = (uint16_t*)y;
+    a.bias = (const uint16_t*)bias;
+    a.M = g.M; a.N = N; a.K = K;
+    a.lda = 0;  // unused: rows are gathered
+    a.ldb = tb ? swn : swk;
+    a.ldc = N;
+    a.batch = 1;
+    a.conv = ConvArgs{(int32_t)s->height, (int32_t)s->width, (int32_t)s->in_channels, (int32_t)s->kernel_w,
+                      (int32_t)s->stride_h, (int32_t)s->stride_w, (int32_t)s->pad_h, (int32_t)s->pad_w,
+                      (int32_t)s->dilation_h, (int32_t)s->dilation_w, (int32_t)g.OH, (int32_t)g.OW};
+    return launch(cfg, (int)dtype, bias != nullptr, MODE_CONV, a, stream, 0, tb);
+}
+
 // Validated arguments; enqueues the im2col kernel.
 mg_status launch_im2col(const mg_conv2d_shape* s, const ConvGeom& g, const void* x, void* cols, int64_t ld, int es,
                         hipStream_t stream) {
@@ -584,7 +626,8 @@ mg_status mg_im2col(const mg_conv2d_shape* shape, const void* x, void* cols, int
 size_t mg_conv2d_workspace_bytes(const mg_conv2d_shape* shape, mg_dtype dtype) {
     ConvGeom g{};
     const int es = elem_bytes(dtype);
-    if (es == 0 || conv_geom(shape, g) != MG_OK || conv_zero_copy(shape, es)) return 0;
+    if (es == 0 || conv_geom(shape, g) != MG_OK || conv_zero_copy(shape, es) || conv_implicit(shape, g, es))
+        return 0;
     return (size_t)(g.M * im2col_ld(g.K, es) * es);
 }
 
@@ -597,6 +640,8 @@ mg_status mg_conv2d(const mg_conv2d_shape* shape, const void* x, const void* w, 
     if (es == 0) return MG_ERR_UNSUPPORTED_DTYPE;
     MG_TRY(check_image(shape, x));
     if (g.M == 0 || shape->out_channels == 0) return MG_OK;
+    if (!conv_zero_copy(shape, es) && conv_implicit(shape, g, es))
+        return conv_implicit_launch(shape, g, x, w, stride_wk, stride_wn, bias, y, dtype, stream);
     const bool direct = conv_zero_copy(shape, es);
     const int64_t ld = direct ? shape->in_channels : im2col_ld(g.K, es);
     const void* A = direct ? x : workspace;

@@ -122,10 +122,16 @@ template <int E, int BK, int NW>
 struct OpKM {
     static constexpr int CH = BK / 8, LINE = BK * 2, BYTES = E * LINE, J = BYTES / 1024 / NW;
     // byte offset (from the tile's first line of the slice) of load j of wave w, lane l
-    __device__ static uint32_t load_off(int w, int j, int lane, int64_t e0, int64_t ext, int64_t ld) {
+    // line of the tile and (swizzled) 16-byte chunk of the slice that load j
+    // of wave w, lane l fetches
+    __device__ static void load_pos(int w, int j, int lane, int& line, int& c) {
         const int q = w * J + j;
-        const int line = q * (1024 / LINE) + lane / CH;
-        const int c = (lane % CH) ^ swz_a<CH>(line);
+        line = q * (1024 / LINE) + lane / CH;
+        c = (lane % CH) ^ swz_a<CH>(line);
+    }
+    __device__ static uint32_t load_off(int w, int j, int lane, int64_t e0, int64_t ext, int64_t ld) {
+        int line, c;
+        load_pos(w, j, lane, line, c);
         const int64_t r = (e0 + line < ext ? line : ext - 1 - e0);
         return (uint32_t)((r * ld + 8 * c) * 2);
     }
@@ -293,15 +299,71 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
     const char* baseA = OA::tile_base(Ag, m0, args.lda) + kt0 * stepA;
     const char* baseB = OB::tile_base(Bg, n0, args.ldb) + kt0 * stepB;
 
+    // Implicit-GEMM convolution: load j of this lane fetches, for output row
+    // m (clamped to M-1 like any tile row) of image n at (oh, ow), the 16-byte
+    // chunk `c` of the slice's channel run of input pixel (oh sh - ph + kh dh,
+    // ow sw - pw + kw dw).  A slice lies within one kernel tap (C % BK == 0);
+    // slices are issued in increasing order, so the tap (kh, kw) and channel
+    // offset c0 advance by one slice per call.  Taps outside the image take
+    // an offset past the buffer's range: the range check returns zeros.
+    [[maybe_unused]] int32_t cv_ih0[JA], cv_iw0[JA];
+    [[maybe_unused]] uint32_t cv_base[JA];
+    [[maybe_unused]] int32_t cv_c0 = 0, cv_kw = 0, cv_khd = 0, cv_kwd = 0;
+    if constexpr (MODE == MODE_CONV) {
+        static_assert(!TA, "the gathered A operand is K-major");
+        const ConvArgs& cv = args.conv;
+        const uint32_t ohw = (uint32_t)cv.OH * (uint32_t)cv.OW;
+#pragma unroll
+        for (int j = 0; j < JA; ++j) {
+            int line, c;
+            OA::load_pos(wave, j, lane, line, c);
+            const uint32_t m = (uint32_t)(m0 + line < M ? m0 + line : M - 1);  // M < 2^31
+            const uint32_t n = m / ohw, rem = m - n * ohw;
+            const uint32_t oh = rem / (uint32_t)cv.OW, ow = rem - oh * (uint32_t)cv.OW;
+            cv_ih0[j] = (int32_t)oh * cv.sh - cv.ph;
+            cv_iw0[j] = (int32_t)ow * cv.sw - cv.pw;
+            // the host keeps the whole image batch below 2^31 bytes
+            cv_base[j] = (n * (uint32_t)cv.H * (uint32_t)cv.W * (uint32_t)cv.C + 8u * (uint32_t)c) * 2u;
+        }
+    }
+
     // direct loads of k-slice kt into ring slot `slot` (a compile-time index)
     // (buffer resources rebased on the slice: offsets stay below 2^31)
     auto issue = [&](int kt, int slot) {
-        const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(baseA + kt * stepA);
+        [[maybe_unused]] uint32_t offA[JA];
+        __amdgpu_buffer_rsrc_t ra;
+        if constexpr (MODE == MODE_CONV) {
+            const ConvArgs& cv = args.conv;
+            ra = buffer_rsrc((const char*)Ag);
+#pragma unroll
+            for (int j = 0; j < JA; ++j) {
+                const int32_t ih = cv_ih0[j] + cv_khd, iw = cv_iw0[j] + cv_kwd;
+                const bool in = (uint32_t)ih < (uint32_t)cv.H && (uint32_t)iw < (uint32_t)cv.W;
+                offA[j] = in ? cv_base[j] + (((uint32_t)ih * (uint32_t)cv.W + (uint32_t)iw) * (uint32_t)cv.C +
+                                             (uint32_t)cv_c0) * 2u
+                             : 0x80000000u;
+            }
+            // next slice: the following channel run, else the next tap
+            cv_c0 += BK;
+            if (cv_c0 == cv.C) {
+                cv_c0 = 0;
+                cv_kwd += cv.dw;
+                if (++cv_kw == cv.KW) {
+                    cv_kw = 0;
+                    cv_kwd = 0;
+                    cv_khd += cv.dh;
+                }
+            }
+        } else {
+            ra = buffer_rsrc(baseA + kt * stepA);
+#pragma unroll
+            for (int j = 0; j < JA; ++j) offA[j] = offA_g[j];
+        }
         const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(baseB + kt * stepB);
         char* sa = slot_ptr(slot);
         char* sb = sa + Cfg::A_BYTES;
 #pragma unroll
-        for (int j = 0; j < JA; ++j) direct_load16(ra, offA_g[j], (lds_void_t*)(sa + (wave * JA + j) * 1024));
+        for (int j = 0; j < JA; ++j) direct_load16(ra, offA[j], (lds_void_t*)(sa + (wave * JA + j) * 1024));
 #pragma unroll
         for (int j = 0; j < JB; ++j) direct_load16(rb, offB_g[j], (lds_void_t*)(sb + (wave * JB + j) * 1024));
     };

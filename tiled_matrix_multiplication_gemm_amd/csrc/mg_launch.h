@@ -70,6 +70,12 @@ mg_status launch_direct(bool epi, int mode, int ta, int tb, const KArgs& a, int6
     } else {
         if (mode == MODE_SPLITK) return launch_split<F, DT>(ta, tb, a, grid, s);
         if (mode == MODE_GROUPED) return launch_fast<F, DT, false, MODE_GROUPED>(a, grid, s);
+        if (mode == MODE_CONV) {
+            if (epi) return tb ? launch_fast<F, DT, true, MODE_CONV, false, true>(a, grid, s)
+                               : launch_fast<F, DT, true, MODE_CONV, false, false>(a, grid, s);
+            return tb ? launch_fast<F, DT, false, MODE_CONV, false, true>(a, grid, s)
+                      : launch_fast<F, DT, false, MODE_CONV, false, false>(a, grid, s);
+        }
         return epi ? launch_fast_t<F, DT, true>(ta, tb, a, grid, s) : launch_fast_t<F, DT, false>(ta, tb, a, grid, s);
     }
 }
@@ -81,9 +87,11 @@ mg_status launch_direct(bool epi, int mode, int ta, int tb, const KArgs& a, int6
 template <class F>
 bool direct_fits(int mode, int ta, int tb, const KArgs& a) {
     constexpr int64_t LIM = (int64_t)1 << 31;
-    if (mode == MODE_PACKED_A || (is_slab<F>::value && (mode == MODE_GROUPED || mode == MODE_SPLITK || ta || tb)))
+    if (mode == MODE_PACKED_A ||
+        (is_slab<F>::value && (mode == MODE_GROUPED || mode == MODE_SPLITK || mode == MODE_CONV || ta || tb)))
         return false;
     if (a.K % F::BK != 0 || a.N % 8 != 0 || (ta && a.M % 8 != 0)) return false;
+    if (mode == MODE_CONV && (ta || a.conv.C % F::BK != 0)) return false;  // a slice within one kernel tap
     const int64_t a_span = ta ? 64 * a.lda * 2 : (int64_t)F::BM * a.lda * 2;
     const int64_t b_span = tb ? (int64_t)F::BN * a.ldb * 2 : 64 * a.ldb * 2;
     return a_span < LIM && b_span < LIM;
@@ -100,7 +108,7 @@ mg_status launch_dt(int dt, bool epi, int mode, int ta, int tb, const KArgs& a, 
                                 : launch_direct<F, DT_BF16>(epi, mode, ta, tb, a, grid, s);
         }
     }
-    if (ta || tb || mode == MODE_SPLITK) return MG_ERR_UNSUPPORTED_LAYOUT;
+    if (ta || tb || mode == MODE_SPLITK || mode == MODE_CONV) return MG_ERR_UNSUPPORTED_LAYOUT;
     if (a.dry) return MG_OK;
     return dt == DT_F16 ? launch_general<C, DT_F16>(epi, mode, a, grid, s)
                         : launch_general<C, DT_BF16>(epi, mode, a, grid, s);

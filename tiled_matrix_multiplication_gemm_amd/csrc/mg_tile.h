@@ -27,7 +27,16 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 enum { DT_F16 = 0, DT_BF16 = 1 };
-enum { MODE_DENSE = 0, MODE_PACKED_A = 1, MODE_GROUPED = 2, MODE_SPLITK = 3 };
+enum { MODE_DENSE = 0, MODE_PACKED_A = 1, MODE_GROUPED = 2, MODE_SPLITK = 3, MODE_CONV = 4 };
+
+// Implicit-GEMM convolution (MODE_CONV): A is the im2col matrix of an NHWC
+// image batch, gathered by the loads themselves.  Output row m = (n OH + oh)
+// OW + ow; column k = (kh KW + kw) C + c.
+struct ConvArgs {
+    int32_t H, W, C, KW;
+    int32_t sh, sw, ph, pw, dh, dw;
+    int32_t OH, OW;
+};
 
 struct KArgs {
     const uint16_t* A;       // dense: A; packed: blocked A; grouped: X
@@ -47,6 +56,7 @@ struct KArgs {
     int32_t group_m;
     int32_t xcd_remap;
     int32_t dry;             // host only: 1 = validate the launch, enqueue nothing
+    ConvArgs conv;           // MODE_CONV only
 };
 
 // Grouped GEMM: which tile workgroup `logical` computes.  Tiles run expert by
