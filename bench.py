@@ -12,7 +12,11 @@ Beside the main figure the line carries:
   cpu_baseline  the CPU oracle timed on this host on a bounded sample of the
                 same workload (whole output rows), scaled to TFLOP/s;
   also          the same measurement for the 1024x1024x2048 fp16 GEMM, its
-                fused bias+ReLU form and the grouped MoE GEMM.
+                fused bias+ReLU form, the grouped MoE GEMM, the 4096^3 fp32
+                GEMM (against the fp32 matrix peak), a 3x3 convolution on the
+                GEMM (implicit im2col; batch 32, 56x56, 64 -> 64 channels,
+                fp16) and attention scores Q K^T (128 heads, 2048 x 2048,
+                d = 128, bf16; bound by writing the 1 GiB of scores).
 
 Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 50] [--no-cpu-baseline] [--no-also]
 """
@@ -31,6 +35,7 @@ if ROOT not in sys.path:
 METRIC = "GEMM TFLOP/s and % of MI355X fp16 MFMA peak (1024x1024x2048 and 8192^3)"
 PEAK_MFMA_TFLOPS = 2516.6   # dense fp16/bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
 PEAK_HBM_GBS = 8000.0       # HBM3E
+PEAK_F32_TFLOPS = 157.3     # dense fp32 matrix (and vector) peak
 
 
 def parse():
@@ -202,6 +207,63 @@ def cpu_baseline(case, target_s: float):
                                                                                        case.K, dt)}
 
 
+def measure_consumers(steps, warmup):
+    """fp32 GEMM, convolution and attention-score workloads: kernel time from
+    HIP events, TFLOP/s, and compulsory HBM bytes per second."""
+    import numpy as np
+    import torch
+
+    import tiled_matrix_multiplication_gemm_amd as mg
+    from tiled_matrix_multiplication_gemm_amd import inputs
+
+    out = {}
+    # fp32 GEMM 4096^3 (the fp32 row of the FlagOS page's table)
+    c = inputs.dense_f32(4096, 4096, 4096, seed=110)
+    A = torch.from_numpy(c.A.view(np.float32)).cuda()
+    B = torch.from_numpy(c.B.view(np.float32)).cuda()
+    C = torch.empty((4096, 4096), device="cuda")
+    wall, mean_ms, _ = time_calls(lambda: mg.mg_gemm(A, B, out=C), steps, warmup)
+    fl = 2.0 * 4096 ** 3
+    ach = fl / (mean_ms * 1e-3) / 1e12
+    out["gemm_4096_f32"] = {"kernel_tflops": round(ach, 2), "frac_f32_peak": round(ach / PEAK_F32_TFLOPS, 4),
+                            "kernel_ms_mean": round(mean_ms, 5)}
+    del A, B, C
+    # 3x3 convolution, implicit GEMM
+    w = inputs.CONV_WORKLOAD
+    cc = inputs.conv_case(w["Nb"], w["H"], w["W"], w["C"], w["OC"], w["KH"], w["KW"], w["dtype"], w["seed_float"],
+                          w["stride"], w["pad"], w["dil"])
+    x, wt = upload(cc.x, cc.dtype), upload(cc.w, cc.dtype)
+    y = torch.empty((w["Nb"], w["H"], w["W"], w["OC"]), dtype=x.dtype, device="cuda")
+    fn = lambda: mg.mg_conv2d(x, wt, w["stride"], w["pad"], w["dil"], out=y)
+    wall, mean_ms, _ = time_calls(fn, steps, warmup)
+    M, K = w["Nb"] * w["H"] * w["W"], w["KH"] * w["KW"] * w["C"]
+    fl = 2.0 * M * K * w["OC"]
+    byts = 2.0 * (x.numel() + wt.numel() + y.numel())
+    ach = fl / (mean_ms * 1e-3) / 1e12
+    gbs = byts / (mean_ms * 1e-3) / 1e9
+    out["conv3x3_n32_56x56_c64_k64_f16"] = {
+        "kernel_tflops": round(ach, 2), "frac_mfma_peak": round(ach / PEAK_MFMA_TFLOPS, 4),
+        "hbm_gbs_compulsory": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+        "kernel_ms_mean": round(mean_ms, 5), "tile_config": mg.mg_config_info(mg.mg_last_config())["name"],
+        "workspace_bytes": mg.mg_conv2d_workspace_bytes(mg.conv2d_shape(x.shape, 3, w["OC"], 1, 1, 1), cc.dtype)}
+    del x, wt, y
+    # attention scores
+    a = inputs.ATTENTION_WORKLOAD
+    ac = inputs.attention_case(a["heads"], a["L"], a["L"], a["d"], a["dtype"], a["seed_float"])
+    q, k = upload(ac.Q, ac.dtype), upload(ac.K, ac.dtype)
+    S = torch.empty((a["heads"], a["L"], a["L"]), dtype=q.dtype, device="cuda")
+    wall, mean_ms, _ = time_calls(lambda: mg.mg_attention_scores(q, k, out=S), steps, warmup)
+    fl = 2.0 * a["heads"] * a["L"] * a["L"] * a["d"]
+    byts = 2.0 * (q.numel() + k.numel() + S.numel())
+    ach = fl / (mean_ms * 1e-3) / 1e12
+    gbs = byts / (mean_ms * 1e-3) / 1e9
+    out["attention_scores_h128_l2048_d128_bf16"] = {
+        "kernel_tflops": round(ach, 2), "frac_mfma_peak": round(ach / PEAK_MFMA_TFLOPS, 4),
+        "hbm_gbs_compulsory": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+        "kernel_ms_mean": round(mean_ms, 5), "tile_config": mg.mg_config_info(mg.mg_last_config())["name"]}
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -263,6 +325,7 @@ def main():
                        "kernel_tflops": round(ach, 2), "frac_mfma_peak": round(ach / PEAK_MFMA_TFLOPS, 4),
                        "hbm_gbs_compulsory": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
                        "kernel_ms_mean": round(r["kernel_ms"], 5), "tile_config": r["tile_config"]}
+        also.update(measure_consumers(min(args.steps, 50), min(args.warmup, 10)))
         line["also"] = also
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(c, args.cpu_seconds)

@@ -80,7 +80,7 @@ SMALL = [(1, 1, 1), (7, 33, 129), (33, 7, 1000), (129, 129, 33), (65, 200, 72),
          (300, 257, 130), (1000, 7, 33), (256, 384, 200), (513, 129, 257),
          (64, 64, 64), (1, 8, 64), (65, 200, 128), (129, 136, 64), (300, 264, 192), (513, 520, 256),
          (70, 72, 32), (96, 40, 96)]
-NUM_CONFIGS = 8
+NUM_CONFIGS = 9
 
 
 def test_config_count_matches_library():
@@ -211,7 +211,7 @@ def test_large_ragged_edges_sampled(orc, integer):
 # shapes the direct-to-LDS rows take (K a multiple of 64, N and M multiples
 # of 8), with ragged tile edges, on every row that has such a kernel.
 TRANSPOSED = [(64, 64, 64), (8, 8, 64), (72, 200, 128), (264, 136, 320), (520, 512, 256), (128, 264, 192)]
-DIRECT_ROWS = [0, 1, 2, 3, 4, 6]
+DIRECT_ROWS = [0, 1, 2, 3, 4, 6, 8]
 
 
 def stored_transposed(bits, dt):

@@ -33,6 +33,7 @@ const mg_config_desc kTable[kNumConfigs] = {
     describe<Cfg2, Fast2>(2, "t64x64_w2x2"),   describe<Cfg3, Fast3>(3, "t128x256_w2x2"),
     describe<Cfg4, Fast4>(4, "t256x128_w2x2"), describe<Cfg5, void>(5, "t128x128k32_w2x2"),
     describe<Cfg6, Fast6>(6, "t256x256_w2x2_k32r5"), describe<Cfg7, Fast7>(7, "t64x64_ksplit4"),
+    describe<Cfg8, Fast8>(8, "t256x64_w4x2"),
 };
 
 std::atomic<int> g_forced{-1};
@@ -43,9 +44,11 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Row choice for dense problems: a workgroup's tile runs on one CU, and the
 // tiles run in rounds of 256 (one per CU), so the time of a row is modelled
 // as rounds * (BM * BN / rate), with `rate` the row's measured per-CU output
-// rate relative to 256x256 tiles (offline sweep on MI355X, 8192^3 bf16).
-// Large outputs get 256x256 tiles, outputs too small to give every CU one of
-// them get smaller tiles (1024 x 1024 -> 64x64).  Grouped GEMMs use the
+// rate relative to 256x256 tiles (offline sweeps on MI355X: 8192^3 bf16 for
+// the square rows, a grid of tall thin fp16 shapes, M 12544..100352, N 64..256,
+// K 576..4608, for the 256x64 row).  Large outputs get 256x256 tiles, outputs
+// too small to give every CU one of them get smaller tiles (1024 x 1024 ->
+// 64x64), tall outputs of 64 or 128 columns get 256x64 slabs.  Grouped GEMMs use the
 // 256x256 row (each expert's weight slab is read by one or two tiles).  A
 // batched product counts the tiles of every entry.
 int select_config(int64_t M, int64_t N, int64_t K, int grouped, int64_t batch = 1) {
@@ -58,7 +61,7 @@ int select_config(int64_t M, int64_t N, int64_t K, int grouped, int64_t batch = 
         double rate;
     };
     static const Cand cands[] = {{0, 256, 256, 1.00}, {3, 128, 256, 0.76}, {4, 256, 128, 0.68},
-                                 {1, 128, 128, 0.49}, {2, 64, 64, 0.50}};
+                                 {1, 128, 128, 0.49}, {2, 64, 64, 0.50},  {8, 256, 64, 0.65}};
     constexpr int64_t kCUs = 256;
     int best = 0;
     double best_t = 0.0;
@@ -151,6 +154,7 @@ mg_status launch(int cfg, int dt, bool epi, int mode, KArgs& a, hipStream_t s, i
         case 5: st = launch_row5(dt, epi, mode, ta, tb, a, grid, s); break;
         case 6: st = launch_row6(dt, epi, mode, ta, tb, a, grid, s); break;
         case 7: st = launch_row7(dt, epi, mode, ta, tb, a, grid, s); break;
+        case 8: st = launch_row8(dt, epi, mode, ta, tb, a, grid, s); break;
         default: return MG_ERR_BAD_CONFIG;
     }
     if (st == MG_OK && !a.dry) g_last.store(cfg);

@@ -37,8 +37,12 @@ using Fast4 = DldsCfg<256, 128, 2, 2, 32, 4>;
 using Fast6 = DldsCfg<256, 256, 2, 2, 32, 5>;
 using Cfg7 = TileCfg<64, 64, 64, 2, 2>;
 using Fast7 = SlabCfg<64, 64, 4, 32, 4>;  // K split over the 4 waves of the workgroup
+// tall, thin outputs (N of 64 or 128 and many rows: convolution GEMMs, narrow
+// projections): a whole 64-column slab per tile, eight waves of 64 x 32
+using Cfg8 = TileCfg<256, 64, 64, 4, 2>;
+using Fast8 = DldsCfg<256, 64, 4, 2, 64, 4>;
 
-inline constexpr int kNumConfigs = 8;
+inline constexpr int kNumConfigs = 9;
 inline constexpr int kGroupM = 8;
 
 template <class F>
@@ -60,6 +64,7 @@ MG_DECLARE_ROW(4);
 MG_DECLARE_ROW(5);
 MG_DECLARE_ROW(6);
 MG_DECLARE_ROW(7);
+MG_DECLARE_ROW(8);
 
 // fp32 GEMM: one configuration (mg_f32.h), defined in mg_f32.hip
 // fp32 kernel tiles: 0 = 128 x 128 (large outputs), 1 = 64 x 64 (outputs
