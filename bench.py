@@ -8,7 +8,10 @@ torch.cuda.synchronize(); each call is also bracketed by HIP events on the
 launch stream, whose mean is the kernel time used for the roofline.
 
 Beside the main figure the line carries:
-  roofline      the GEMM kernel against the dense bf16 MFMA peak;
+  roofline      the GEMM kernel against the dense bf16 MFMA peak (and against
+                that peak scaled to the graphics clock the chip ran at);
+  telemetry     graphics clock and socket power (amdsmi) over a short soak
+                of the same call after the timed region;
   cpu_baseline  the CPU oracle timed on this host on a bounded sample of the
                 same workload (whole output rows), scaled to TFLOP/s;
   also          the same measurement for the 1024x1024x2048 fp16 GEMM, its
@@ -121,6 +124,75 @@ def time_calls(fn, steps: int, warmup: int):
     return wall, sum(per) / len(per), per[len(per) // 2]
 
 
+def soak_telemetry(fn, seconds: float = 1.6):
+    """Graphics clock and socket power while `fn` runs back to back.
+
+    Sampled through amdsmi on a background thread during a soak that follows
+    the timed region (never inside it).  The driver's metrics table trails
+    the hardware by up to about a second, so only samples from the second
+    half of the soak are kept.  Returns None where amdsmi is unavailable."""
+    import statistics
+    import threading
+
+    import torch
+
+    try:
+        import amdsmi
+
+        amdsmi.amdsmi_init()
+    except Exception:
+        return None
+    try:
+        handles = amdsmi.amdsmi_get_processor_handles()
+        if len(handles) != 1:
+            return None
+        h = handles[0]
+        limit_w = None
+        try:
+            limit_w = float(amdsmi.amdsmi_get_power_info(h)["power_limit"]) / 1e6  # reported in microwatts
+        except Exception:
+            pass
+        samples = []
+        stop = threading.Event()
+
+        def sample():
+            while not stop.is_set():
+                try:
+                    m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+                    clks = [v for v in (m.get("current_gfxclks") or [m.get("current_gfxclk")])
+                            if isinstance(v, (int, float)) and 0 < v < 65535]
+                    pw = m.get("current_socket_power")
+                    samples.append((time.perf_counter(), sum(clks) / len(clks) if clks else None,
+                                    float(pw) if isinstance(pw, (int, float)) and pw < 65535 else None))
+                except Exception:
+                    pass
+                time.sleep(0.02)
+
+        th = threading.Thread(target=sample, daemon=True)
+        th.start()
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(16):
+                fn()
+            torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        stop.set()
+        th.join()
+        keep = [x for x in samples if x[0] >= t0 + (t1 - t0) / 2]
+        clk = [x[1] for x in keep if x[1] is not None]
+        pw = [x[2] for x in keep if x[2] is not None]
+        return {"gfx_clock_mhz": round(statistics.median(clk), 1) if clk else None,
+                "socket_power_w": round(statistics.median(pw), 1) if pw else None,
+                "power_limit_w": limit_w, "samples": len(keep), "soak_s": round(t1 - t0, 2)}
+    except Exception:
+        return None
+    finally:
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:
+            pass
+
+
 def dense_setup(name, variant="float"):
     import torch
 
@@ -147,7 +219,7 @@ def measure_dense(name, steps, warmup):
     d = mg.mg_config_info(mg.mg_last_config())
     hbm_bytes = 2.0 * (c.M * c.K + c.K * c.N + c.M * c.N) + (2.0 * c.N if c.bias is not None else 0.0)
     return dict(case=c, flops=flops, wall=wall, kernel_ms=mean_ms, kernel_ms_median=med_ms, tile_config=d["name"],
-                kernel=kernel_name(d, c.K, c.N), compulsory_bytes=hbm_bytes)
+                kernel=kernel_name(d, c.K, c.N), compulsory_bytes=hbm_bytes, fn=fn)
 
 
 def kernel_name(d, K, N):
@@ -308,6 +380,15 @@ def main():
                      "kernel_ms_median": round(main_res["kernel_ms_median"], 4),
                      "kernel": "%s (%s)" % (main_res["kernel"], main_res["tile_config"])},
     }
+    # The chip lowers its clock to stay within its power limit; the same
+    # kernel's rate at the clock it actually ran at is the fraction of the
+    # matrix cores' peak scaled to that clock (256 CU x 4096 flop/clk).
+    tel = soak_telemetry(main_res["fn"])
+    line["telemetry"] = tel
+    if tel and tel.get("gfx_clock_mhz"):
+        peak_clk = 256 * 4096 * tel["gfx_clock_mhz"] * 1e6 / 1e12
+        line["roofline"]["peak_at_clock"] = round(peak_clk, 1)
+        line["roofline"]["frac_at_clock"] = round(achieved / peak_clk, 4)
     sys.stdout.flush()
     if not args.no_also:
         also = {}
