@@ -8,6 +8,14 @@
   section 2.1, which also fixes the order of got and ref) and no NaN / Inf;
 * a Freivalds screen of a whole output against a random +-1 vector, to catch
   missing or garbage tiles a sample could miss;
+* Higham's a-priori bound for floating-point summation (N. J. Higham,
+  "Accuracy and Stability of Numerical Algorithms", 2nd ed., section 3.1):
+  an fp32 sum of K exact products, in any order, is within
+  gamma_K * sum_k |a_ik||b_kj| of the exact value, gamma_n = n u / (1 - n u),
+  u = 2^-24; one rounding to the output type adds at most u_out |x|
+  (u_out = 2^-11 for fp16, 2^-8 for bf16) and, for fp16, half the subnormal
+  spacing 2^-25.  Far tighter than the 1e-2 gate on N(0,1)/sqrt(K) data, it
+  catches dropped or doubled k-blocks and a wrong output rounding;
 * the seeded 4096-element sample and the deterministic edge set.
 """
 from __future__ import annotations
@@ -71,6 +79,48 @@ def freivalds_rows(got_bits, A_f64, B_f64, dtype: int, seed: int = 0, atol: floa
     bound = N * atol + rtol * (np.abs(A_f64) @ np.abs(B_f64).sum(axis=1))
     bad = ~(np.isfinite(lhs) & (np.abs(lhs - rhs) <= bound))
     return np.flatnonzero(bad)
+
+
+U_F32 = 2.0 ** -24
+U_OUT = {F16: 2.0 ** -11, BF16: 2.0 ** -8}
+SUBNORMAL_FLOOR = {F16: 2.0 ** -25, BF16: 0.0}
+
+
+def gamma(n: int, u: float = U_F32) -> float:
+    """gamma_n = n u / (1 - n u), the summation constant (n u < 1)."""
+    assert n * u < 1.0
+    return n * u / (1.0 - n * u)
+
+
+def higham_bound(absdot, ref, K: int, dtype: int, abs_bias=None) -> np.ndarray:
+    """Bound on |got - ref| for an fp32-accumulated dot product of K exact
+    products, rounded once to `dtype`: (1 + u_out) E + u_out |ref| + floor with
+    E = gamma_K sum_k |a_k b_k| (gamma_{K+1} and + |bias| when an fp32 bias
+    add follows).  ReLU is 1-Lipschitz, so the bound carries through it."""
+    absdot = np.asarray(absdot, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if abs_bias is not None:
+        E = gamma(K + 1) * (absdot + np.asarray(abs_bias, dtype=np.float64))
+    else:
+        E = gamma(max(K, 1)) * absdot
+    u_out = U_OUT[dtype]
+    return (1.0 + u_out) * E + u_out * np.abs(ref) + SUBNORMAL_FLOOR[dtype]
+
+
+def higham_ratio(got_bits, ref, bound, dtype: int) -> float:
+    """max |got - ref| / bound over the elements (inf if any got is not finite)."""
+    got = to_f64(got_bits, dtype)
+    ref = np.asarray(ref, dtype=np.float64)
+    if got.size == 0:
+        return 0.0
+    if not np.all(np.isfinite(got)):
+        return float("inf")
+    return float(np.max(np.abs(got - ref) / np.asarray(bound, dtype=np.float64)))
+
+
+def abs_bits(bits) -> np.ndarray:
+    """|x| of fp16 / bf16 bit patterns (sign bit cleared)."""
+    return np.asarray(bits, dtype=np.uint16) & np.uint16(0x7FFF)
 
 
 def sample_positions(M: int, N: int, count: int, seed: int) -> tuple[np.ndarray, np.ndarray]:

@@ -4,9 +4,11 @@ Gates (oracle/compare.py): bit-exact for integer-valued inputs (the fp32
 accumulation of small integers is exact, so one rounding of the exact sum is
 the only correct output), |got - ref| <= 1e-2 + 1e-2 |ref| for random floats,
 unchanged guard bands around every output, and identical bits on a repeated
-call.  Small shapes compare every output element; the 8192^3 and grouped
-workloads compare the seeded 4096-element sample plus the edge set, and
-screen the whole output with Freivalds' check.
+call.  Random-float results must also lie inside Higham's bound for an fp32
+sum of exact products plus one output rounding.  Small shapes compare every
+output element; the 8192^3 and grouped workloads compare the seeded
+4096-element sample plus the edge set, and screen the whole output with
+Freivalds' check.
 """
 import numpy as np
 import pytest
@@ -72,6 +74,18 @@ def check_full(orc, case, cfg=-1, **kw):
         assert_bitexact(got, ref_q, case.dtype, case.name)
     else:
         assert_tolerance(got, ref, case.dtype, case.name)
+        absdot, _ = orc.gemm(compare.abs_bits(case.A), compare.abs_bits(case.B), case.dtype)
+        assert_higham(got, ref, absdot, case)
+
+
+def assert_higham(got, ref, absdot, case):
+    """Higham's fp32 summation bound (plus one output rounding) on every
+    checked element: tighter than the 1e-2 gate by orders of magnitude."""
+    bias = getattr(case, "bias", None)
+    abs_bias = None if bias is None else np.abs(compare.to_f64(bias, case.dtype))
+    bound = compare.higham_bound(absdot, ref, case.K, case.dtype, abs_bias=abs_bias)
+    ratio = compare.higham_ratio(got, ref, bound, case.dtype)
+    assert ratio <= 1.0, "%s: error exceeds the fp32 summation bound (max ratio %.3g)" % (case.name, ratio)
 
 
 # general-kernel shapes (K % 64 != 0 or N % 8 != 0) and direct-to-LDS shapes
@@ -172,6 +186,8 @@ def test_workload_8192_bf16_sampled(orc, variant):
         assert_bitexact(got[rows, cols], ref_q, c.dtype, name)
     else:
         assert_tolerance(got[rows, cols], ref, c.dtype, name)
+        absdot, _ = orc.gemm_sampled(compare.abs_bits(c.A), compare.abs_bits(c.B), c.dtype, rows, cols)
+        assert_higham(got[rows, cols], ref, absdot, c)
     bad = compare.freivalds_rows(got, compare.to_f64(c.A, c.dtype), compare.to_f64(c.B, c.dtype), c.dtype, seed=5)
     assert bad.size == 0, "Freivalds screen fails on rows %s" % bad[:10]
 
@@ -516,6 +532,8 @@ def test_workload_grouped_moe_sampled(orc, variant):
         assert_bitexact(got[rows, cols], ref_q, c.dtype, name)
     else:
         assert_tolerance(got[rows, cols], ref, c.dtype, name)
+        absdot, _ = orc.grouped_sampled(compare.abs_bits(c.X), compare.abs_bits(c.W), c.offsets, c.dtype, rows, cols)
+        assert_higham(got[rows, cols], ref, absdot, c)
     Xf = compare.to_f64(c.X, c.dtype)
     for e in range(c.E):
         r0, r1 = c.offsets[e], c.offsets[e + 1]
