@@ -98,8 +98,17 @@ __device__ __forceinline__ int swz_a(int row) {
     if constexpr (ACH == 8) return (row ^ (row >> 3)) & 7;
     else return (row >> 2) & 3;
 }
+// B: a transposing read takes 32 bytes from each of 4 consecutive k-rows;
+// the swizzle puts those 4 pieces in 4 distinct 64-byte windows of the
+// 256-byte bank row.  k-rows of 256 bytes or more all start a bank row, so
+// the window is krow % 4; 128-byte k-rows alternate between the two halves
+// of a bank row, so the window needs only (krow / 2) % 2.
 template <int BCH>
-__device__ __forceinline__ int swz_b(int krow) { return (4 * (krow & 3)) & (BCH - 1); }
+__device__ __forceinline__ int swz_b(int krow) {
+    static_assert(BCH >= 8, "k-rows of at least 128 bytes");
+    if constexpr (BCH == 8) return 4 * ((krow >> 1) & 1);
+    else return 4 * (krow & 3);
+}
 
 // The two operand layouts.  The MFMA wants, for each of 32 rows (of A) or
 // columns (of B), 8 consecutive k values per lane.

@@ -22,6 +22,8 @@ import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 COPY_BYTES = 256 * 1024 * 1024  # bytes read and bytes written by the probe's copy kernel
+SIMDS = 256 * 4                 # MI355X: 256 CUs of 4 SIMDs
+SHADER_ENGINES = 32             # 8 XCDs of 4 shader engines
 
 
 def source_hash() -> str:
@@ -122,6 +124,12 @@ def write_counters(dirs, out, cmd, kernel_key: str = "gemm_"):
             f.write("%s = %.6g\n" % (k, vals[k]))
         if "SQ_INSTS_MFMA" in vals and "SQ_VALU_MFMA_BUSY_CYCLES" in vals:
             f.write("mfma_busy_cycles_per_instruction = %.2f\n" % (vals["SQ_VALU_MFMA_BUSY_CYCLES"] / vals["SQ_INSTS_MFMA"]))
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in vals and "SQ_BUSY_CYCLES" in vals:
+            # MFMA busy cycles are summed over the 1024 SIMDs, SQ busy cycles
+            # over the 32 shader engines: the ratio of the per-unit means is
+            # the fraction of the kernel's cycles the matrix cores were busy
+            f.write("mfma_busy_fraction = %.4f\n" % ((vals["SQ_VALU_MFMA_BUSY_CYCLES"] / SIMDS) /
+                                                     (vals["SQ_BUSY_CYCLES"] / SHADER_ENGINES)))
         if "SQ_LDS_BANK_CONFLICT" in vals and "SQ_LDS_IDX_ACTIVE" in vals:
             f.write("lds_bank_conflict_ratio = %.4f\n" % (vals["SQ_LDS_BANK_CONFLICT"] / max(vals["SQ_LDS_IDX_ACTIVE"], 1)))
         if "TCC_HIT_sum" in vals and "TCC_MISS_sum" in vals:
