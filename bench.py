@@ -21,7 +21,7 @@ Beside the main figure the line carries:
                 fp16) and attention scores Q K^T (128 heads, 2048 x 2048,
                 d = 128, bf16; bound by writing the 1 GiB of scores).
 
-Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 50] [--no-cpu-baseline] [--no-also]
+Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 50] [--no-cpu-baseline] [--no-also] [--no-telemetry]
 """
 from __future__ import annotations
 
@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--workload", default="gemm_8192_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-also", action="store_true")
+    ap.add_argument("--no-telemetry", action="store_true",
+                    help="skip the clock/power soak after the timed region (profiled runs: keeps the timed calls last)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the CPU-baseline sample")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="for counter collection: one GEMM, a plain copy of known size, one GEMM; no timing")
@@ -383,7 +385,7 @@ def main():
     # The chip lowers its clock to stay within its power limit; the same
     # kernel's rate at the clock it actually ran at is the fraction of the
     # matrix cores' peak scaled to that clock (256 CU x 4096 flop/clk).
-    tel = soak_telemetry(main_res["fn"])
+    tel = None if args.no_telemetry else soak_telemetry(main_res["fn"])
     line["telemetry"] = tel
     if tel and tel.get("gfx_clock_mhz"):
         peak_clk = 256 * 4096 * tel["gfx_clock_mhz"] * 1e6 / 1e12
