@@ -155,6 +155,27 @@ def test_workload_bias_relu_1024x1024x2048_f16(orc, variant):
     check_full(orc, inputs.dense_workload("gemm_bias_relu_1024x1024x2048_f16", variant))
 
 
+@pytest.mark.parametrize("dtype", [F16, BF16])
+def test_bias_relu_with_unaligned_bias(orc, dtype):
+    # the fast kernel loads the bias before its K loop in 8-byte pieces when
+    # the bias is 8-byte aligned; a bias one element into its buffer takes
+    # the element-by-element epilogue instead
+    import torch
+
+    c = inputs.integer_dense(320, 264, 256, dtype, 515, epilogue=True, name="bias_unaligned")
+    announce("dense bias one element off alignment dt=%d" % dtype)
+    buf = torch.zeros(c.N + 8, dtype=torch.float16 if dtype == F16 else torch.bfloat16, device="cuda")
+    buf[1:c.N + 1] = to_dev(c.bias, dtype)
+    bias = buf[1:c.N + 1]
+    assert bias.data_ptr() % 8 != 0
+    out = Guarded(c.M, c.N, dtype)
+    mg.mg_gemm_bias_relu(to_dev(c.A, dtype), to_dev(c.B, dtype), bias, out=out.mat)
+    torch.cuda.synchronize()
+    assert out.guards_intact()
+    _, ref_q = orc.gemm(c.A, c.B, dtype, bias=c.bias, relu=True)
+    assert_bitexact(out.result(), ref_q, dtype, c.name)
+
+
 def test_rounding_ties_to_even_in_bf16_and_f16(orc):
     # sums of entries in 1..4 over K=2048 land far above 256 (bf16) and 2048
     # (fp16), where many exact sums fall on ties of the output spacing

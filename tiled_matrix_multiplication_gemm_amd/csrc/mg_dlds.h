@@ -516,6 +516,27 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
     const int64_t wave_rows = M - m0 - wm * Cfg::WTM;
     const int live = __builtin_amdgcn_readfirstlane(
         (int)(wave_rows >= Cfg::WTM ? FM : (wave_rows <= 0 ? 0 : (wave_rows + 31) / 32)));
+    // Fused epilogue: the bias values of this lane's output columns are
+    // loaded before the K loop, so their latency is not paid at the end.
+    // Lane l's columns in block j are, for group q, the 4 adjacent columns
+    // j*32 + 4 (l / 32) + 8 q: one 8-byte load each when the bias is 8-byte
+    // aligned (N % 8 == 0 here, so a group lies wholly inside or outside N);
+    // otherwise the epilogue reads the bias element by element.  Loads older
+    // than the ring's only make its waits stricter.
+    [[maybe_unused]] u32x2 bias_v[FN][4];
+    [[maybe_unused]] bool bias_pre = false;
+    if constexpr (EPI) {
+        bias_pre = ((uintptr_t)args.bias & 7) == 0;
+        if (bias_pre) {
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t col = n0 + wn * Cfg::WTN + j * 32 + 4 * (lane >> 5) + 8 * q;
+                    bias_v[j][q] = col < N ? *(const u32x2*)(args.bias + col) : u32x2{0u, 0u};
+                }
+        }
+    }
     if (live == FM) main_loop(std::integral_constant<int, FM>{});
     else main_loop(live);
 
@@ -531,13 +552,15 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
     // One 32x32 tile at a time (a scheduling barrier keeps the compiler from
     // pulling every accumulator out at once); interior tiles skip the checks.
     const bool interior = (m0 + BM <= M) && (n0 + BN <= N);
-    auto pack4 = [&](const f32x16& c, int q, int64_t col) -> u32x2 {
+    auto pack4 = [&](const f32x16& c, int j, int q, int64_t col) -> u32x2 {
         float v[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             v[t] = c[4 * q + t];
             if constexpr (EPI) {
-                const float bt = (col + t < N) ? to_float<DT>(args.bias[col + t]) : 0.0f;
+                const uint16_t pre = (uint16_t)(bias_v[j][q][t >> 1] >> (16 * (t & 1)));
+                const float bt = bias_pre ? to_float<DT>(pre)
+                                          : ((col + t < N) ? to_float<DT>(args.bias[col + t]) : 0.0f);
                 v[t] = v[t] + bt;
                 v[t] = (v[t] > 0.0f) ? v[t] : 0.0f;
             }
@@ -584,7 +607,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int c = cl + 8 * q;
-                    const u32x2 w = pack4(acc[i][j], q, n0 + wn * Cfg::WTN + c);
+                    const u32x2 w = pack4(acc[i][j], j, q, n0 + wn * Cfg::WTN + c);
                     *(lds_u32x2_t*)(stage + row * RB + ((c >> 3) ^ stage_swz(row)) * 16 + (c & 7) * 2) = w;
                 }
             }
@@ -612,7 +635,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
                 uint16_t* cp = Cg + row * args.ldc + col0;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const u32x2 w = pack4(acc[i][j], q, col0 + 8 * q);
+                    const u32x2 w = pack4(acc[i][j], j, q, col0 + 8 * q);
                     if (row_ok && (interior || col0 + 8 * q < N)) *(u32x2*)(cp + 8 * q) = w;
                 }
             }
