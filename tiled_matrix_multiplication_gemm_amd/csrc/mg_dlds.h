@@ -254,8 +254,10 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
 
     // ---- which tile (same order as the general kernel) --------------------
     int total = (int)gridDim.x;
+    [[maybe_unused]] GroupOffsets go{0, false};
     if constexpr (MODE == MODE_GROUPED) {
-        total = grouped_tiles<BM>(args);
+        go = load_group_offsets(args);
+        total = grouped_tiles<BM>(args, go);
         if ((int)blockIdx.x >= total) return;
     }
     int logical = args.xcd_remap ? xcd_logical(blockIdx.x, total) : (int)blockIdx.x;
@@ -267,7 +269,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
     int split = 0;  // split-K: which K range (workgroups of one split are contiguous)
     if constexpr (MODE == MODE_GROUPED) {
         int e, r0, rows;
-        if (!grouped_tile<BM>(args, logical, e, r0, rows, pm, pn)) return;
+        if (!grouped_tile<BM>(args, go, logical, e, r0, rows, pm, pn)) return;
         M = rows;
         Ag += (int64_t)r0 * args.lda;
         Bg += (int64_t)e * args.stride_we;

@@ -68,29 +68,45 @@ struct KArgs {
 // grouped_tiles() counts the tiles: the host sizes the grid for the worst
 // case (it does not read the device offsets), and the XCD renumbering must
 // spread the real tiles, not the grid, over the 8 XCDs.
-template <int BM>
-__device__ __forceinline__ int grouped_tiles(const KArgs& args) {
+//
+// The offsets as a wave reads them: with fewer than 64 experts one vector
+// load puts offsets[e] in lane e and every lookup below is a v_readlane, so
+// the walk over the experts waits on memory once instead of once per expert.
+struct GroupOffsets {
+    int v;          // lane e: offsets[e] (when in_lanes)
+    bool in_lanes;  // E < 64
+};
+__device__ __forceinline__ GroupOffsets load_group_offsets(const KArgs& args) {
+    GroupOffsets g;
+    g.in_lanes = args.E < 64;
+    const int lane = (int)(threadIdx.x & 63);
+    g.v = (g.in_lanes && lane <= args.E) ? args.offsets[lane] : 0;
+    return g;
+}
+// The walk over the experts, with `off(e)` giving offsets[e].
+template <int BM, class Off>
+__device__ __forceinline__ int grouped_tiles_walk(const KArgs& args, Off off) {
     const int T = (int)args.M;
     int total = 0;
-    int a = args.offsets[0];
+    int a = off(0);
     a = a < 0 ? 0 : (a > T ? T : a);
     for (int e = 0; e < args.E; ++e) {
-        int b = args.offsets[e + 1];
+        int b = off(e + 1);
         b = b < a ? a : (b > T ? T : b);
         total += (b - a + BM - 1) / BM;
         a = b;
     }
     return total * args.tiles_n;
 }
-template <int BM>
-__device__ __forceinline__ bool grouped_tile(const KArgs& args, int logical, int& e, int& r0, int& rows, int& pm,
-                                             int& pn) {
+template <int BM, class Off>
+__device__ __forceinline__ bool grouped_tile_walk(const KArgs& args, Off off, int logical, int& e, int& r0,
+                                                  int& rows, int& pm, int& pn) {
     const int T = (int)args.M;
     int base = 0;
-    int a = args.offsets[0];
+    int a = off(0);
     a = a < 0 ? 0 : (a > T ? T : a);
     for (e = 0; e < args.E; ++e) {
-        int b = args.offsets[e + 1];
+        int b = off(e + 1);
         b = b < a ? a : (b > T ? T : b);
         const int mt = (b - a + BM - 1) / BM;
         const int cnt = mt * args.tiles_n;
@@ -106,6 +122,21 @@ __device__ __forceinline__ bool grouped_tile(const KArgs& args, int logical, int
         a = b;
     }
     return false;
+}
+// One walk per source of the offsets, chosen outside the loop (a select
+// inside it would issue the memory load on every step anyway).
+template <int BM>
+__device__ __forceinline__ int grouped_tiles(const KArgs& args, const GroupOffsets& go) {
+    if (go.in_lanes) return grouped_tiles_walk<BM>(args, [&](int e) { return __builtin_amdgcn_readlane(go.v, e); });
+    return grouped_tiles_walk<BM>(args, [&](int e) { return args.offsets[e]; });
+}
+template <int BM>
+__device__ __forceinline__ bool grouped_tile(const KArgs& args, const GroupOffsets& go, int logical, int& e, int& r0,
+                                             int& rows, int& pm, int& pn) {
+    if (go.in_lanes)
+        return grouped_tile_walk<BM>(args, [&](int i) { return __builtin_amdgcn_readlane(go.v, i); }, logical, e, r0,
+                                     rows, pm, pn);
+    return grouped_tile_walk<BM>(args, [&](int i) { return args.offsets[i]; }, logical, e, r0, rows, pm, pn);
 }
 
 template <int BM_, int BN_, int BK_, int WM_, int WN_>
@@ -223,8 +254,10 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_tile_kernel(const KArgs args) {
 
     // ---- which tile -------------------------------------------------------
     int total = (int)gridDim.x;
+    [[maybe_unused]] GroupOffsets go{0, false};
     if constexpr (MODE == MODE_GROUPED) {
-        total = grouped_tiles<BM>(args);
+        go = load_group_offsets(args);
+        total = grouped_tiles<BM>(args, go);
         if ((int)blockIdx.x >= total) return;
     }
     int logical = args.xcd_remap ? xcd_logical(blockIdx.x, total) : (int)blockIdx.x;
@@ -235,7 +268,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_tile_kernel(const KArgs args) {
     int pm, pn;
     if constexpr (MODE == MODE_GROUPED) {
         int e, r0, rows;
-        if (!grouped_tile<BM>(args, logical, e, r0, rows, pm, pn)) return;
+        if (!grouped_tile<BM>(args, go, logical, e, r0, rows, pm, pn)) return;
         M = rows;
         Ag += (int64_t)r0 * args.lda;
         Bg += (int64_t)e * args.stride_we;
