@@ -529,15 +529,13 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
     [[maybe_unused]] bool bias_pre = false;
     if constexpr (EPI) {
         bias_pre = ((uintptr_t)args.bias & 7) == 0;
-        if (bias_pre) {
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int64_t col = n0 + wn * Cfg::WTN + j * 32 + 4 * (lane >> 5) + 8 * q;
-                    bias_v[j][q] = col < N ? *(const u32x2*)(args.bias + col) : u32x2{0u, 0u};
-                }
-        }
+            for (int q = 0; q < 4; ++q) {
+                const int64_t col = n0 + wn * Cfg::WTN + j * 32 + 4 * (lane >> 5) + 8 * q;
+                bias_v[j][q] = (bias_pre && col < N) ? *(const u32x2*)(args.bias + col) : u32x2{0u, 0u};
+            }
     }
     if (live == FM) main_loop(std::integral_constant<int, FM>{});
     else main_loop(live);
