@@ -580,6 +580,25 @@ def test_grouped_skewed_counts_full(orc, dtype, K):
             assert_tolerance(out.result(), ref, dtype, "grouped skewed")
 
 
+@pytest.mark.parametrize("E", [63, 64, 100])
+@pytest.mark.parametrize("K", [128, 72])
+def test_grouped_many_experts(orc, E, K):
+    # below 64 experts the kernels read the offsets from lanes of one vector
+    # load, from 64 on one by one from memory: both walks, on the fast (K =
+    # 128) and the general (K = 72) kernel, with empty and ragged experts
+    rng = np.random.default_rng(E)
+    counts = rng.integers(0, 40, size=E)
+    counts[::7] = 0
+    counts[3] = 257
+    c = inputs.random_grouped(E=E, T=int(counts.sum()), K=K, N=136, dtype=BF16, seed=E + K, counts=counts,
+                              integer=True)
+    announce("grouped E=%d K=%d T=%d" % (E, K, c.T))
+    out = run_grouped(c)
+    assert out.guards_intact()
+    _, ref_q = orc.grouped_gemm(c.X, c.W, c.offsets, BF16)
+    assert_bitexact(out.result(), ref_q, BF16, "grouped E %d K %d" % (E, K))
+
+
 def test_grouped_every_config(orc):
     counts = np.array([5, 0, 130, 67, 1])
     for K in (72, 192):
