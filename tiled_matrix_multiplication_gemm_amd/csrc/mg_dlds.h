@@ -591,6 +591,12 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
         constexpr int CH = Cfg::WTN / 8;  // 16-byte chunks per staged row
         constexpr int RB = Cfg::WTN * 2;  // bytes per staged row
         auto stage_swz = [](int row) { return (row ^ (row >> 3)) & (CH - 1); };
+        // The 32 lanes one ds_write_b64 serves together hold rows 0..31 of a
+        // block at the same 8-byte half of their chunks; swapping the halves
+        // of every other group of rows (bit HS of the row) puts them in
+        // distinct banks.  The read-back swaps them back.
+        constexpr int HS = CH == 4 ? 2 : 4;
+        auto stage_half = [](int row) { return (row >> HS) & 1; };
         wait_vmcnt<0>();
         ring_barrier();  // every wave is out of the K loop: the ring is free
         char* stage = nullptr;
@@ -608,7 +614,8 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
                 for (int q = 0; q < 4; ++q) {
                     const int c = cl + 8 * q;
                     const u32x2 w = pack4(acc[i][j], j, q, n0 + wn * Cfg::WTN + c);
-                    *(lds_u32x2_t*)(stage + row * RB + ((c >> 3) ^ stage_swz(row)) * 16 + (c & 7) * 2) = w;
+                    *(lds_u32x2_t*)(stage + row * RB + ((c >> 3) ^ stage_swz(row)) * 16 +
+                                    (((c & 7) * 2) ^ (8 * stage_half(row)))) = w;
                 }
             }
         }
@@ -619,7 +626,8 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
 #pragma unroll
         for (int it = 0; it < Cfg::WTM / ROWS_PER_LOAD; ++it) {
             const int row = it * ROWS_PER_LOAD + rsub;
-            const u32x4 w = *(const lds_u32x4_t*)(stage + row * RB + (ch ^ stage_swz(row)) * 16);
+            u32x4 w = *(const lds_u32x4_t*)(stage + row * RB + (ch ^ stage_swz(row)) * 16);
+            if (stage_half(row)) w = u32x4{w[2], w[3], w[0], w[1]};
             const int64_t grow = m0 + wm * Cfg::WTM + row;
             if (interior || (grow < M && col < N)) *(u32x4*)(Cg + grow * args.ldc + col) = w;
         }
