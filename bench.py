@@ -12,6 +12,8 @@ Beside the main figure the line carries:
                 that peak scaled to the graphics clock the chip ran at);
   telemetry     graphics clock and socket power (amdsmi) over a short soak
                 of the same call after the timed region;
+  cold_*        kernel time (median, p90) with the caches flushed by a
+                512 MiB write before each call (not with --no-also);
   cpu_baseline  the CPU oracle timed on this host on a bounded sample of the
                 same workload (whole output rows), scaled to TFLOP/s;
   also          the same measurement for the 1024x1024x2048 fp16 GEMM, its
@@ -22,6 +24,7 @@ Beside the main figure the line carries:
                 d = 128, bf16; bound by writing the 1 GiB of scores).
 
 Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 50] [--no-cpu-baseline] [--no-also] [--no-telemetry]
+                      [--no-cold]
 """
 from __future__ import annotations
 
@@ -49,6 +52,7 @@ def parse():
     ap.add_argument("--workload", default="gemm_8192_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-also", action="store_true")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache timings")
     ap.add_argument("--no-telemetry", action="store_true",
                     help="skip the clock/power soak after the timed region (profiled runs: keeps the timed calls last)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the CPU-baseline sample")
@@ -124,6 +128,30 @@ def time_calls(fn, steps: int, warmup: int):
     wall = time.perf_counter() - t0
     per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
     return wall, sum(per) / len(per), per[len(per) // 2]
+
+
+FLUSH_BYTES = 512 * 1024 * 1024  # more than the 256 MB last-level cache plus the 8 x 4 MB L2
+
+
+def time_cold(fn, reps: int):
+    """Kernel time with cold caches: before each timed call a 512 MiB buffer
+    is written, evicting the last-level cache and every L2, so the operands
+    come from HBM.  Returns (median, p90) in ms of the HIP-event times."""
+    import torch
+
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    fn()
+    for i in range(reps):
+        flush.fill_(float(i))
+        starts[i].record()
+        fn()
+        ends[i].record()
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in zip(starts, ends))
+    del flush
+    return per[len(per) // 2], per[min(len(per) - 1, (9 * len(per)) // 10)]
 
 
 def soak_telemetry(fn, seconds: float = 1.6):
@@ -256,7 +284,7 @@ def measure_grouped(name, steps, warmup):
     hbm_bytes = 2.0 * (c.T * c.K + c.E * c.K * c.N + c.T * c.N) + 4.0 * (c.E + 1)
     cfg = mg.mg_config_info(mg.mg_last_config())["name"]
     return dict(case=c, flops=flops, wall=wall, kernel_ms=mean_ms, kernel_ms_median=med_ms, tile_config=cfg,
-                compulsory_bytes=hbm_bytes)
+                compulsory_bytes=hbm_bytes, fn=fn)
 
 
 def cpu_baseline(case, target_s: float):
@@ -386,6 +414,10 @@ def main():
     # kernel's rate at the clock it actually ran at is the fraction of the
     # matrix cores' peak scaled to that clock (256 CU x 4096 flop/clk).
     tel = None if args.no_telemetry else soak_telemetry(main_res["fn"])
+    if not args.no_also and not args.no_cold:
+        cmed, cp90 = time_cold(main_res["fn"], 20)
+        line["roofline"]["cold_kernel_ms_median"] = round(cmed, 4)
+        line["roofline"]["cold_kernel_ms_p90"] = round(cp90, 4)
     line["telemetry"] = tel
     if tel and tel.get("gfx_clock_mhz"):
         peak_clk = 256 * 4096 * tel["gfx_clock_mhz"] * 1e6 / 1e12
@@ -397,9 +429,11 @@ def main():
         for name in ("gemm_1024x1024x2048_f16", "gemm_bias_relu_1024x1024x2048_f16"):
             r = measure_dense(name, max(args.steps, 50), max(args.warmup, 10))
             ach = r["flops"] / (r["kernel_ms"] * 1e-3) / 1e12
+            cmed, cp90 = (None, None) if args.no_cold else time_cold(r["fn"], 100)
             also[name] = {"tflops": round(r["flops"] * max(args.steps, 50) / r["wall"] / 1e12, 2),
                           "kernel_tflops": round(ach, 2), "frac_mfma_peak": round(ach / PEAK_MFMA_TFLOPS, 4),
-                          "kernel_ms_mean": round(r["kernel_ms"], 5), "tile_config": r["tile_config"]}
+                          "kernel_ms_mean": round(r["kernel_ms"], 5), "tile_config": r["tile_config"],
+                          "cold_kernel_ms_median": cmed and round(cmed, 5), "cold_kernel_ms_p90": cp90 and round(cp90, 5)}
         gname = "grouped_moe_e32_t8192_k1024_n4096_f16"
         r = measure_grouped(gname, args.steps, args.warmup)
         ach = r["flops"] / (r["kernel_ms"] * 1e-3) / 1e12
@@ -408,6 +442,10 @@ def main():
                        "kernel_tflops": round(ach, 2), "frac_mfma_peak": round(ach / PEAK_MFMA_TFLOPS, 4),
                        "hbm_gbs_compulsory": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
                        "kernel_ms_mean": round(r["kernel_ms"], 5), "tile_config": r["tile_config"]}
+        if not args.no_cold:
+            cmed, cp90 = time_cold(r["fn"], 20)
+            also[gname]["cold_kernel_ms_median"] = round(cmed, 5)
+            also[gname]["cold_kernel_ms_p90"] = round(cp90, 5)
         also.update(measure_consumers(min(args.steps, 50), min(args.warmup, 10)))
         line["also"] = also
     if not args.no_cpu_baseline:
