@@ -137,11 +137,17 @@ def _bits(a) -> np.ndarray:
     return a
 
 
+MAX_THREADS = 16  # a GPU host's CPU share per GPU; more cores than this are not ours to use
+
+
 def default_threads() -> int:
+    """Threads for the full-output oracle: the cores this process may run on,
+    at most MAX_THREADS."""
     try:
-        return max(1, len(os.sched_getaffinity(0)))
+        n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        return max(1, os.cpu_count() or 1)
+        n = os.cpu_count() or 1
+    return max(1, min(MAX_THREADS, n))
 
 
 def decode(bits, dtype: int) -> np.ndarray:

@@ -6,8 +6,6 @@
 * tolerance check |got - ref| <= atol + rtol*|ref| with ref the unrounded fp64
   oracle value, atol = rtol = 1e-2 for fp16 / bf16 ("Triton study notes",
   section 2.1, which also fixes the order of got and ref) and no NaN / Inf;
-* a Freivalds screen of a whole output against a random +-1 vector, to catch
-  missing or garbage tiles a sample could miss;
 * Higham's a-priori bound for floating-point summation (N. J. Higham,
   "Accuracy and Stability of Numerical Algorithms", 2nd ed., section 3.1):
   an fp32 sum of K exact products, in any order, is within
@@ -60,25 +58,6 @@ def describe(idx, got_bits, ref, dtype, shape=None, limit=5) -> str:
         pos = np.unravel_index(i, shape) if shape is not None else i
         lines.append("  at %s: got %r ref %r" % (pos, got[i], ref[i]))
     return "\n".join(lines)
-
-
-def freivalds_rows(got_bits, A_f64, B_f64, dtype: int, seed: int = 0, atol: float = 1e-2, rtol: float = 1e-2,
-                   bias_f64=None) -> np.ndarray:
-    """Rows i failing |sum_j r_j got_ij - sum_k a_ik (B r)_k| <= N*atol + rtol*sum_k|a_ik| sum_j|b_kj|.
-
-    Implied by the per-element tolerance (for ReLU-free outputs); cheap enough
-    for a whole 8192 x 8192 output.  bias_f64 adds sum_j r_j bias_j to the
-    reference side."""
-    got = to_f64(got_bits, dtype)
-    N = got.shape[1]
-    r = np.random.default_rng(seed).choice(np.array([-1.0, 1.0]), size=N)
-    lhs = got @ r
-    rhs = A_f64 @ (B_f64 @ r)
-    if bias_f64 is not None:
-        rhs = rhs + float(bias_f64 @ r)
-    bound = N * atol + rtol * (np.abs(A_f64) @ np.abs(B_f64).sum(axis=1))
-    bad = ~(np.isfinite(lhs) & (np.abs(lhs - rhs) <= bound))
-    return np.flatnonzero(bad)
 
 
 U_F32 = 2.0 ** -24

@@ -344,3 +344,15 @@ def test_conv_workspace_follows_a_forced_row(L):
     finally:
         L.mg_set_config(-1)
     assert L.mg_conv2d_workspace_bytes(ctypes.byref(shape()), F16) == 0
+
+
+def test_binding_refuses_host_tensors_before_any_call():
+    """Host tensors never reach the library: the binding raises first."""
+    import torch
+
+    a, b = torch.zeros(8, 8, dtype=torch.float16), torch.zeros(8, 8, dtype=torch.float16)
+    for fn in (lambda: mg.mg_gemm(a, b), lambda: mg.mg_gemm_bias_relu(a, b, torch.zeros(8, dtype=torch.float16)),
+               lambda: mg.mg_gemm_splitk(a, b, splits=2), lambda: mg.mg_gemm_batched(a[None], b[None]),
+               lambda: mg.mg_attention_scores(a[None], b[None])):
+        with pytest.raises(RuntimeError, match="GPU tensors only"):
+            fn()

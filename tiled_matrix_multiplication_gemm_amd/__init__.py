@@ -145,9 +145,32 @@ def _stream(t):
 
 
 def _require_gpu(*ts):
+    """Every tensor on the GPU, all on the first one's device."""
     for t in ts:
         if not t.is_cuda:
             raise RuntimeError("mi355gemm operates on GPU tensors only (got a %s tensor)" % t.device)
+    for t in ts[1:]:
+        if t.device != ts[0].device:
+            raise RuntimeError("MG_ERR_INVALID_ARG: tensors on different devices (%s, %s)" % (ts[0].device, t.device))
+
+
+def _same_dtype(ref, *ts):
+    for t in ts:
+        if t.dtype != ref.dtype:
+            raise RuntimeError("MG_ERR_UNSUPPORTED_DTYPE: operands must share one dtype (%s, %s)" % (ref.dtype, t.dtype))
+
+
+def _check_out(out, shape, like):
+    """A caller-supplied output: the exact shape, like's dtype and device,
+    and a unit inner stride (the C ABI sees only a pointer and row strides,
+    so a smaller or differently typed buffer would be overrun or misread)."""
+    _require_gpu(like, out)
+    if tuple(out.shape) != tuple(shape):
+        raise RuntimeError("MG_ERR_INVALID_ARG: out has shape %s, expected %s" % (tuple(out.shape), tuple(shape)))
+    if out.dtype != like.dtype:
+        raise RuntimeError("MG_ERR_UNSUPPORTED_DTYPE: out is %s, expected %s" % (out.dtype, like.dtype))
+    if shape[-1] > 1 and out.stride(-1) != 1:
+        raise RuntimeError("MG_ERR_UNSUPPORTED_LAYOUT: out needs a unit inner stride")
 
 
 def mg_gemm(a, b, out=None):
@@ -159,8 +182,10 @@ def mg_gemm(a, b, out=None):
     K2, N = b.shape
     if K2 != K:
         raise RuntimeError("MG_ERR_INVALID_ARG: inner dimensions differ (%d vs %d)" % (K, K2))
+    _same_dtype(a, b)
     if out is None:
         out = torch.empty((M, N), dtype=a.dtype, device=a.device)
+    _check_out(out, (M, N), a)
     _check(lib().mg_gemm(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, a.stride(0), a.stride(1),
                          b.stride(0), b.stride(1), out.stride(0), out.stride(1), _dtype_code(a), _dtype_code(out),
                          _stream(a)))
@@ -176,10 +201,10 @@ def mg_gemm_bias_relu(a, b, bias, out=None):
     K2, N = b.shape
     if K2 != K or bias.shape != (N,) or (N > 1 and bias.stride(0) != 1):
         raise RuntimeError("MG_ERR_INVALID_ARG: shapes a[M,K], b[K,N], contiguous bias[N] expected")
-    if bias.dtype != a.dtype:
-        raise RuntimeError("MG_ERR_UNSUPPORTED_DTYPE: bias must have the output dtype")
+    _same_dtype(a, b, bias)
     if out is None:
         out = torch.empty((M, N), dtype=a.dtype, device=a.device)
+    _check_out(out, (M, N), a)
     _check(lib().mg_gemm_bias_relu(a.data_ptr(), b.data_ptr(), bias.data_ptr(), out.data_ptr(), M, N, K,
                                    a.stride(0), a.stride(1), b.stride(0), b.stride(1), out.stride(0),
                                    out.stride(1), _dtype_code(a), _dtype_code(out), _stream(a)))
@@ -198,8 +223,10 @@ def mg_gemm_batched(a, b, out=None):
         raise RuntimeError("MG_ERR_INVALID_ARG: a[batch,M,K] and b[batch,K,N] expected")
     batch, M, K = a.shape
     N = b.shape[2]
+    _same_dtype(a, b)
     if out is None:
         out = torch.empty((batch, M, N), dtype=a.dtype, device=a.device)
+    _check_out(out, (batch, M, N), a)
     _check(lib().mg_gemm_batched(a.data_ptr(), b.data_ptr(), out.data_ptr(), batch, M, N, K, a.stride(1),
                                  a.stride(2), b.stride(1), b.stride(2), out.stride(1), out.stride(2), a.stride(0),
                                  b.stride(0), out.stride(0), _dtype_code(a), _dtype_code(out), _stream(a)))
@@ -226,13 +253,18 @@ def mg_gemm_splitk(a, b, splits: int | None = None, workspace=None, out=None):
     K2, N = b.shape
     if K2 != K:
         raise RuntimeError("MG_ERR_INVALID_ARG: inner dimensions differ (%d vs %d)" % (K, K2))
+    _same_dtype(a, b)
     if out is None:
         out = torch.empty((M, N), dtype=a.dtype, device=a.device)
+    _check_out(out, (M, N), a)
     if splits is None:
         splits = mg_splitk_choose(M, N, K)
     need = mg_splitk_workspace_bytes(M, N, splits)
     if workspace is None:
         workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=a.device)
+    _require_gpu(a, workspace)
+    if not workspace.is_contiguous():
+        raise RuntimeError("MG_ERR_INVALID_ARG: the workspace must be contiguous")
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib().mg_gemm_splitk(a.data_ptr(), b.data_ptr(), out.data_ptr(), workspace.data_ptr(), ws_bytes, splits,
                                 M, N, K, a.stride(0), a.stride(1), b.stride(0), b.stride(1), out.stride(0),
@@ -257,6 +289,7 @@ def mg_grouped_gemm(x, w, offsets, out=None):
         raise RuntimeError("MG_ERR_UNSUPPORTED_DTYPE: x and w must share a dtype")
     if out is None:
         out = torch.empty((T, N), dtype=x.dtype, device=x.device)
+    _check_out(out, (T, N), x)
     if x.stride(1) != 1 and K > 1 or out.stride(1) != 1 and N > 1:
         raise RuntimeError("MG_ERR_UNSUPPORTED_LAYOUT: unit inner strides required")
     _check(lib().mg_grouped_gemm(x.data_ptr(), w.data_ptr(), out.data_ptr(), offsets.data_ptr(), E, T, N, K,
@@ -280,6 +313,9 @@ def mg_prepack_a(a, BK: int, out=None):
     M, K = a.shape
     if out is None:
         out = torch.empty(((K + BK - 1) // BK, M, BK), dtype=a.dtype, device=a.device)
+    _check_out(out, ((K + BK - 1) // BK, M, BK), a)
+    if not out.is_contiguous():
+        raise RuntimeError("MG_ERR_UNSUPPORTED_LAYOUT: the packed output must be contiguous")
     if a.stride(1) != 1 and K > 1:
         raise RuntimeError("MG_ERR_UNSUPPORTED_LAYOUT: unit inner stride required")
     _check(lib().mg_prepack_a(a.data_ptr(), out.data_ptr(), M, K, a.stride(0), BK, _dtype_code(a), _stream(a)))
@@ -294,8 +330,12 @@ def mg_gemm_prepacked(ap, BK: int, b, M: int, K: int, out=None):
     K2, N = b.shape
     if K2 != K:
         raise RuntimeError("MG_ERR_INVALID_ARG: inner dimensions differ")
+    _same_dtype(b, ap)
+    if not ap.is_contiguous() or ap.numel() < (K + BK - 1) // BK * M * BK:
+        raise RuntimeError("MG_ERR_INVALID_ARG: ap must be a contiguous packed [ceil(K/BK), M, BK] tensor")
     if out is None:
         out = torch.empty((M, N), dtype=b.dtype, device=b.device)
+    _check_out(out, (M, N), b)
     _check(lib().mg_gemm_prepacked(ap.data_ptr(), BK, b.data_ptr(), out.data_ptr(), M, N, K, b.stride(0),
                                    b.stride(1), out.stride(0), out.stride(1), _dtype_code(b), _stream(b)))
     return out
@@ -365,6 +405,7 @@ def mg_im2col(x, kernel, stride=1, pad=0, dil=1, ld: int | None = None, out=None
     M = shape.batch * oh * ow
     if out is None:
         out = torch.empty((M, ld), dtype=x.dtype, device=x.device)
+    _check_out(out, (M, ld), x)
     if out.shape != (M, ld) or not out.is_contiguous():
         raise RuntimeError("MG_ERR_INVALID_ARG: out must be a contiguous [%d, %d] tensor" % (M, ld))
     _check(lib().mg_im2col(ctypes.byref(shape), x.data_ptr(), out.data_ptr(), ld, _dtype_code(x), _stream(x)))
@@ -401,12 +442,17 @@ def mg_conv2d(x, w, stride=1, pad=0, dil=1, bias=None, weight_layout: str = "hwi
             raise RuntimeError("MG_ERR_INVALID_ARG: contiguous bias[OC] of x's dtype expected")
     if out is None:
         out = torch.empty((shape.batch, oh, ow, OC), dtype=x.dtype, device=x.device)
+    _check_out(out, (shape.batch, oh, ow, OC), x)
     if tuple(out.shape) != (shape.batch, oh, ow, OC) or not out.is_contiguous():
         raise RuntimeError("MG_ERR_INVALID_ARG: out must be a contiguous [%d, %d, %d, %d] tensor"
                            % (shape.batch, oh, ow, OC))
     need = mg_conv2d_workspace_bytes(shape, _dtype_code(x))
     if workspace is None and need > 0:
         workspace = torch.empty((need,), dtype=torch.uint8, device=x.device)
+    if workspace is not None:
+        _require_gpu(x, workspace)
+        if not workspace.is_contiguous():
+            raise RuntimeError("MG_ERR_INVALID_ARG: the workspace must be contiguous")
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().mg_conv2d(ctypes.byref(shape), x.data_ptr(), w.data_ptr(), swk, swn,
@@ -431,6 +477,7 @@ def mg_attention_scores(q, k, out=None):
         raise RuntimeError("MG_ERR_UNSUPPORTED_LAYOUT: unit stride along d and one dtype required")
     if out is None:
         out = torch.empty((H, Lq, Lk), dtype=q.dtype, device=q.device)
+    _check_out(out, (H, Lq, Lk), q)
     _check(lib().mg_attention_scores(q.data_ptr(), k.data_ptr(), out.data_ptr(), H, Lq, Lk, d, q.stride(0),
                                      q.stride(1), k.stride(0), k.stride(1), out.stride(0), out.stride(1),
                                      _dtype_code(q), _stream(q)))
