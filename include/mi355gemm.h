@@ -154,6 +154,29 @@ mg_status mg_gemm_splitk(const void* A, const void* B, void* C, void* workspace,
                          mg_dtype in_dtype, mg_dtype out_dtype, hipStream_t stream);
 
 /*
+ * mg_gemm_splitk without a workspace argument and without any allocation,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  The fp32
+ * partials go to a fixed scratch array inside the library: one per GPU, of
+ * mg_splitk_noalloc_max_bytes() bytes (32 MiB), created when the library is
+ * first used on that GPU and held until the process ends.  A problem whose
+ * partials (splits * M * N * 4 bytes) exceed it is MG_ERR_INVALID_ARG;
+ * everything else as mg_gemm_splitk().  The call makes no hipMalloc, hipFree
+ * or other allocating call; its only HIP calls besides the launches are
+ * hipGetDevice and, on the first call on a device, hipGetSymbolAddress.
+ * Every call on one GPU shares that GPU's array and overwrites the part it
+ * uses before reading it: calls on one GPU must not overlap in time (calls
+ * on one stream never do; calls on different streams race).
+ */
+size_t mg_splitk_noalloc_max_bytes(void);
+mg_status mg_gemm_splitk_noalloc(const void* A, const void* B, void* C, int64_t splits,
+                                 int64_t M, int64_t N, int64_t K,
+                                 int64_t stride_am, int64_t stride_ak,
+                                 int64_t stride_bk, int64_t stride_bn,
+                                 int64_t stride_cm, int64_t stride_cn,
+                                 mg_dtype in_dtype, mg_dtype out_dtype, hipStream_t stream);
+
+/*
  * Grouped GEMM for the expert layer of a mixture-of-experts model, in one
  * launch: for every expert e,
  *     Y[o_e : o_{e+1}, :] = X[o_e : o_{e+1}, :] * W[e]

@@ -43,7 +43,8 @@ EXPORTED = (
     "mg_splitk_workspace_bytes", "mg_splitk_choose", "mg_grouped_gemm", "mg_prepacked_bytes",
     "mg_prepack_a", "mg_config_bk", "mg_gemm_prepacked", "mg_num_configs", "mg_config_info",
     "mg_set_config", "mg_last_config", "mg_select_config", "mg_conv2d_output_hw", "mg_im2col",
-    "mg_conv2d_workspace_bytes", "mg_conv2d", "mg_attention_scores",
+    "mg_conv2d_workspace_bytes", "mg_conv2d", "mg_attention_scores", "mg_splitk_noalloc_max_bytes",
+    "mg_gemm_splitk_noalloc",
 )
 
 
@@ -82,6 +83,10 @@ def lib() -> ctypes.CDLL:
         L.mg_splitk_choose.argtypes = [i64, i64, i64]
         L.mg_gemm_splitk.restype = cint
         L.mg_gemm_splitk.argtypes = [vp, vp, vp, vp, ctypes.c_size_t] + [i64] * 10 + [cint, cint, vp]
+        L.mg_splitk_noalloc_max_bytes.restype = ctypes.c_size_t
+        L.mg_splitk_noalloc_max_bytes.argtypes = []
+        L.mg_gemm_splitk_noalloc.restype = cint
+        L.mg_gemm_splitk_noalloc.argtypes = [vp, vp, vp] + [i64] * 10 + [cint, cint, vp]
         L.mg_grouped_gemm.restype = cint
         L.mg_grouped_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, cint, vp]
         L.mg_prepacked_bytes.restype = ctypes.c_size_t
@@ -269,6 +274,33 @@ def mg_gemm_splitk(a, b, splits: int | None = None, workspace=None, out=None):
     _check(lib().mg_gemm_splitk(a.data_ptr(), b.data_ptr(), out.data_ptr(), workspace.data_ptr(), ws_bytes, splits,
                                 M, N, K, a.stride(0), a.stride(1), b.stride(0), b.stride(1), out.stride(0),
                                 out.stride(1), _dtype_code(a), _dtype_code(out), _stream(a)))
+    return out
+
+
+def mg_splitk_noalloc_max_bytes() -> int:
+    return int(lib().mg_splitk_noalloc_max_bytes())
+
+
+def mg_gemm_splitk_noalloc(a, b, splits: int | None = None, out=None):
+    """out = a @ b by split-K with the partials in the library's own scratch
+    array (no workspace, nothing allocated by the library; `out` must be
+    given by callers that cannot allocate)."""
+    import torch
+
+    _require_gpu(a, b)
+    M, K = a.shape
+    K2, N = b.shape
+    if K2 != K:
+        raise RuntimeError("MG_ERR_INVALID_ARG: inner dimensions differ (%d vs %d)" % (K, K2))
+    _same_dtype(a, b)
+    if out is None:
+        out = torch.empty((M, N), dtype=a.dtype, device=a.device)
+    _check_out(out, (M, N), a)
+    if splits is None:
+        splits = mg_splitk_choose(M, N, K)
+    _check(lib().mg_gemm_splitk_noalloc(a.data_ptr(), b.data_ptr(), out.data_ptr(), splits, M, N, K, a.stride(0),
+                                        a.stride(1), b.stride(0), b.stride(1), out.stride(0), out.stride(1),
+                                        _dtype_code(a), _dtype_code(out), _stream(a)))
     return out
 
 

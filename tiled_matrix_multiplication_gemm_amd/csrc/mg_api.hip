@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 #include <stdint.h>
 
@@ -463,22 +464,30 @@ size_t mg_splitk_workspace_bytes(int64_t M, int64_t N, int64_t splits) {
     return (size_t)(splits * M * N) * sizeof(float);
 }
 
-mg_status mg_gemm_splitk(const void* A, const void* B, void* C, void* workspace, size_t workspace_bytes,
-                         int64_t splits, int64_t M, int64_t N, int64_t K, int64_t stride_am, int64_t stride_ak,
-                         int64_t stride_bk, int64_t stride_bn, int64_t stride_cm, int64_t stride_cn,
-                         mg_dtype in_dtype, mg_dtype out_dtype, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Split-K, validation of everything but the workspace (no HIP call).
+mg_status splitk_check(const void* A, const void* B, void* C, int64_t splits, int64_t M, int64_t N, int64_t K,
+                       int64_t stride_am, int64_t stride_ak, int64_t stride_bk, int64_t stride_bn, int64_t stride_cm,
+                       int64_t stride_cn, mg_dtype in_dtype, mg_dtype out_dtype, int& ta, int& tb) {
     if (M < 0 || N < 0 || K < 0 || splits < 1 || splits > 4096) return MG_ERR_INVALID_ARG;
     MG_TRY(check_dtype(in_dtype, out_dtype));
-    const int ta = (stride_ak == 1 || K <= 1) ? 0 : ((stride_am == 1 || M <= 1) ? 1 : -1);
-    const int tb = (stride_bn == 1 || N <= 1) ? 0 : ((stride_bk == 1 || K <= 1) ? 1 : -1);
+    ta = (stride_ak == 1 || K <= 1) ? 0 : ((stride_am == 1 || M <= 1) ? 1 : -1);
+    tb = (stride_bn == 1 || N <= 1) ? 0 : ((stride_bk == 1 || K <= 1) ? 1 : -1);
     if (ta < 0 || tb < 0) return MG_ERR_UNSUPPORTED_LAYOUT;
     MG_TRY(ta ? check_matrix(A, K, M, stride_ak, stride_am) : check_matrix(A, M, K, stride_am, stride_ak));
     MG_TRY(tb ? check_matrix(B, N, K, stride_bn, stride_bk) : check_matrix(B, K, N, stride_bk, stride_bn));
-    MG_TRY(check_matrix(C, M, N, stride_cm, stride_cn));
-    if (M == 0 || N == 0) return MG_OK;
-    if (workspace == nullptr || workspace_bytes < mg_splitk_workspace_bytes(M, N, splits))
-        return MG_ERR_INVALID_ARG;
-    if (!aligned16(workspace)) return MG_ERR_MISALIGNED;
+    return check_matrix(C, M, N, stride_cm, stride_cn);
+}
+
+// Split-K launch on a validated problem with a workspace of at least
+// splits * M * N floats.
+mg_status splitk_launch(const void* A, const void* B, void* C, void* workspace, int64_t splits, int64_t M, int64_t N,
+                        int64_t K, int64_t stride_am, int64_t stride_ak, int64_t stride_bk, int64_t stride_bn,
+                        int64_t stride_cm, mg_dtype in_dtype, int ta, int tb, hipStream_t stream,
+                        bool dry = false) {
     const int cfg = select_config_splitk(M, N, splits);
     if (cfg < 0 || cfg >= kNumConfigs) return MG_ERR_BAD_CONFIG;
     KArgs a{};
@@ -491,7 +500,76 @@ mg_status mg_gemm_splitk(const void* A, const void* B, void* C, void* workspace,
     a.ldc = stride_cm;
     a.ws = (float*)workspace;
     a.splits = (int32_t)splits;
+    a.dry = dry ? 1 : 0;
     return launch(cfg, (int)in_dtype, false, MODE_SPLITK, a, stream, ta, tb);
+}
+
+// ---- split-K without allocation ------------------------------------------------
+// The fp32 partials of mg_gemm_splitk_noalloc live in this array: one copy
+// per GPU, created when the library's code object is loaded on that GPU and
+// held until the process ends.  Host code never uses the name itself (on the
+// host it is only a stand-in for the symbol): the device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (nullptr on error).
+void* scratch_address() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+mg_status mg_gemm_splitk(const void* A, const void* B, void* C, void* workspace, size_t workspace_bytes,
+                         int64_t splits, int64_t M, int64_t N, int64_t K, int64_t stride_am, int64_t stride_ak,
+                         int64_t stride_bk, int64_t stride_bn, int64_t stride_cm, int64_t stride_cn,
+                         mg_dtype in_dtype, mg_dtype out_dtype, hipStream_t stream) {
+    int ta = 0, tb = 0;
+    MG_TRY(splitk_check(A, B, C, splits, M, N, K, stride_am, stride_ak, stride_bk, stride_bn, stride_cm, stride_cn,
+                        in_dtype, out_dtype, ta, tb));
+    if (M == 0 || N == 0) return MG_OK;
+    if (workspace == nullptr || workspace_bytes < mg_splitk_workspace_bytes(M, N, splits))
+        return MG_ERR_INVALID_ARG;
+    if (!aligned16(workspace)) return MG_ERR_MISALIGNED;
+    return splitk_launch(A, B, C, workspace, splits, M, N, K, stride_am, stride_ak, stride_bk, stride_bn, stride_cm,
+                         in_dtype, ta, tb, stream);
+}
+
+size_t mg_splitk_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+mg_status mg_gemm_splitk_noalloc(const void* A, const void* B, void* C, int64_t splits, int64_t M, int64_t N,
+                                 int64_t K, int64_t stride_am, int64_t stride_ak, int64_t stride_bk,
+                                 int64_t stride_bn, int64_t stride_cm, int64_t stride_cn, mg_dtype in_dtype,
+                                 mg_dtype out_dtype, hipStream_t stream) {
+    int ta = 0, tb = 0;
+    MG_TRY(splitk_check(A, B, C, splits, M, N, K, stride_am, stride_ak, stride_bk, stride_bn, stride_cm, stride_cn,
+                        in_dtype, out_dtype, ta, tb));
+    if (M == 0 || N == 0) return MG_OK;
+    if (mg_splitk_workspace_bytes(M, N, splits) > kNoAllocScratchBytes) return MG_ERR_INVALID_ARG;
+    // the shape checks of the launch itself, still without a HIP call
+    MG_TRY(splitk_launch(A, B, C, nullptr, splits, M, N, K, stride_am, stride_ak, stride_bk, stride_bn, stride_cm,
+                         in_dtype, ta, tb, stream, /*dry=*/true));
+    void* ws = scratch_address();
+    if (ws == nullptr) return MG_ERR_HIP;
+    return splitk_launch(A, B, C, ws, splits, M, N, K, stride_am, stride_ak, stride_bk, stride_bn, stride_cm,
+                         in_dtype, ta, tb, stream);
 }
 
 mg_status mg_grouped_gemm(const void* X, const void* W, void* Y, const int32_t* expert_offsets, int64_t E, int64_t T,
