@@ -249,16 +249,7 @@ def measure_dense(name, steps, warmup):
     d = mg.mg_config_info(mg.mg_last_config())
     hbm_bytes = 2.0 * (c.M * c.K + c.K * c.N + c.M * c.N) + (2.0 * c.N if c.bias is not None else 0.0)
     return dict(case=c, flops=flops, wall=wall, kernel_ms=mean_ms, kernel_ms_median=med_ms, tile_config=d["name"],
-                kernel=kernel_name(d, c.K, c.N), compulsory_bytes=hbm_bytes, fn=fn)
-
-
-def kernel_name(d, K, N):
-    """The kernel family a table row launches for this K and N (the host
-    takes the direct-to-LDS kernel when K is a multiple of its slice and N of
-    8; dense problems only)."""
-    if d["direct_lds"] and K % d["direct_bk"] == 0 and N % 8 == 0:
-        return "gemm_kslab_kernel" if d["direct_ksplit"] > 1 else "gemm_dlds_kernel"
-    return "gemm_tile_kernel"
+                kernel=mg.mg_last_kernel(), compulsory_bytes=hbm_bytes, fn=fn)
 
 
 def grouped_setup(name, variant="float"):

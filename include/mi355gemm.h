@@ -72,10 +72,11 @@ const char* mg_status_string(mg_status status);
  * Strides are in elements; a transposed view is a swap of the two strides
  * (the strided 2-D view of "Triton study notes", section 1.2).  The stored
  * row stride of each operand must be a multiple of 8 and at least its row
- * length; any other stride pattern is MG_ERR_UNSUPPORTED_LAYOUT.  A
- * transposed operand is supported on the direct-to-LDS kernels only, i.e.
- * when K is a multiple of the chosen row's K slice, N % 8 == 0 and, for a
- * transposed A, M % 8 == 0; otherwise MG_ERR_UNSUPPORTED_LAYOUT.
+ * length; any other stride pattern is MG_ERR_UNSUPPORTED_LAYOUT.  Any M, N
+ * and K are accepted in either layout (the direct-to-LDS kernels zero-fill
+ * a K tail and mask the N tail); a transposed operand is refused
+ * (MG_ERR_UNSUPPORTED_LAYOUT) only under a configuration forced with
+ * mg_set_config() that has no direct-to-LDS kernel.
  *
  * fp32 (in_dtype == out_dtype == MG_F32; the 4096^3 fp32 row of the FlagOS
  * cross-chip page's benchmark table, section 3.4): fp32 inputs on the fp32
@@ -137,10 +138,9 @@ mg_status mg_gemm_batched(const void* A, const void* B, void* C, int64_t batch,
  * the partials in split order (deterministic) and rounds once into C.  Both
  * kernels run on `stream`; the workspace must not be used by another call
  * until they have finished.  Operands as for mg_gemm(), transposed ones
- * included; the shape must suit the direct-to-LDS kernels (K in whole
- * slices of the chosen row, N % 8 == 0, M % 8 == 0 for a transposed A),
- * else MG_ERR_UNSUPPORTED_LAYOUT.  splits in [1, 4096]; a workspace that is
- * null or too small is MG_ERR_INVALID_ARG.
+ * included, any K; N must be a multiple of 8 (the partials are summed 8
+ * columns at a time), else MG_ERR_UNSUPPORTED_LAYOUT.  splits in [1, 4096];
+ * a workspace that is null or too small is MG_ERR_INVALID_ARG.
  */
 size_t mg_splitk_workspace_bytes(int64_t M, int64_t N, int64_t splits);
 /* A split count for mg_gemm_splitk() from a time model of this library on
@@ -301,9 +301,7 @@ mg_status mg_conv2d(const mg_conv2d_shape* shape, const void* x, const void* w, 
  * softmax are not part of it).  Q_h: Lq x d rows (row stride stride_qm,
  * head stride stride_qh), K_h: Lk x d rows (stride_kn, stride_kh), S_h: Lq x
  * Lk (stride_sm, stride_sh).  The batched GEMM with K_h as a transposed B
- * operand; fp16 or bf16; d must be a whole number of the chosen tile's K
- * slices (a multiple of 64 always is) and Lk % 8 == 0, else
- * MG_ERR_UNSUPPORTED_LAYOUT; strides multiples of 8.
+ * operand; fp16 or bf16; any Lq, Lk and d; strides multiples of 8.
  */
 mg_status mg_attention_scores(const void* Q, const void* K, void* S, int64_t heads, int64_t Lq, int64_t Lk,
                               int64_t d, int64_t stride_qh, int64_t stride_qm, int64_t stride_kh,
@@ -321,8 +319,11 @@ typedef struct {
     int group_m;              /* tile rows visited together (L2 reuse)     */
     int xcd_remap;            /* 1: consecutive tiles stay on one XCD      */
     int lds_bytes;            /* shared memory of one workgroup            */
-    int direct_lds;           /* 1: has the direct-to-LDS kernel, used when
-                                 K % direct_bk == 0 and N % 8 == 0         */
+    int direct_lds;           /* 1: has a direct-to-LDS kernel: the
+                                 pipelined kernel takes every shape, the
+                                 K-split one (direct_ksplit > 1) dense
+                                 row-major problems with K % direct_bk == 0
+                                 and N % 8 == 0                            */
     int direct_bk;            /* K slice of the direct-to-LDS kernel       */
     int direct_stages;        /* LDS ring slots of the direct kernel       */
     int direct_lds_bytes;     /* shared memory of the direct kernel        */
@@ -338,6 +339,10 @@ mg_status mg_config_info(int id, mg_config_desc* out);
 mg_status mg_set_config(int id);
 /* Configuration id used by the most recent successful call in this process. */
 int mg_last_config(void);
+/* Kernel family of the most recent successful 16-bit GEMM launch in this
+ * process: 0 = general register-staged kernel, 1 = direct-to-LDS pipelined
+ * kernel, 2 = direct-to-LDS K-split kernel; -1 before any launch. */
+int mg_last_kernel(void);
 /* Configuration the table selects for a dense problem of this shape. */
 int mg_select_config(int64_t M, int64_t N, int64_t K, mg_dtype dtype, int grouped);
 

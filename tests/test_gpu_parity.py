@@ -95,6 +95,7 @@ SMALL = [(1, 1, 1), (7, 33, 129), (33, 7, 1000), (129, 129, 33), (65, 200, 72),
          (64, 64, 64), (1, 8, 64), (65, 200, 128), (129, 136, 64), (300, 264, 192), (513, 520, 256),
          (70, 72, 32), (96, 40, 96)]
 NUM_CONFIGS = 9
+DIRECT_ROWS = [0, 1, 2, 3, 4, 6, 8]  # rows with the pipelined direct-to-LDS kernel
 
 
 def test_config_count_matches_library():
@@ -104,6 +105,10 @@ def test_config_count_matches_library():
 @pytest.mark.parametrize("cfg", range(NUM_CONFIGS))
 @pytest.mark.parametrize("dtype", [F16, BF16])
 def test_small_ragged_shapes_every_config(orc, cfg, dtype):
+    """Every shape on every row.  Rows with a pipelined direct-to-LDS kernel
+    run it on every shape (K and N tails included); the K-split row takes its
+    own kernel where K fills whole slices and N % 8 == 0, and row 5 has only
+    the general kernel."""
     for i, (M, N, K) in enumerate(SMALL):
         for integer in (True, False):
             for epi in (False, True):
@@ -113,6 +118,13 @@ def test_small_ragged_shapes_every_config(orc, cfg, dtype):
                 else:
                     c = inputs.random_dense(M, N, K, dtype, seed, epilogue=epi, name="small")
                 check_full(orc, c, cfg)
+                if cfg in DIRECT_ROWS or cfg == -1:
+                    expect = "gemm_dlds_kernel"
+                elif cfg == 7:
+                    expect = "gemm_kslab_kernel" if K % 32 == 0 and N % 8 == 0 else "gemm_tile_kernel"
+                else:
+                    expect = "gemm_tile_kernel"
+                assert mg.mg_last_kernel() == expect, (cfg, M, N, K, mg.mg_last_kernel())
 
 
 @pytest.mark.parametrize("pads", [(8, 0, 0), (0, 16, 0), (0, 0, 8), (24, 8, 40)])
@@ -253,8 +265,8 @@ def test_large_ragged_edges(orc, integer):
 # Transposed operands (strides swapped, "Triton study notes" section 1.2):
 # shapes the direct-to-LDS rows take (K a multiple of 64, N and M multiples
 # of 8), with ragged tile edges, on every row that has such a kernel.
-TRANSPOSED = [(64, 64, 64), (8, 8, 64), (72, 200, 128), (264, 136, 320), (520, 512, 256), (128, 264, 192)]
-DIRECT_ROWS = [0, 1, 2, 3, 4, 6, 8]
+TRANSPOSED = [(64, 64, 64), (8, 8, 64), (72, 200, 128), (264, 136, 320), (520, 512, 256), (128, 264, 192),
+              (70, 61, 100), (33, 200, 129), (136, 7, 57), (257, 130, 203)]
 
 
 def stored_transposed(bits, dt):
@@ -267,16 +279,25 @@ def stored_transposed(bits, dt):
     return to_dev(full, dt)[:, :R].t()
 
 
+def stored_row_major(bits, dt):
+    """bits ([R,C]) row-major with the row stride rounded up to a multiple of 8."""
+    R, C = bits.shape
+    ld = (C + 7) // 8 * 8
+    full = np.zeros((R, ld), dtype=np.uint16)
+    full[:, :C] = bits
+    return to_dev(full, dt)[:, :C]
+
+
 def run_transposed(case, ta, tb, cfg=-1):
     """Run a dense case with A and/or B handed over as transposed views of
     their transposes (stored [K,M] / [N,K]); returns (bits, guards intact)."""
     import torch
 
     dt = case.dtype
-    A = stored_transposed(case.A, dt) if ta else to_dev(case.A, dt)
-    B = stored_transposed(case.B, dt) if tb else to_dev(case.B, dt)
+    A = stored_transposed(case.A, dt) if ta else stored_row_major(case.A, dt)
+    B = stored_transposed(case.B, dt) if tb else stored_row_major(case.B, dt)
     assert (A.stride(0) == 1) == bool(ta) or case.M == 1 or case.K == 1
-    out = Guarded(case.M, case.N, dt)
+    out = Guarded(case.M, case.N, dt, ld=(case.N + 7) // 8 * 8)
     mg.mg_set_config(cfg)
     try:
         if case.bias is not None:
@@ -312,13 +333,14 @@ def test_transposed_operands_every_direct_row(orc, cfg, ta, tb):
                     assert_tolerance(got, ref, dtype, c.name)
 
 
-def test_transposed_operands_outside_the_direct_kernels_are_refused():
-    # a transposed A needs M % 8 == 0; K must fill whole slices
+def test_transposed_operands_without_a_direct_kernel_are_refused():
+    # only row 5 has no direct-to-LDS kernel: forced, it refuses transposed
+    # operands; the table's own choice takes them on ragged shapes too
     for (M, N, K, ta, tb) in [(70, 64, 64, 1, 0), (64, 64, 40, 1, 0), (64, 64, 40, 0, 1)]:
         c = inputs.integer_dense(M, N, K, F16, 7, name="refused")
-        announce("transposed refused M=%d N=%d K=%d ta=%d tb=%d" % (M, N, K, ta, tb))
+        announce("transposed refused on row 5 M=%d N=%d K=%d ta=%d tb=%d" % (M, N, K, ta, tb))
         with pytest.raises(RuntimeError, match="UNSUPPORTED_LAYOUT"):
-            run_transposed(c, ta, tb)
+            run_transposed(c, ta, tb, cfg=5)
 
 
 @pytest.mark.parametrize("ta,tb", [(1, 0), (0, 1), (1, 1)])

@@ -44,7 +44,7 @@ EXPORTED = (
     "mg_prepack_a", "mg_config_bk", "mg_gemm_prepacked", "mg_num_configs", "mg_config_info",
     "mg_set_config", "mg_last_config", "mg_select_config", "mg_conv2d_output_hw", "mg_im2col",
     "mg_conv2d_workspace_bytes", "mg_conv2d", "mg_attention_scores", "mg_splitk_noalloc_max_bytes",
-    "mg_gemm_splitk_noalloc",
+    "mg_gemm_splitk_noalloc", "mg_last_kernel",
 )
 
 
@@ -105,6 +105,8 @@ def lib() -> ctypes.CDLL:
         L.mg_set_config.argtypes = [cint]
         L.mg_last_config.restype = cint
         L.mg_last_config.argtypes = []
+        L.mg_last_kernel.restype = cint
+        L.mg_last_kernel.argtypes = []
         L.mg_select_config.restype = cint
         L.mg_select_config.argtypes = [i64, i64, i64, cint, cint]
         shp = ctypes.POINTER(Conv2dShape)
@@ -391,6 +393,14 @@ def mg_set_config(cid: int) -> None:
 
 def mg_last_config() -> int:
     return int(lib().mg_last_config())
+
+
+KERNEL_FAMILIES = {-1: None, 0: "gemm_tile_kernel", 1: "gemm_dlds_kernel", 2: "gemm_kslab_kernel"}
+
+
+def mg_last_kernel() -> str | None:
+    """Kernel family of the last 16-bit GEMM launch in this process."""
+    return KERNEL_FAMILIES[int(lib().mg_last_kernel())]
 
 
 def mg_select_config(M: int, N: int, K: int, dtype: int = MG_F16, grouped: bool = False) -> int:

@@ -39,6 +39,7 @@ const mg_config_desc kTable[kNumConfigs] = {
 
 std::atomic<int> g_forced{-1};
 std::atomic<int> g_last{-1};
+std::atomic<int> g_last_kernel{-1};
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -389,6 +390,10 @@ mg_status check_image(const mg_conv2d_shape* s, const void* x) {
 
 }  // namespace
 
+namespace mg {
+void note_kernel(int family) { g_last_kernel.store(family); }
+}  // namespace mg
+
 extern "C" {
 
 const char* mg_status_string(mg_status status) {
@@ -676,6 +681,8 @@ mg_status mg_set_config(int id) {
 }
 
 int mg_last_config(void) { return g_last.load(); }
+
+int mg_last_kernel(void) { return g_last_kernel.load(); }
 
 int mg_select_config(int64_t M, int64_t N, int64_t K, mg_dtype dtype, int grouped) {
     (void)dtype;

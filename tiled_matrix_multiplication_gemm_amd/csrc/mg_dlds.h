@@ -10,11 +10,17 @@
 // memory latency), with XOR-swizzled 16-byte chunks against bank conflicts
 // (FlagOS cross-chip page, section 2.3).
 //
-// Preconditions (checked by the host): K % BK == 0, N % 8 == 0, and a tile's
-// operand offsets fit in 31 bits (BM * lda and 64 * ldb elements).  Rows past
-// M and column chunks past N are clamped to the last valid ones, so every
-// load is in bounds; what they feed are output rows / columns that are never
-// stored.
+// Preconditions (checked by the host): a tile's operand offsets fit in 31
+// bits (BM * lda and 64 * ldb elements).  Rows past M and 8-element chunks
+// past N are clamped to the last valid ones; what they feed are output rows
+// and columns that are never stored.  K need not fill whole slices: in the
+// last slice, 16-byte chunks (K-major operand) or k-rows (MN-major operand)
+// that lie wholly past K take a load offset beyond the buffer resource's
+// range, which the hardware answers with zeros, and when K % 8 != 0 the
+// K-major fragments of that slice are masked in registers (the chunk that
+// straddles K brings in elements of the row's padding).  Every 16-byte
+// chunk that is loaded is 16-byte aligned and holds at least one element
+// of the operand, so it lies in a page the operand occupies.
 #pragma once
 
 #include <type_traits>
@@ -144,6 +150,12 @@ struct OpKM {
         const int64_t r = (e0 + line < ext ? line : ext - 1 - e0);
         return (uint32_t)((r * ld + 8 * c) * 2);
     }
+    // first k (within the slice) of the chunk that load j of wave w, lane l fetches
+    __device__ static int load_k(int w, int j, int lane) {
+        int line, c;
+        load_pos(w, j, lane, line, c);
+        return 8 * c;
+    }
     __device__ static const char* tile_base(const uint16_t* p, int64_t e0, int64_t ld) {
         return (const char*)(p + e0 * ld);
     }
@@ -160,11 +172,14 @@ struct OpKM {
 template <int E, int BK, int NW>
 struct OpMN {
     static constexpr int CH = E / 8, LINE = E * 2, BYTES = BK * LINE, J = BYTES / 1024 / NW;
+    // k-row (within the slice) that load j of wave w, lane l fetches from
+    __device__ static int load_k(int w, int j, int lane) { return (w * J + j) * (512 / E) + (8 * lane) / E; }
+    // chunks past the extent are clamped to the chunk that holds its last
+    // element (e0 is a multiple of 8, so every chunk stays 16-byte aligned)
     __device__ static uint32_t load_off(int w, int j, int lane, int64_t e0, int64_t ext, int64_t ld) {
-        const int q = w * J + j;
-        const int krow = q * (512 / E) + (8 * lane) / E;
+        const int krow = load_k(w, j, lane);
         const int c = (lane % CH) ^ swz_b<CH>(krow);
-        const int64_t cn = (e0 + 8 * c <= ext - 8) ? 8 * c : ext - 8 - e0;
+        const int64_t cn = (e0 + 8 * c < ext) ? 8 * c : ((ext - 1) & ~(int64_t)7) - e0;
         return (uint32_t)((krow * ld + cn) * 2);
     }
     __device__ static const char* tile_base(const uint16_t* p, int64_t e0, int64_t) { return (const char*)(p + e0); }
@@ -211,7 +226,7 @@ __device__ __forceinline__ void ring_barrier() {
 }
 
 // One LDS ring slot: a distinct shared-memory object per (slot index, kernel).
-template <class Cfg, int DT, bool EPI, int MODE, bool TA, bool TB>
+template <class Cfg, int DT, bool EPI, int MODE, bool TA, bool TB, bool KT>
 struct DldsTag {};
 template <int BYTES, int I, class Tag>
 __device__ __forceinline__ char* lds_slot() {
@@ -220,8 +235,10 @@ __device__ __forceinline__ char* lds_slot() {
 }
 
 // TA: A is given transposed (stored [K,M], lda = its k-row stride);
-// TB: B is given transposed (stored [N,K], ldb = its row stride).
-template <class Cfg, int DT, bool EPI, int MODE, bool TA = false, bool TB = false>
+// TB: B is given transposed (stored [N,K], ldb = its row stride);
+// KT: K is not a whole number of slices (this instance masks the last one;
+// the others carry no trace of the masking).
+template <class Cfg, int DT, bool EPI, int MODE, bool TA = false, bool TB = false, bool KT = false>
 __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;
     constexpr int FM = Cfg::FM, FN = Cfg::FN, JA = Cfg::JA, JB = Cfg::JB;
@@ -230,7 +247,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
     // compiler can tell reads of one slot from direct loads landing in another
     // (a single array would make it wait for every load in flight before each
     // LDS read).
-    using Tag = DldsTag<Cfg, DT, EPI, MODE, TA, TB>;
+    using Tag = DldsTag<Cfg, DT, EPI, MODE, TA, TB, KT>;
     using OA = std::conditional_t<TA, OpMN<Cfg::BM, Cfg::BK, Cfg::NW>, OpKM<Cfg::BM, Cfg::BK, Cfg::NW>>;
     using OB = std::conditional_t<TB, OpKM<Cfg::BN, Cfg::BK, Cfg::NW>, OpMN<Cfg::BN, Cfg::BK, Cfg::NW>>;
     static_assert(OA::J == Cfg::JA && OB::J == Cfg::JB, "operand slices split like the ring");
@@ -285,12 +302,21 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
     }
     const int64_t N = args.N, K = args.K;
     const int64_t m0 = (int64_t)pm * BM, n0 = (int64_t)pn * BN;
-    int nk = (int)(K / BK);
+    int nk = (int)((K + BK - 1) / BK);
     int kt0 = 0;  // this workgroup's K slices are [kt0, kt0 + nk)
     if constexpr (MODE == MODE_SPLITK) {
         const int all = nk;
         kt0 = (int)((int64_t)split * all / args.splits);
         nk = (int)((int64_t)(split + 1) * all / args.splits) - kt0;
+    }
+    // Whether this workgroup's last slice reaches past K (its loads are then
+    // masked), and whether a 16-byte chunk straddles K (K-major fragments of
+    // that slice are then masked in registers).  A convolution's slices lie
+    // within one kernel tap each, so its K is a whole number of slices.
+    bool ragged = false, kmask = false;
+    if constexpr (KT && MODE != MODE_CONV) {
+        ragged = nk > 0 && (int64_t)(kt0 + nk) * BK > K;
+        kmask = ragged && (K % 8) != 0;
     }
 
     // ---- per-lane source offsets of the direct loads ---------------------
@@ -338,10 +364,17 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
         }
     }
 
+    // Prepacked A ([ceil(K/BKP), M, BKP], BKP = lda a multiple of BK): slice
+    // kt is columns (kt % rp) BK .. of block kt / rp, whose rows are BKP
+    // elements long.
+    [[maybe_unused]] int rp = 1;
+    if constexpr (MODE == MODE_PACKED_A) rp = (int)(args.lda / BK);
+
     // direct loads of k-slice kt into ring slot `slot` (a compile-time index)
-    // (buffer resources rebased on the slice: offsets stay below 2^31)
-    auto issue = [&](int kt, int slot) {
-        [[maybe_unused]] uint32_t offA[JA];
+    // (buffer resources rebased on the slice: offsets stay below 2^31);
+    // `masked`: the slice reaches past K
+    auto issue = [&](int kt, int slot, bool masked) {
+        uint32_t offA[JA], offB[JB];
         __amdgpu_buffer_rsrc_t ra;
         if constexpr (MODE == MODE_CONV) {
             const ConvArgs& cv = args.conv;
@@ -366,9 +399,29 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
                 }
             }
         } else {
-            ra = buffer_rsrc(baseA + kt * stepA);
+            if constexpr (MODE == MODE_PACKED_A) {
+                const int kb = kt / rp, kr = kt - kb * rp;
+                ra = buffer_rsrc((const char*)(Ag + ((int64_t)kb * M + m0) * args.lda + kr * BK));
+            } else {
+                ra = buffer_rsrc(baseA + kt * stepA);
+            }
 #pragma unroll
             for (int j = 0; j < JA; ++j) offA[j] = offA_g[j];
+        }
+#pragma unroll
+        for (int j = 0; j < JB; ++j) offB[j] = offB_g[j];
+        if constexpr (KT && MODE != MODE_CONV) {
+            if (masked) {
+                // chunks (K-major) or k-rows (MN-major) wholly past K: an
+                // offset past the resource's range, answered with zeros
+                const int64_t kbase = (int64_t)(kt0 + kt) * BK;
+#pragma unroll
+                for (int j = 0; j < JA; ++j)
+                    if (kbase + OA::load_k(wave, j, lane) >= K) offA[j] = 0x80000000u;
+#pragma unroll
+                for (int j = 0; j < JB; ++j)
+                    if (kbase + OB::load_k(wave, j, lane) >= K) offB[j] = 0x80000000u;
+            }
         }
         const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(baseB + kt * stepB);
         char* sa = slot_ptr(slot);
@@ -376,7 +429,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
 #pragma unroll
         for (int j = 0; j < JA; ++j) direct_load16(ra, offA[j], (lds_void_t*)(sa + (wave * JA + j) * 1024));
 #pragma unroll
-        for (int j = 0; j < JB; ++j) direct_load16(rb, offB_g[j], (lds_void_t*)(sb + (wave * JB + j) * 1024));
+        for (int j = 0; j < JB; ++j) direct_load16(rb, offB[j], (lds_void_t*)(sb + (wave * JB + j) * 1024));
     };
 
     f32x16 acc[FM][FN];
@@ -414,6 +467,27 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
         if (lv == 0) return;
 #pragma unroll
         for (int j = 0; j < FN; ++j) f.b[j] = OB::read(sb, offBj[j], wn * Cfg::WTN, j, s, lane);
+    };
+    // Slice t, step s: zero the elements at k >= K of the K-major fragments
+    // (lane l holds k = 16 s + 8 (l / 32) + 0..7 of the slice) when a chunk
+    // straddles K (K % 8 != 0); chunks wholly past K, and the MN-major
+    // operand's k-rows past K, were loaded as zeros.
+    auto mask_frags = [&](Frags& f, int t, int s) {
+        const int64_t left = kmask ? K - ((int64_t)(kt0 + t) * BK + 16 * s) : 16;
+        const int v0 = left <= 0 ? 0 : (left >= 16 ? 16 : (int)left);
+        const int v = (lane >> 5) ? (v0 > 8 ? v0 - 8 : 0) : (v0 > 8 ? 8 : v0);
+        auto keep = [&](u32x4& w) {
+#pragma unroll
+            for (int d = 0; d < 4; ++d) w[d] = (2 * d + 1 < v) ? w[d] : ((2 * d < v) ? (w[d] & 0xFFFFu) : 0u);
+        };
+        if constexpr (!TA) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) keep(f.a[i]);
+        }
+        if constexpr (TB) {
+#pragma unroll
+            for (int j = 0; j < FN; ++j) keep(f.b[j]);
+        }
     };
     auto mfma_step = [&](const Frags& f, auto lv) {
 #pragma unroll
@@ -473,7 +547,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
             } else if (steady) {
                 wait_vmcnt<L * (R - 3)>();
                 ring_barrier();
-                issue(t + R - 1, (u + R - 1) % R);
+                issue(t + R - 1, (u + R - 1) % R, false);
                 read_frags(nxt, (u + 1) % R, 0, lv);
             } else {
                 // slices issued so far: 0 .. min(t+R-2, nk-1); in steady state
@@ -481,8 +555,15 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
                 if (t + R - 2 <= nk - 1) wait_vmcnt<L * (R - 3)>();
                 else wait_vmcnt<0>();
                 ring_barrier();
-                if (t + R - 1 < nk) issue(t + R - 1, (u + R - 1) % R);
+                if (t + R - 1 < nk) issue(t + R - 1, (u + R - 1) % R, ragged && t + R - 1 == nk - 1);
                 if (t + 1 < nk) read_frags(nxt, (u + 1) % R, 0, lv);
+            }
+            // K-tail instance: outside the steady trips every step masks its
+            // K-major fragments with selects (no branch, so the step stays one
+            // block in which reads and MFMAs interleave); only the last slice
+            // has anything to clear
+            if constexpr (KT) {
+                if (!steady) mask_frags(cur, t, s);
             }
             mfma_step(cur, lv);
             if (steady && s + 1 == STEPS) interleave(std::integral_constant<int, JA + JB>{});
@@ -492,14 +573,16 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
     auto main_loop = [&](auto lv) {
         if (nk <= 0) return;
         const int pre = nk < R - 1 ? nk : R - 1;
-        for (int t = 0; t < pre; ++t) issue(t, t);
+        for (int t = 0; t < pre; ++t) issue(t, t, ragged && t == nk - 1);
         if (pre == R - 1) wait_vmcnt<L * (R - 2)>();  // slice 0 landed, R-2 slices still in flight
         else wait_vmcnt<0>();
         ring_barrier();
         read_frags(F0, 0, 0, lv);
         int trip = 0;
-        // steady trips: slices trip .. trip+R-1 all satisfy t + R - 1 < nk
-        for (; trip + 2 * R - 1 <= nk; trip += R) {
+        // steady trips: slices trip .. trip+R-1 all satisfy t + R - 1 < nk;
+        // a last slice that reaches past K is issued and consumed outside them
+        const int nk_steady = ragged ? nk - 1 : nk;
+        for (; trip + 2 * R - 1 <= nk_steady; trip += R) {
 #pragma unroll
             for (int u = 0; u < R; ++u) slice(trip + u, u, true, lv);
         }
@@ -522,9 +605,9 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
     // loaded before the K loop, so their latency is not paid at the end.
     // Lane l's columns in block j are, for group q, the 4 adjacent columns
     // j*32 + 4 (l / 32) + 8 q: one 8-byte load each when the bias is 8-byte
-    // aligned (N % 8 == 0 here, so a group lies wholly inside or outside N);
-    // otherwise the epilogue reads the bias element by element.  Loads older
-    // than the ring's only make its waits stricter.
+    // aligned (element by element for the group that straddles N); otherwise
+    // the epilogue reads the bias element by element.  Loads older than the
+    // ring's only make its waits stricter.
     [[maybe_unused]] u32x2 bias_v[FN][4];
     [[maybe_unused]] bool bias_pre = false;
     if constexpr (EPI) {
@@ -534,7 +617,14 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int64_t col = n0 + wn * Cfg::WTN + j * 32 + 4 * (lane >> 5) + 8 * q;
-                bias_v[j][q] = (bias_pre && col < N) ? *(const u32x2*)(args.bias + col) : u32x2{0u, 0u};
+                if (bias_pre && col + 4 <= N) {
+                    bias_v[j][q] = *(const u32x2*)(args.bias + col);
+                } else {
+                    uint32_t h[4];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) h[t] = (bias_pre && col + t < N) ? (uint32_t)args.bias[col + t] : 0u;
+                    bias_v[j][q] = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+                }
             }
     }
     if (live == FM) main_loop(std::integral_constant<int, FM>{});
@@ -548,7 +638,8 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
     // once every wave has left the K loop), row-major per wave with XOR-
     // swizzled 16-byte chunks; the wave then reads back whole chunks and
     // writes each output row as contiguous 16-byte pieces, 8 rows per store
-    // (N % 8 == 0 on this path, so a chunk is entirely inside or outside N).
+    // (the one chunk of a row that straddles N, when N % 8 != 0, element by
+    // element).
     // One 32x32 tile at a time (a scheduling barrier keeps the compiler from
     // pulling every accumulator out at once); interior tiles skip the checks.
     const bool interior = (m0 + BM <= M) && (n0 + BN <= N);
@@ -629,7 +720,14 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
             u32x4 w = *(const lds_u32x4_t*)(stage + row * RB + (ch ^ stage_swz(row)) * 16);
             if (stage_half(row)) w = u32x4{w[2], w[3], w[0], w[1]};
             const int64_t grow = m0 + wm * Cfg::WTM + row;
-            if (interior || (grow < M && col < N)) *(u32x4*)(Cg + grow * args.ldc + col) = w;
+            if (interior || (grow < M && col + 8 <= N)) {
+                *(u32x4*)(Cg + grow * args.ldc + col) = w;
+            } else if (grow < M && col < N) {
+                // the chunk that straddles N (N % 8 != 0): its valid elements
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (col + e < N) Cg[grow * args.ldc + col + e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+            }
         }
     } else {
 #pragma unroll
@@ -644,7 +742,13 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const u32x2 w = pack4(acc[i][j], j, q, col0 + 8 * q);
-                    if (row_ok && (interior || col0 + 8 * q < N)) *(u32x2*)(cp + 8 * q) = w;
+                    if (row_ok && (interior || col0 + 8 * q + 4 <= N)) {
+                        *(u32x2*)(cp + 8 * q) = w;
+                    } else if (row_ok) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (col0 + 8 * q + e < N) cp[8 * q + e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+                    }
                 }
             }
         }

@@ -2,3 +2,4 @@
 #include "mg_launch.h"
 
 MG_DEFINE_ROW(5, Cfg5, void)
+MG_DEFINE_ROW_TAIL(5, void)

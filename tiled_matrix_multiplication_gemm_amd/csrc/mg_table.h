@@ -43,6 +43,9 @@ using Cfg8 = TileCfg<256, 64, 64, 4, 2>;
 using Fast8 = DldsCfg<256, 64, 4, 2, 64, 4>;
 
 inline constexpr int kNumConfigs = 9;
+
+// Kernel family of the last launch (mg_last_kernel): 0 general, 1 direct-to-LDS, 2 K-split.
+void note_kernel(int family);
 inline constexpr int kGroupM = 8;
 
 template <class F>
@@ -65,6 +68,23 @@ MG_DECLARE_ROW(5);
 MG_DECLARE_ROW(6);
 MG_DECLARE_ROW(7);
 MG_DECLARE_ROW(8);
+
+// The same for problems whose K is not a whole number of the row's slices
+// (direct-to-LDS kernel instances that mask the last slice), defined in
+// mg_row<cfg>_tail.hip; rows without such a kernel define it as an error.
+#define MG_DECLARE_ROW_TAIL(n)                                                                              \
+    mg_status launch_row##n##_tail(int dt, bool epi, int mode, int ta, int tb, const KArgs& a, int64_t grid, \
+                                   hipStream_t s)
+MG_DECLARE_ROW_TAIL(0);
+MG_DECLARE_ROW_TAIL(1);
+MG_DECLARE_ROW_TAIL(2);
+MG_DECLARE_ROW_TAIL(3);
+MG_DECLARE_ROW_TAIL(4);
+MG_DECLARE_ROW_TAIL(5);
+MG_DECLARE_ROW_TAIL(6);
+MG_DECLARE_ROW_TAIL(7);
+MG_DECLARE_ROW_TAIL(8);
+using RowLauncher = mg_status (*)(int, bool, int, int, int, const KArgs&, int64_t, hipStream_t);
 
 // fp32 GEMM: one configuration (mg_f32.h), defined in mg_f32.hip
 // fp32 kernel tiles: 0 = 128 x 128 (large outputs), 1 = 64 x 64 (outputs

@@ -107,6 +107,18 @@ def integer_dense(M, N, K, dtype, seed, lo=-4, hi=4, epilogue=False, name="custo
                      None if bias is None else to_bits(bias, dtype), relu=epilogue, integer=True)
 
 
+def subnormal_dense(M, N, K, seed, name="subnormal") -> DenseCase:
+    """fp16 A whose entries are k * 2^-24 with k uniform on -4..4 (zero and
+    the four smallest subnormals of either sign), B integers on -4..4.  Every
+    product and partial sum is an integer multiple of 2^-24 below 2^24 of
+    them, exact in fp32, so one rounding of the exact sum is the only
+    correct fp16 output (subnormal itself when |sum| < 2^-14)."""
+    rng = np.random.default_rng(seed)
+    A = rng.integers(-4, 5, size=(M, K)).astype(np.float64) * 2.0 ** -24
+    B = rng.integers(-4, 5, size=(K, N)).astype(np.float64)
+    return DenseCase(name, M, N, K, F16, to_bits(A, F16), to_bits(B, F16), integer=True)
+
+
 def dense_f32(M, N, K, seed, integer=False, epilogue=False, name="f32"):
     """fp32 inputs as uint32 bit patterns: N(0,1)/sqrt(K) values, or integers
     on -4..4 (exact products and sums); bias N(0, 0.1) or integers."""
