@@ -108,9 +108,11 @@ def upload(bits, dt):
     return t.view(torch.float16 if dt == 0 else torch.bfloat16)
 
 
-def time_calls(fn, steps: int, warmup: int):
+def time_calls(fn, steps: int, warmup: int, per_call: bool = False):
     """Warm up, then time exactly `steps` calls: wall clock over the whole
-    region (synchronised on both sides) and HIP events around each call."""
+    region (synchronised on both sides) and HIP events around each call.
+    Returns (wall s, mean ms, median ms), plus the sorted per-call ms list
+    when per_call is set."""
     import torch
 
     for _ in range(warmup):
@@ -127,7 +129,15 @@ def time_calls(fn, steps: int, warmup: int):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    if per_call:
+        return wall, sum(per) / len(per), per[len(per) // 2], per
     return wall, sum(per) / len(per), per[len(per) // 2]
+
+
+def spread(per):
+    """min / median / p90 of a sorted list of per-call times (ms)."""
+    return {"min": round(per[0], 5), "median": round(per[len(per) // 2], 5),
+            "p90": round(per[min(len(per) - 1, (9 * len(per)) // 10)], 5)}
 
 
 FLUSH_BYTES = 512 * 1024 * 1024  # more than the 256 MB last-level cache plus the 8 x 4 MB L2
@@ -244,12 +254,12 @@ def measure_dense(name, steps, warmup):
     import tiled_matrix_multiplication_gemm_amd as mg
 
     c, fn = dense_setup(name)
-    wall, mean_ms, med_ms = time_calls(fn, steps, warmup)
+    wall, mean_ms, med_ms, per = time_calls(fn, steps, warmup, per_call=True)
     flops = 2.0 * c.M * c.N * c.K
     d = mg.mg_config_info(mg.mg_last_config())
     hbm_bytes = 2.0 * (c.M * c.K + c.K * c.N + c.M * c.N) + (2.0 * c.N if c.bias is not None else 0.0)
     return dict(case=c, flops=flops, wall=wall, kernel_ms=mean_ms, kernel_ms_median=med_ms, tile_config=d["name"],
-                kernel=mg.mg_last_kernel(), compulsory_bytes=hbm_bytes, fn=fn)
+                kernel=mg.mg_last_kernel(), compulsory_bytes=hbm_bytes, fn=fn, spread=spread(per))
 
 
 def grouped_setup(name, variant="float"):
@@ -270,12 +280,12 @@ def measure_grouped(name, steps, warmup):
     import tiled_matrix_multiplication_gemm_amd as mg
 
     c, fn = grouped_setup(name)
-    wall, mean_ms, med_ms = time_calls(fn, steps, warmup)
+    wall, mean_ms, med_ms, per = time_calls(fn, steps, warmup, per_call=True)
     flops = 2.0 * c.T * c.K * c.N
     hbm_bytes = 2.0 * (c.T * c.K + c.E * c.K * c.N + c.T * c.N) + 4.0 * (c.E + 1)
     cfg = mg.mg_config_info(mg.mg_last_config())["name"]
     return dict(case=c, flops=flops, wall=wall, kernel_ms=mean_ms, kernel_ms_median=med_ms, tile_config=cfg,
-                compulsory_bytes=hbm_bytes, fn=fn)
+                compulsory_bytes=hbm_bytes, fn=fn, spread=spread(per))
 
 
 def cpu_baseline(case, target_s: float):
@@ -357,6 +367,123 @@ def measure_consumers(steps, warmup):
     return out
 
 
+def measure_shapes(steps, warmup):
+    """Shapes off the tile grid (K not a whole number of slices, N % 8 != 0)
+    next to the aligned shape of the same size, random N(0,1)/sqrt(K) data."""
+    import torch
+
+    import tiled_matrix_multiplication_gemm_amd as mg
+    from tiled_matrix_multiplication_gemm_amd import inputs
+
+    out = {}
+    for M, N, K, dt in ((4096, 4096, 4096, inputs.F16), (4096, 4096, 4100, inputs.F16),
+                        (8192, 8190, 8192, inputs.BF16)):
+        c = inputs.random_dense(M, N, K, dt, 7000 + K % 97 + N % 89)
+        ld = (N + 7) // 8 * 8
+        A = upload(c.A, dt)
+        Bfull = torch.zeros((K, ld), dtype=A.dtype, device="cuda")
+        Bfull[:, :N] = upload(c.B, dt)
+        B = Bfull[:, :N]
+        Cfull = torch.empty((M, ld), dtype=A.dtype, device="cuda")
+        C = Cfull[:, :N]
+        if K % 8:  # a row stride that spans whole 16-byte chunks
+            Afull = torch.zeros((M, (K + 7) // 8 * 8), dtype=A.dtype, device="cuda")
+            Afull[:, :K] = A
+            A = Afull[:, :K]
+        fn = lambda: mg.mg_gemm(A, B, out=C)
+        _, mean_ms, _, per = time_calls(fn, steps, warmup, per_call=True)
+        fl = 2.0 * M * N * K
+        out["gemm_%dx%dx%d_%s" % (M, N, K, "bf16" if dt else "f16")] = {
+            "kernel_tflops": round(fl / (mean_ms * 1e-3) / 1e12, 2), "kernel_ms_mean": round(mean_ms, 5),
+            "warm_ms": spread(per), "kernel": mg.mg_last_kernel(),
+            "tile_config": mg.mg_config_info(mg.mg_last_config())["name"]}
+        del A, B, C, Bfull, Cfull
+    return out
+
+
+def measure_prepack(steps, warmup):
+    """The layout planner: the blocked A [ceil(K/BK), M, BK] on the same
+    kernel against the row-major A, and the cost of the blocking copy."""
+    import torch
+
+    import tiled_matrix_multiplication_gemm_amd as mg
+    from tiled_matrix_multiplication_gemm_amd import inputs
+
+    out = {}
+    for name in ("gemm_1024x1024x2048_f16", "gemm_8192_bf16"):
+        c = inputs.dense_workload(name, "float")
+        A, B = upload(c.A, c.dtype), upload(c.B, c.dtype)
+        C = torch.empty((c.M, c.N), dtype=A.dtype, device="cuda")
+        BK = mg.mg_config_bk(c.M, c.N, c.K, c.dtype)
+        Ap = mg.mg_prepack_a(A, BK)
+        n = max(steps, 50) if c.M < 4096 else steps
+        _, plain, _, pp = time_calls(lambda: mg.mg_gemm(A, B, out=C), n, warmup, per_call=True)
+        _, packed, _, pk = time_calls(lambda: mg.mg_gemm_prepacked(Ap, BK, B, c.M, c.K, out=C), n, warmup,
+                                      per_call=True)
+        kern = mg.mg_last_kernel()
+        _, copy, _, pc = time_calls(lambda: mg.mg_prepack_a(A, BK, out=Ap), n, warmup, per_call=True)
+        out[name] = {"plain_ms": spread(pp), "packed_ms": spread(pk), "prepack_copy_ms": spread(pc),
+                     "packed_kernel": kern, "bk": BK,
+                     "planner": {"uses_to_pay": mg.mg_prepack_uses_to_pay(c.M, c.N, c.K, c.dtype)}}
+        del A, B, C, Ap
+    return out
+
+
+def oracle_timing():
+    """The oracle per workload on this host (a reported baseline): the full
+    output of the 256^3 and 1024x1024x2048 workloads (median of 3 runs), the
+    4096-element sample of the 8192^3 and grouped ones, each with all cores
+    the process may use (at most 16) and with one; sampled figures are
+    extrapolated to the full problem and labelled so."""
+    import statistics
+
+    import numpy as np
+
+    import oracle
+    from oracle import compare
+    from tiled_matrix_multiplication_gemm_amd import inputs
+
+    out = {}
+    many = oracle.default_threads()
+    for name in ("gemm_256_f16", "gemm_1024x1024x2048_f16", "gemm_bias_relu_1024x1024x2048_f16"):
+        c = inputs.dense_workload(name, "float")
+        rec = {}
+        for label, th in (("threads_%d" % many, many), ("threads_1", 1)):
+            ts = []
+            for _ in range(3):
+                t0 = time.perf_counter()
+                oracle.gemm(c.A, c.B, c.dtype, bias=c.bias, relu=c.relu, nthreads=th)
+                ts.append(time.perf_counter() - t0)
+            t = statistics.median(ts)
+            rec[label] = {"s": round(t, 4), "gflops": round(2.0 * c.M * c.N * c.K / t / 1e9, 3)}
+        out[name] = dict(rec, sample="full output, median of 3")
+    c = inputs.dense_workload("gemm_8192_bf16", "float")
+    w = inputs.DENSE_WORKLOADS["gemm_8192_bf16"]
+    rows, cols = compare.sample_positions(c.M, c.N, 4096, w["seed_sample"])
+    rec = {}
+    for label, th in (("threads_%d" % many, many), ("threads_1", 1)):
+        t0 = time.perf_counter()
+        oracle.gemm_sampled(c.A, c.B, c.dtype, rows, cols, nthreads=th)
+        t = time.perf_counter() - t0
+        g = 2.0 * 4096 * c.K / t / 1e9
+        rec[label] = {"s": round(t, 4), "gflops": round(g, 3),
+                      "extrapolated_full_s": round(2.0 * c.M * c.N * c.K / (g * 1e9), 1)}
+    out["gemm_8192_bf16"] = dict(rec, sample="4096 sampled outputs (times include decoding the inputs)")
+    g = inputs.grouped_workload("grouped_moe_e32_t8192_k1024_n4096_f16", "float")
+    wg = inputs.GROUPED_WORKLOADS["grouped_moe_e32_t8192_k1024_n4096_f16"]
+    rows, cols = compare.sample_positions(g.T, g.N, 4096, wg["seed_sample"])
+    t0 = time.perf_counter()
+    oracle.grouped_sampled(g.X, g.W, g.offsets, g.dtype, rows, cols)
+    t = time.perf_counter() - t0
+    gf = 2.0 * 4096 * g.K / t / 1e9
+    out["grouped_moe_e32_t8192_k1024_n4096_f16"] = {
+        "threads_1": {"s": round(t, 4), "gflops": round(gf, 3),
+                      "extrapolated_full_s": round(2.0 * g.T * g.N * g.K / (gf * 1e9), 1)},
+        "sample": "4096 sampled outputs, one thread (times include decoding the inputs)"}
+    del np
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -415,15 +542,17 @@ def main():
         line["roofline"]["peak_at_clock"] = round(peak_clk, 1)
         line["roofline"]["frac_at_clock"] = round(achieved / peak_clk, 4)
     sys.stdout.flush()
+    line["roofline"]["warm_ms"] = main_res["spread"]
     if not args.no_also:
         also = {}
-        for name in ("gemm_1024x1024x2048_f16", "gemm_bias_relu_1024x1024x2048_f16"):
+        for name in ("gemm_256_f16", "gemm_1024x1024x2048_f16", "gemm_bias_relu_1024x1024x2048_f16"):
             r = measure_dense(name, max(args.steps, 50), max(args.warmup, 10))
             ach = r["flops"] / (r["kernel_ms"] * 1e-3) / 1e12
             cmed, cp90 = (None, None) if args.no_cold else time_cold(r["fn"], 100)
             also[name] = {"tflops": round(r["flops"] * max(args.steps, 50) / r["wall"] / 1e12, 2),
                           "kernel_tflops": round(ach, 2), "frac_mfma_peak": round(ach / PEAK_MFMA_TFLOPS, 4),
-                          "kernel_ms_mean": round(r["kernel_ms"], 5), "tile_config": r["tile_config"],
+                          "kernel_ms_mean": round(r["kernel_ms"], 5), "warm_ms": r["spread"],
+                          "tile_config": r["tile_config"], "kernel": r["kernel"],
                           "cold_kernel_ms_median": cmed and round(cmed, 5), "cold_kernel_ms_p90": cp90 and round(cp90, 5)}
         gname = "grouped_moe_e32_t8192_k1024_n4096_f16"
         r = measure_grouped(gname, args.steps, args.warmup)
@@ -432,15 +561,20 @@ def main():
         also[gname] = {"tflops": round(r["flops"] * args.steps / r["wall"] / 1e12, 2),
                        "kernel_tflops": round(ach, 2), "frac_mfma_peak": round(ach / PEAK_MFMA_TFLOPS, 4),
                        "hbm_gbs_compulsory": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
-                       "kernel_ms_mean": round(r["kernel_ms"], 5), "tile_config": r["tile_config"]}
+                       "kernel_ms_mean": round(r["kernel_ms"], 5), "warm_ms": r["spread"],
+                       "tile_config": r["tile_config"]}
         if not args.no_cold:
             cmed, cp90 = time_cold(r["fn"], 20)
             also[gname]["cold_kernel_ms_median"] = round(cmed, 5)
             also[gname]["cold_kernel_ms_p90"] = round(cp90, 5)
         also.update(measure_consumers(min(args.steps, 50), min(args.warmup, 10)))
+        also["off_grid_shapes"] = measure_shapes(min(args.steps, 50), min(args.warmup, 10))
+        also["layout_planner"] = measure_prepack(min(args.steps, 50), min(args.warmup, 10))
         line["also"] = also
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(c, args.cpu_seconds)
+        if not args.no_also:
+            line["cpu_baseline"]["per_workload"] = oracle_timing()
     print(json.dumps(line))
     sys.stdout.flush()
 

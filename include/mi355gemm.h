@@ -221,6 +221,17 @@ mg_status mg_gemm_prepacked(const void* Ap, int64_t BK, const void* B, void* C,
                             int64_t stride_cm, int64_t stride_cn,
                             mg_dtype dtype, hipStream_t stream);
 
+/*
+ * The layout planner's cost/benefit test ("Using Triton to optimise GEMM
+ * across chips", section 3.2: re-lay A out only when the gain exceeds the cost
+ * of the copy).  For an M x N x K GEMM on the row the table selects: the
+ * number of GEMMs that must share one blocked A (mg_prepack_a) before the
+ * blocking copy has paid for itself, from the packed/plain time ratio and
+ * the copy rate that the offline sweep measured; -1 when the blocked layout
+ * is not faster on that row (then prepacking never pays).  Host only.
+ */
+int64_t mg_prepack_uses_to_pay(int64_t M, int64_t N, int64_t K, mg_dtype dtype);
+
 /* ---- GEMM consumers ------------------------------------------------------- */
 
 /*
@@ -343,7 +354,10 @@ int mg_last_config(void);
  * process: 0 = general register-staged kernel, 1 = direct-to-LDS pipelined
  * kernel, 2 = direct-to-LDS K-split kernel; -1 before any launch. */
 int mg_last_kernel(void);
-/* Configuration the table selects for a dense problem of this shape. */
+/* Configuration the table selects for a problem of this shape: dense when
+ * `grouped` is 0, else a grouped problem of `grouped` experts over M = T
+ * rows.  The table's model and its per-shape cache are generated by the
+ * offline sweep (mg_rates.h from profiles/table_sweep.json). */
 int mg_select_config(int64_t M, int64_t N, int64_t K, mg_dtype dtype, int grouped);
 
 #ifdef __cplusplus

@@ -1,0 +1,128 @@
+"""The configuration table is a product of the offline sweep.
+
+profiles/table_sweep.json holds the times of every row on every swept shape
+(measured on MI355X by `sweep run`); csrc/mg_rates.h is generated from it by
+`sweep fit`.  These CPU tests check that the committed header is exactly
+what the fit produces from the committed JSON, that the compiled library
+picks the measured best row for every swept shape, that off-sweep shapes get
+the model's choice (recomputed here in Python from the JSON alone), and that
+the split-K count and the layout planner's decision follow the same model.
+"""
+import json
+import math
+import os
+
+import pytest
+
+import tiled_matrix_multiplication_gemm_amd as mg
+from tiled_matrix_multiplication_gemm_amd import sweep
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def data():
+    with open(os.path.join(ROOT, "profiles", "table_sweep.json")) as f:
+        return json.load(f)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(mg.LIB_PATH):
+        pytest.skip("library not built")
+    L = mg.lib()
+    L.mg_set_config(-1)
+    return L
+
+
+def test_header_is_generated_from_the_json(data):
+    with open(sweep.HEADER) as f:
+        assert f.read() == sweep.header_text(data, os.path.relpath(sweep.DEFAULT_JSON, sweep.ROOT))
+
+
+def test_every_swept_shape_takes_its_measured_best_row(data, L):
+    S = sweep.summarize(data)
+    for b in S["dense_best"]:
+        ms = {int(r): t for r, t in next(r for r in data["dense"] if (r["M"], r["N"], r["K"]) ==
+                                         (b["M"], b["N"], b["K"]))["ms"].items()}
+        assert ms[b["best_row"]] == min(ms[r] for r in ms if r in (0, 1, 2, 3, 4, 6, 8))
+        assert L.mg_select_config(b["M"], b["N"], b["K"], b["dtype"], 0) == b["best_row"], b
+    for b in S["grouped_best"]:
+        assert L.mg_select_config(b["T"], b["N"], b["K"], b["dtype"], b["E"]) == b["best_row"], b
+
+
+OFF_SWEEP = [(8192, 4096, 4096), (777, 1300, 960), (100000, 96, 2048), (64, 64, 64), (2560, 2560, 2560),
+             (16384, 16384, 1024), (300, 9000, 4096), (1, 1, 1)]
+
+
+@pytest.mark.parametrize("M,N,K", OFF_SWEEP)
+def test_off_sweep_shapes_take_the_models_choice(data, L, M, N, K):
+    F = sweep.fit(data)
+    assert L.mg_select_config(M, N, K, 0, 0) == sweep.model_pick(data, F, M, N, K)
+
+
+@pytest.mark.parametrize("E,T,N,K", [(4, 1000, 512, 256), (128, 65536, 2048, 1024), (32, 8192, 1024, 4096)])
+def test_grouped_shapes_take_the_models_choice(data, L, E, T, N, K):
+    F = sweep.fit(data)
+    assert L.mg_select_config(T, N, K, 0, E) == sweep.model_pick(data, F, T, N, K, E)
+
+
+def _py_splitk_choose(data, M, N, K):
+    F = sweep.fit(data)
+    S = sweep.summarize(data)
+    rows = [x for x in sweep._model_rows(data) if x[0] in (0, 1, 2)]
+    best_s, best_t = 1, 0.0
+    s = 1
+    while s <= 64:
+        if s > 1 and K // s < 256:
+            break
+        t = min(sweep.model_seconds(F, bm, bn, r, sweep._cdiv(sweep._cdiv(M, bm) * sweep._cdiv(N, bn) * s, 256),
+                                    sweep._cdiv(K, s)) for (r, bm, bn) in rows)
+        if s > 1:
+            t += 2.0 * s * M * N * 4.0 / S["splitk"]["partial_bytes_per_s"]
+        if best_t == 0.0 or t < best_t * 0.95:
+            best_t, best_s = t, s
+        s *= 2
+    return best_s
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 65536), (512, 512, 32768), (1024, 1024, 16384), (128, 4096, 16384),
+                                   (2048, 2048, 16384), (1024, 1024, 2048), (8192, 8192, 8192)])
+def test_split_count_follows_the_model(data, L, M, N, K):
+    assert L.mg_splitk_choose(M, N, K) == _py_splitk_choose(data, M, N, K)
+
+
+def test_split_choice_against_the_measured_times(data, L):
+    """Where the sweep timed split counts, the chosen count is within 35 % of
+    the fastest measured one, and never splits an output that fills the GPU."""
+    for rec in data["splitk"]:
+        ms = {int(s): t for s, t in rec["ms"].items()}
+        s = L.mg_splitk_choose(rec["M"], rec["N"], rec["K"])
+        if s in ms:
+            assert ms[s] <= 1.35 * min(ms.values()), (rec, s)
+    assert L.mg_splitk_choose(8192, 8192, 8192) == 1
+
+
+def test_layout_planner_gate(data, L):
+    """The planner prepacks only where the sweep measured the blocked A
+    faster on the chosen row, after enough reuses to pay for the copy."""
+    S = sweep.summarize(data)
+    ratio = {int(r): v for r, v in S["packed_ratio"].items()}
+    F = S["fit"]
+    rows = {r: (bm, bn) for (r, bm, bn) in sweep._model_rows(data)}
+    for (M, N, K) in [(1024, 1024, 2048), (8192, 8192, 8192), (4096, 4096, 4096), (2048, 2048, 2048),
+                      (12544, 256, 2304), (65536, 64, 1152), (777, 1300, 960)]:
+        got = L.mg_prepack_uses_to_pay(M, N, K, 0)
+        row = L.mg_select_config(M, N, K, 0, 0)
+        if ratio.get(row, -1.0) <= 0.0 or ratio[row] >= 1.0:
+            assert got == -1, (M, N, K, row)
+            continue
+        bm, bn = rows[row]
+        t = sweep.model_seconds(F, bm, bn, row, sweep._cdiv(sweep._cdiv(M, bm) * sweep._cdiv(N, bn), 256), K)
+        bk = mg.mg_config_info(row)["bk"]
+        copy = (2.0 * M * K + 2.0 * sweep._cdiv(K, bk) * M * bk) / S["copy_bytes_per_s"]
+        want = math.ceil(copy / (t * (1.0 - ratio[row])))
+        assert got == want and got > 1, (M, N, K, got, want)
+    # the two workloads' rows measured the blocked A slower: never prepack
+    assert L.mg_prepack_uses_to_pay(1024, 1024, 2048, 0) == -1
+    assert L.mg_prepack_uses_to_pay(8192, 8192, 8192, 1) == -1

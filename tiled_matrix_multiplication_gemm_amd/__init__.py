@@ -44,7 +44,7 @@ EXPORTED = (
     "mg_prepack_a", "mg_config_bk", "mg_gemm_prepacked", "mg_num_configs", "mg_config_info",
     "mg_set_config", "mg_last_config", "mg_select_config", "mg_conv2d_output_hw", "mg_im2col",
     "mg_conv2d_workspace_bytes", "mg_conv2d", "mg_attention_scores", "mg_splitk_noalloc_max_bytes",
-    "mg_gemm_splitk_noalloc", "mg_last_kernel",
+    "mg_gemm_splitk_noalloc", "mg_last_kernel", "mg_prepack_uses_to_pay",
 )
 
 
@@ -105,6 +105,8 @@ def lib() -> ctypes.CDLL:
         L.mg_set_config.argtypes = [cint]
         L.mg_last_config.restype = cint
         L.mg_last_config.argtypes = []
+        L.mg_prepack_uses_to_pay.restype = i64
+        L.mg_prepack_uses_to_pay.argtypes = [i64, i64, i64, cint]
         L.mg_last_kernel.restype = cint
         L.mg_last_kernel.argtypes = []
         L.mg_select_config.restype = cint
@@ -375,6 +377,16 @@ def mg_gemm_prepacked(ap, BK: int, b, M: int, K: int, out=None):
     return out
 
 
+def mg_prepack_uses_to_pay(M: int, N: int, K: int, dtype: int = MG_F16) -> int:
+    """GEMMs sharing one blocked A after which prepacking pays (-1: never)."""
+    return int(lib().mg_prepack_uses_to_pay(M, N, K, dtype))
+
+
+def mg_select_config(M: int, N: int, K: int, dtype: int = MG_F16, grouped: int = 0) -> int:
+    """The table's row for a dense problem, or a grouped one of `grouped` experts."""
+    return int(lib().mg_select_config(M, N, K, dtype, int(grouped)))
+
+
 def mg_num_configs() -> int:
     return int(lib().mg_num_configs())
 
@@ -403,8 +415,6 @@ def mg_last_kernel() -> str | None:
     return KERNEL_FAMILIES[int(lib().mg_last_kernel())]
 
 
-def mg_select_config(M: int, N: int, K: int, dtype: int = MG_F16, grouped: bool = False) -> int:
-    return int(lib().mg_select_config(M, N, K, dtype, int(bool(grouped))))
 
 
 # ---- GEMM consumers --------------------------------------------------------

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cmath>
 #include <mutex>
 #include <type_traits>
 #include <stdint.h>
@@ -11,6 +12,7 @@
 #include "mi355gemm.h"
 #include "mg_im2col.h"
 #include "mg_table.h"
+#include "mg_rates.h"
 
 namespace {
 
@@ -43,64 +45,71 @@ std::atomic<int> g_last_kernel{-1};
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Row choice for dense problems: a workgroup's tile runs on one CU, and the
-// tiles run in rounds of 256 (one per CU), so the time of a row is modelled
-// as rounds * (BM * BN / rate), with `rate` the row's measured per-CU output
-// rate relative to 256x256 tiles (offline sweeps on MI355X: 8192^3 bf16 for
-// the square rows, a grid of tall thin fp16 shapes, M 12544..100352, N 64..256,
-// K 576..4608, for the 256x64 row).  Large outputs get 256x256 tiles, outputs
-// too small to give every CU one of them get smaller tiles (1024 x 1024 ->
-// 64x64), tall outputs of 64 or 128 columns get 256x64 slabs.  Grouped GEMMs use the
-// 256x256 row (each expert's weight slab is read by one or two tiles).  A
-// batched product counts the tiles of every entry.
-int select_config(int64_t M, int64_t N, int64_t K, int grouped, int64_t batch = 1) {
-    (void)K;
+// Row choice.  A workgroup's tile runs on one CU, and the tiles run in
+// rounds of 256 (one per CU), so the time of a row is modelled as
+// rounds * (BM * BN * K * kSecPerElemK / rate + kFixedSec), with the row's
+// per-CU output rate, the seconds per output element and k, and the fixed
+// time per tile fitted by the offline sweep (mg_rates.h, generated from
+// profiles/table_sweep.json).  A shape the sweep timed takes the row that
+// measured fastest on it (the cached top-1 of "Using Triton to optimise GEMM
+// across chips", section 3.3).  Grouped problems count the tiles of E
+// experts with T / E rows each (the host does not read the device offsets);
+// a batched product counts the tiles of every entry.
+double model_seconds(const rates::RowRate& r, int64_t tiles, int64_t K) {
+    return (double)cdiv(tiles, 256) * ((double)r.bm * r.bn * (double)K * rates::kSecPerElemK / r.rate +
+                                       rates::kFixedSec);
+}
+
+int64_t tiles_of(const rates::RowRate& r, int64_t M, int64_t N, int64_t experts, int64_t batch) {
+    if (experts > 0) return experts * cdiv(cdiv(M, experts), r.bm) * cdiv(N, r.bn);
+    return cdiv(M, r.bm) * cdiv(N, r.bn) * (batch > 1 ? batch : 1);
+}
+
+int select_config(int64_t M, int64_t N, int64_t K, int64_t experts, int64_t batch = 1) {
     int forced = g_forced.load();
     if (forced >= 0) return forced;
-    if (grouped) return 0;
-    struct Cand {
-        int id, bm, bn;
-        double rate;
-    };
-    static const Cand cands[] = {{0, 256, 256, 1.00}, {3, 128, 256, 0.76}, {4, 256, 128, 0.68},
-                                 {1, 128, 128, 0.49}, {2, 64, 64, 0.50},  {8, 256, 64, 0.65}};
-    constexpr int64_t kCUs = 256;
-    int best = 0;
-    double best_t = 0.0;
-    for (const Cand& c : cands) {
-        const int64_t tiles = cdiv(M, c.bm) * cdiv(N, c.bn) * (batch > 1 ? batch : 1);
-        const double t = (double)cdiv(tiles, kCUs) * ((double)c.bm * c.bn / c.rate);
-        if (best_t == 0.0 || t < best_t) {
+    if (batch <= 1) {
+        for (const rates::Swept& sw : rates::kSwept)
+            if (sw.M == M && sw.N == N && sw.K == K && sw.experts == experts) return sw.row;
+    }
+    int best = rates::kRows[0].id;
+    double best_t = -1.0;
+    for (const rates::RowRate& r : rates::kRows) {
+        const double t = model_seconds(r, tiles_of(r, M, N, experts, batch), K);
+        if (best_t < 0.0 || t < best_t) {
             best_t = t;
-            best = c.id;
+            best = r.id;
         }
     }
     return best;
 }
 
-// Split-K rows: those with a direct-to-LDS kernel for small and mid-size
-// tiles, chosen by the same rounds x tile-rate model with the tiles of every
-// split counted (each split runs K / splits of the product).
-int select_config_splitk(int64_t M, int64_t N, int64_t splits) {
-    int forced = g_forced.load();
-    if (forced >= 0) return forced;
-    struct Cand {
-        int id, bm, bn;
-        double rate;
-    };
-    static const Cand cands[] = {{0, 256, 256, 1.00}, {1, 128, 128, 0.49}, {2, 64, 64, 0.50}};
-    constexpr int64_t kCUs = 256;
-    int best = 2;
-    double best_t = 0.0;
-    for (const Cand& c : cands) {
-        const int64_t tiles = cdiv(M, c.bm) * cdiv(N, c.bn) * splits;
-        const double t = (double)cdiv(tiles, kCUs) * ((double)c.bm * c.bn / c.rate);
-        if (best_t == 0.0 || t < best_t) {
+// Split-K runs on the rows whose fast kernel serves small and mid-size
+// tiles (0, 1, 2), chosen by the same model with the tiles of every split
+// counted and K / splits per tile.
+bool splitk_row(int id) { return id == 0 || id == 1 || id == 2; }
+
+double splitk_seconds(int64_t M, int64_t N, int64_t K, int64_t splits, int* row) {
+    double best_t = -1.0;
+    for (const rates::RowRate& r : rates::kRows) {
+        if (!splitk_row(r.id)) continue;
+        const double t = model_seconds(r, tiles_of(r, M, N, 0, 1) * splits, cdiv(K, splits));
+        if (best_t < 0.0 || t < best_t) {
             best_t = t;
-            best = c.id;
+            if (row) *row = r.id;
         }
     }
-    return best;
+    // the fp32 partials, written and read back
+    if (splits > 1) best_t += 2.0 * (double)splits * (double)M * (double)N * 4.0 / rates::kPartialBytesPerSec;
+    return best_t;
+}
+
+int select_config_splitk(int64_t M, int64_t N, int64_t K, int64_t splits) {
+    int forced = g_forced.load();
+    if (forced >= 0) return forced;
+    int row = 2;
+    splitk_seconds(M, N, K, splits, &row);
+    return row;
 }
 
 // ---- validation --------------------------------------------------------------
@@ -433,35 +442,47 @@ mg_status mg_gemm_batched(const void* A, const void* B, void* C, int64_t batch, 
 }
 
 int64_t mg_splitk_choose(int64_t M, int64_t N, int64_t K) {
-    // Time model per split count s (seconds): rounds of 256 tiles, each tile
-    // BM*BN*(K/s) outputs-times-k at the row's relative rate (a 256x256x8192
-    // tile takes 0.205 ms on MI355X) plus 3 us of fill and drain, and for
-    // s > 1 the partials written and read back at 4 TB/s plus a launch.
+    // the split count of least modelled time (mg_rates.h: the rows' fitted
+    // tile times and the measured rate of writing and reading the fp32
+    // partials); a split must win by 5 %, and runs keep at least 256 of K
     if (M <= 0 || N <= 0 || K <= 0) return 1;
-    struct Cand {
-        int bm, bn;
-        double rate;
-    };
-    static const Cand cands[] = {{256, 256, 1.00}, {128, 128, 0.49}, {64, 64, 0.50}};
-    const double per_elem_k = 0.205e-3 / (65536.0 * 8192.0);
     int64_t best_s = 1;
     double best_t = 0.0;
     for (int64_t s = 1; s <= 64; s *= 2) {
-        if (s > 1 && K / s < 256) break;  // keep at least a few slices per run
-        double t = 0.0;
-        for (const Cand& c : cands) {
-            const int64_t tiles = cdiv(M, c.bm) * cdiv(N, c.bn) * s;
-            const double tt = (double)cdiv(tiles, 256) *
-                              ((double)c.bm * c.bn / c.rate * ((double)K / s) * per_elem_k + 3e-6);
-            if (t == 0.0 || tt < t) t = tt;
-        }
-        if (s > 1) t += 2.0 * s * M * N * 4.0 / 4e12 + 3e-6;
-        if (best_t == 0.0 || t < best_t * 0.95) {  // a split must win by 5 %
+        if (s > 1 && K / s < 256) break;
+        const double t = splitk_seconds(M, N, K, s, nullptr);
+        if (best_t == 0.0 || t < best_t * 0.95) {
             best_t = t;
             best_s = s;
         }
     }
     return best_s;
+}
+
+int64_t mg_prepack_uses_to_pay(int64_t M, int64_t N, int64_t K, mg_dtype dtype) {
+    // The layout planner's cost/benefit test ("Using Triton to optimise GEMM
+    // across chips", section 3.2: re-lay A out only when the gain exceeds the
+    // copy): the gain per call is the modelled time of the chosen row times
+    // (1 - packed/plain time ratio measured by the sweep), the cost is the
+    // blocking copy (read A, write the blocked copy) at the copy rate the
+    // sweep measured.  Returns the number of GEMMs sharing one blocked A
+    // after which the copy has paid for itself, or -1 when the blocked
+    // layout is not faster on this row.
+    (void)dtype;
+    if (M <= 0 || N <= 0 || K <= 0) return -1;
+    const int cfg = select_config(M, N, K, 0);
+    if (cfg < 0 || cfg >= kNumConfigs) return -1;
+    const double ratio = rates::kPackedRatio[cfg];
+    if (ratio <= 0.0 || ratio >= 1.0) return -1;
+    double t_plain = -1.0;
+    for (const rates::RowRate& r : rates::kRows)
+        if (r.id == cfg) t_plain = model_seconds(r, tiles_of(r, M, N, 0, 1), K);
+    if (t_plain <= 0.0) return -1;
+    const int64_t bk = kTable[cfg].bk;
+    const double copy = (2.0 * (double)M * (double)K + 2.0 * (double)cdiv(K, bk) * (double)M * (double)bk) /
+                        rates::kCopyBytesPerSec;
+    const double gain = t_plain * (1.0 - ratio);
+    return (int64_t)std::ceil(copy / gain);
 }
 
 size_t mg_splitk_workspace_bytes(int64_t M, int64_t N, int64_t splits) {
@@ -493,7 +514,7 @@ mg_status splitk_launch(const void* A, const void* B, void* C, void* workspace, 
                         int64_t K, int64_t stride_am, int64_t stride_ak, int64_t stride_bk, int64_t stride_bn,
                         int64_t stride_cm, mg_dtype in_dtype, int ta, int tb, hipStream_t stream,
                         bool dry = false) {
-    const int cfg = select_config_splitk(M, N, splits);
+    const int cfg = select_config_splitk(M, N, K, splits);
     if (cfg < 0 || cfg >= kNumConfigs) return MG_ERR_BAD_CONFIG;
     KArgs a{};
     a.A = (const uint16_t*)A;
@@ -592,7 +613,7 @@ mg_status mg_grouped_gemm(const void* X, const void* W, void* Y, const int32_t* 
     }
     if (T == 0 || N == 0) return MG_OK;
     if (expert_offsets == nullptr) return MG_ERR_INVALID_ARG;
-    const int cfg = select_config(T, N, K, 1);
+    const int cfg = select_config(T, N, K, E > 0 ? E : 1);
     if (cfg < 0 || cfg >= kNumConfigs) return MG_ERR_BAD_CONFIG;
     KArgs a{};
     a.A = (const uint16_t*)X;
@@ -686,7 +707,7 @@ int mg_last_kernel(void) { return g_last_kernel.load(); }
 
 int mg_select_config(int64_t M, int64_t N, int64_t K, mg_dtype dtype, int grouped) {
     (void)dtype;
-    return select_config(M, N, K, grouped);
+    return select_config(M, N, K, grouped > 0 ? grouped : 0);
 }
 
 mg_status mg_conv2d_output_hw(const mg_conv2d_shape* shape, int64_t* out_h, int64_t* out_w) {

@@ -1,107 +1,434 @@
-"""Offline sweep of the configuration table on the GPU.
+"""Offline sweep of the configuration table, and the table generated from it.
 
-  python -m tiled_matrix_multiplication_gemm_amd.sweep [--rounds 5] [--out FILE] [workload ...]
+  python -m tiled_matrix_multiplication_gemm_amd.sweep run [--out profiles/table_sweep.json] [--rounds 3]
+  python -m tiled_matrix_multiplication_gemm_amd.sweep fit [--json profiles/table_sweep.json]
+  python -m tiled_matrix_multiplication_gemm_amd.sweep check
 
-Times every table row on each workload through the C ABI (forcing the row
-with mg_set_config), visiting the rows round-robin for several rounds so that
-clock drift and warm-up do not favour the rows measured last, and reports
-the median kernel time per row.  The results are the evidence behind the
-shape classes of select_config() in csrc/mg_api.hip.  Inputs are the
-workloads' seeded float inputs.
+The pages tune a GEMM by benchmarking candidate configurations on the target
+and keeping the best one ("Using Triton to optimise GEMM across chips",
+section 3.3: top-1 per shape, cached; FlagOS cross-chip page, section 5.2:
+target description -> candidates -> compile and time -> pick -> store).
+Here the candidates are the compiled rows of the table and the picking is
+done once, offline:
+
+`run` (GPU) times every row on a grid of shapes -- the five workloads,
+squares, tall-skinny and wide outputs, large K, shapes off the tile grid,
+grouped (MoE) problems -- forcing each row through mg_set_config and visiting
+the rows round-robin so that clock drift does not favour the rows measured
+last; it also times split-K counts on the under-filled shapes, the prepacked
+A against the row-major A, and a plain copy (HBM rate).  Raw times go to a
+JSON file.
+
+`fit` (CPU) fits the time model of select_config() to those times -- per row
+t = rounds * (BM * BN * K * c / rate_row + f), rounds = ceil(tiles / 256),
+one tile per CU at a time -- and writes csrc/mg_rates.h: the fitted per-row
+rates, c and f, the copy rate, the prepacked/plain time ratio per row, and
+the measured best row of every swept shape, which select_config() returns
+for that exact shape (the cache of the pages' top-1) before it consults the
+model.  The fit and the generated header are both functions of the JSON
+alone; `check` regenerates the header and compares it with the committed
+one.
 """
 from __future__ import annotations
 
 import argparse
+import json
+import math
 import os
 import statistics
 import sys
 
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+DEFAULT_JSON = os.path.join(ROOT, "profiles", "table_sweep.json")
+HEADER = os.path.join(PKG, "csrc", "mg_rates.h")
+CUS = 256
 
-def _upload(bits, dt):
-    import numpy as np
+F16, BF16 = 0, 1
+# (M, N, K, dtype): the dense shape grid
+DENSE_SHAPES = [
+    (256, 256, 256, F16), (1024, 1024, 2048, F16), (8192, 8192, 8192, BF16),      # the dense workloads
+    (512, 512, 512, F16), (1024, 1024, 1024, F16), (2048, 2048, 2048, F16), (4096, 4096, 4096, BF16),
+    (3072, 3072, 3072, F16), (2048, 2048, 8192, BF16), (4096, 1024, 4096, F16), (1024, 4096, 4096, F16),
+    (16384, 128, 4096, F16), (65536, 64, 1152, F16), (25088, 128, 1152, F16), (100352, 64, 576, F16),
+    (12544, 256, 2304, F16), (256, 16384, 4096, F16), (128, 4096, 16384, BF16),  # tall-skinny and wide
+    (256, 256, 65536, BF16), (512, 512, 32768, BF16), (1024, 1024, 16384, F16),  # large K
+    (4096, 4096, 4100, F16), (8192, 8190, 8192, BF16), (1000, 1000, 1000, F16), (3000, 5000, 4096, BF16),
+]
+# (E, T, N, K, dtype): grouped problems, balanced routing drawn like the MoE workload
+GROUPED_SHAPES = [(32, 8192, 4096, 1024, F16), (8, 2048, 1024, 1024, F16), (64, 16384, 1408, 2048, BF16),
+                  (16, 4096, 2048, 512, F16)]
+SPLIT_SHAPES = [(256, 256, 65536, BF16), (512, 512, 32768, BF16), (1024, 1024, 16384, F16),
+                (128, 4096, 16384, BF16), (2048, 2048, 16384, BF16), (1024, 1024, 2048, F16)]
+PACKED_SHAPES = [(1024, 1024, 2048, F16), (4096, 4096, 4096, BF16), (8192, 8192, 8192, BF16)]
+SPLITS = [1, 2, 4, 8, 16]
+
+
+# ---- GPU side -------------------------------------------------------------------
+def _time(fn, target_ms=4.0, rounds=1):
+    """Median per-call ms over `rounds` batches of back-to-back calls (HIP
+    events around each batch, so launch gaps are those of a stream of calls)."""
     import torch
 
-    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda()
-    return t.view(torch.float16 if dt == 0 else torch.bfloat16)
+    fn()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    fn()
+    e.record()
+    torch.cuda.synchronize()
+    one = max(s.elapsed_time(e), 1e-3)
+    reps = int(min(200, max(3, target_ms / one)))
+    out = []
+    for _ in range(rounds):
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        out.append(s.elapsed_time(e) / reps)
+    return statistics.median(out)
 
 
-def _setup(name):
+def _dense_tensors(M, N, K, dt, seed):
+    import torch
+
+    from tiled_matrix_multiplication_gemm_amd import inputs
+
+    c = inputs.random_dense(M, N, K, dt, seed)
+    tdt = torch.float16 if dt == F16 else torch.bfloat16
+
+    def padded(bits, rows, cols):
+        import numpy as np
+
+        ld = (cols + 7) // 8 * 8
+        full = np.zeros((rows, ld), dtype=np.uint16)
+        full[:, :cols] = bits
+        return torch.from_numpy(full.view(np.int16)).cuda().view(tdt)[:, :cols]
+
+    A, B = padded(c.A, M, K), padded(c.B, K, N)
+    C = torch.empty((M, (N + 7) // 8 * 8), dtype=tdt, device="cuda")[:, :N]
+    return A, B, C
+
+
+def run(out_path, rounds):
     import numpy as np
     import torch
 
     import tiled_matrix_multiplication_gemm_amd as mg
     from tiled_matrix_multiplication_gemm_amd import inputs
 
-    if name in inputs.GROUPED_WORKLOADS:
-        c = inputs.grouped_workload(name)
-        X, W = _upload(c.X, c.dtype), _upload(c.W, c.dtype)
-        off = torch.from_numpy(c.offsets.astype(np.int32)).cuda()
-        Y = torch.empty((c.T, c.N), dtype=X.dtype, device="cuda")
-        return (lambda: mg.mg_grouped_gemm(X, W, off, out=Y)), 2.0 * c.T * c.K * c.N
-    c = inputs.dense_workload(name)
-    A, B = _upload(c.A, c.dtype), _upload(c.B, c.dtype)
-    C = torch.empty((c.M, c.N), dtype=A.dtype, device="cuda")
-    if c.bias is not None:
-        bias = _upload(c.bias, c.dtype)
-        return (lambda: mg.mg_gemm_bias_relu(A, B, bias, out=C)), 2.0 * c.M * c.N * c.K
-    return (lambda: mg.mg_gemm(A, B, out=C)), 2.0 * c.M * c.N * c.K
+    rows = [r for r in range(mg.mg_num_configs())]
+    res = {"device": torch.cuda.get_device_name(0), "rounds": rounds, "cus": CUS,
+           "rows": {str(r): mg.mg_config_info(r) for r in rows}, "dense": [], "grouped": [], "splitk": [],
+           "packed": []}
+    for (M, N, K, dt) in DENSE_SHAPES:
+        A, B, C = _dense_tensors(M, N, K, dt, 11 + M % 97 + N % 89 + K % 83)
+        times = {r: [] for r in rows}
+        for rnd in range(rounds):
+            for r in (rows if rnd % 2 == 0 else rows[::-1]):
+                mg.mg_set_config(r)
+                try:
+                    times[r].append(_time(lambda: mg.mg_gemm(A, B, out=C)))
+                finally:
+                    mg.mg_set_config(-1)
+        rec = {"M": M, "N": N, "K": K, "dtype": dt,
+               "ms": {str(r): round(statistics.median(v), 5) for r, v in times.items()},
+               "table_row_at_sweep": mg.mg_select_config(M, N, K, dt)}
+        res["dense"].append(rec)
+        print("dense %5d x %5d x %5d: %s" % (M, N, K, " ".join("%d:%.4f" % (r, float(t)) for r, t in
+                                                           sorted((int(a), b) for a, b in rec["ms"].items()))),
+              flush=True)
+        del A, B, C
+    for (E, T, N, K, dt) in GROUPED_SHAPES:
+        g = inputs.random_grouped(E=E, T=T, K=K, N=N, dtype=dt, seed=300 + E)
+        tdt = torch.float16 if dt == F16 else torch.bfloat16
+        X = torch.from_numpy(np.ascontiguousarray(g.X).view(np.int16)).cuda().view(tdt)
+        W = torch.from_numpy(np.ascontiguousarray(g.W).view(np.int16)).cuda().view(tdt)
+        off = torch.from_numpy(g.offsets.astype(np.int32)).cuda()
+        Y = torch.empty((T, N), dtype=tdt, device="cuda")
+        times = {r: [] for r in rows}
+        for rnd in range(rounds):
+            for r in (rows if rnd % 2 == 0 else rows[::-1]):
+                mg.mg_set_config(r)
+                try:
+                    times[r].append(_time(lambda: mg.mg_grouped_gemm(X, W, off, out=Y)))
+                finally:
+                    mg.mg_set_config(-1)
+        rec = {"E": E, "T": T, "N": N, "K": K, "dtype": dt, "counts": [int(x) for x in g.counts],
+               "ms": {str(r): round(statistics.median(v), 5) for r, v in times.items()}}
+        res["grouped"].append(rec)
+        print("grouped E=%d T=%d N=%d K=%d: %s" % (E, T, N, K, rec["ms"]), flush=True)
+        del X, W, Y
+    for (M, N, K, dt) in SPLIT_SHAPES:
+        A, B, C = _dense_tensors(M, N, K, dt, 77 + K % 101)
+        ms = {}
+        for s in SPLITS:
+            if s == 1:
+                ms["1"] = round(_time(lambda: mg.mg_gemm(A, B, out=C), rounds=rounds), 5)
+            else:
+                ws = torch.empty((mg.mg_splitk_workspace_bytes(M, N, s),), dtype=torch.uint8, device="cuda")
+                ms[str(s)] = round(_time(lambda: mg.mg_gemm_splitk(A, B, splits=s, workspace=ws, out=C),
+                                         rounds=rounds), 5)
+                del ws
+        res["splitk"].append({"M": M, "N": N, "K": K, "dtype": dt, "ms": ms})
+        print("split-K %d x %d x %d: %s" % (M, N, K, ms), flush=True)
+        del A, B, C
+    for (M, N, K, dt) in PACKED_SHAPES:
+        A, B, C = _dense_tensors(M, N, K, dt, 55 + K % 101)
+        rec = {"M": M, "N": N, "K": K, "dtype": dt, "plain_ms": {}, "packed_ms": {}}
+        for r in rows:
+            d = mg.mg_config_info(r)
+            if not d["direct_lds"] or d["direct_ksplit"] > 1:
+                continue
+            mg.mg_set_config(r)
+            try:
+                BK = d["bk"]
+                Ap = mg.mg_prepack_a(A, BK)
+                plain, packed = [], []
+                for rnd in range(rounds):
+                    plain.append(_time(lambda: mg.mg_gemm(A, B, out=C)))
+                    packed.append(_time(lambda: mg.mg_gemm_prepacked(Ap, BK, B, M, K, out=C)))
+                rec["plain_ms"][str(r)] = round(statistics.median(plain), 5)
+                rec["packed_ms"][str(r)] = round(statistics.median(packed), 5)
+                if r == 0:
+                    rec["copy_ms"] = round(_time(lambda: mg.mg_prepack_a(A, BK, out=Ap), rounds=rounds), 5)
+                    rec["copy_bytes"] = 2 * M * K + 2 * ((K + BK - 1) // BK) * M * BK
+                del Ap
+            finally:
+                mg.mg_set_config(-1)
+        res["packed"].append(rec)
+        print("packed %d x %d x %d: plain %s packed %s copy %s" % (M, N, K, rec["plain_ms"], rec["packed_ms"],
+                                                                 rec.get("copy_ms")), flush=True)
+        del A, B, C
+    n = 1 << 27
+    src = torch.ones(n, dtype=torch.float16, device="cuda")
+    dst = torch.empty_like(src)
+    cms = _time(lambda: dst.copy_(src), rounds=rounds)
+    res["copy"] = {"bytes": 4 * n, "ms": round(cms, 5), "gbs": round(4 * n / (cms * 1e-3) / 1e9, 1)}
+    with open(out_path, "w") as f:
+        json.dump(res, f, indent=1, sort_keys=True)
+    print("wrote", out_path)
 
 
-def _time(fn, reps):
-    import torch
+# ---- the fit (CPU) -------------------------------------------------------------
+def _cdiv(a, b):
+    return -(-a // b)
 
-    s = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
-    e = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
-    for i in range(reps):
-        s[i].record()
-        fn()
-        e[i].record()
-    torch.cuda.synchronize()
-    return statistics.median(a.elapsed_time(b) for a, b in zip(s, e))
+
+def _model_rows(data):
+    """Rows the model chooses among: those with a pipelined direct-to-LDS kernel."""
+    out = []
+    for k, d in sorted(data["rows"].items(), key=lambda kv: int(kv[0])):
+        if d["direct_lds"] and d["direct_ksplit"] == 1:
+            out.append((int(k), d["bm"], d["bn"]))
+    return out
+
+
+def grouped_tiles(T, E, N, bm, bn):
+    """Tiles of a grouped problem with balanced routing (the host does not
+    read the device offsets): E experts of T / E rows each."""
+    rows_per = _cdiv(T, max(E, 1))
+    return max(E, 1) * _cdiv(rows_per, bm) * _cdiv(N, bn)
+
+
+def fit(data):
+    """Per-row relative rates, the seconds per output element and k of a
+    256 x 256 tile (c) and the fixed time per tile (f), fitted to the dense
+    times by alternating least squares on relative error."""
+    rows = _model_rows(data)
+    obs = []  # (row, bm, bn, rounds, K, seconds)
+    for rec in data["dense"]:
+        for (r, bm, bn) in rows:
+            t = rec["ms"].get(str(r))
+            if t is None:
+                continue
+            tiles = _cdiv(rec["M"], bm) * _cdiv(rec["N"], bn)
+            obs.append((r, bm, bn, _cdiv(tiles, data["cus"]), rec["K"], float(t) * 1e-3))
+    rate = {r: 1.0 for (r, _, _) in rows}
+    c, f = 0.205e-3 / (65536.0 * 8192.0), 3e-6
+    for _ in range(50):
+        # c, f by weighted linear least squares on t / rounds = x c + f, weights 1 / t
+        sxx = sx = s1 = sxy = sy = 0.0
+        for (r, bm, bn, rnd, K, t) in obs:
+            x = bm * bn * K / rate[r]
+            y = t / rnd
+            w = 1.0 / (y * y)
+            sxx += w * x * x
+            sx += w * x
+            s1 += w
+            sxy += w * x * y
+            sy += w * y
+        det = sxx * s1 - sx * sx
+        c = (sxy * s1 - sx * sy) / det
+        f = max(0.0, (sxx * sy - sx * sxy) / det)
+        # rates: median over shapes of the implied rate (row 0 fixed at 1)
+        for (r, _, _) in rows:
+            imp = [bm * bn * K * c / max(t / rnd - f, 1e-9) for (rr, bm, bn, rnd, K, t) in obs if rr == r]
+            rate[r] = statistics.median(imp) if imp else 1.0
+        base = rate[rows[0][0]]
+        for r in rate:
+            rate[r] /= base
+    return {"rate": {str(r): round(rate[r], 4) for r in rate}, "c": c, "f": f}
+
+
+def model_seconds(F, bm, bn, r, rounds, K):
+    return rounds * (bm * bn * K * F["c"] / F["rate"][str(r)] + F["f"])
+
+
+def model_pick(data, F, M, N, K, E=0):
+    best, best_t = None, None
+    for (r, bm, bn) in _model_rows(data):
+        tiles = grouped_tiles(M, E, N, bm, bn) if E else _cdiv(M, bm) * _cdiv(N, bn)
+        t = model_seconds(F, bm, bn, r, _cdiv(tiles, data["cus"]), K)
+        if best_t is None or t < best_t:
+            best, best_t = r, t
+    return best
+
+
+def packed_ratio(data):
+    """packed time / plain time per row (median over the swept shapes)."""
+    per = {}
+    for rec in data["packed"]:
+        for r, p in rec["packed_ms"].items():
+            per.setdefault(r, []).append(p / rec["plain_ms"][r])
+    return {r: round(statistics.median(v), 4) for r, v in per.items()}
+
+
+def copy_rate(data):
+    """Bytes per second of the blocking copy (mg_prepack_a), median over shapes."""
+    v = [rec["copy_bytes"] / (rec["copy_ms"] * 1e-3) for rec in data["packed"] if "copy_ms" in rec]
+    return statistics.median(v)
+
+
+def summarize(data):
+    """The fit, the best row of every swept shape, and how the model does."""
+    F = fit(data)
+    nrows = len(data["rows"])
+    best = []
+    lost = []
+    agree = 0
+    for rec in data["dense"]:
+        ms = {int(r): float(t) for r, t in rec["ms"].items() if int(r) in dict((a, 0) for a, _, _ in _model_rows(data))}
+        b = min(ms, key=lambda r: ms[r])
+        m = model_pick(data, F, rec["M"], rec["N"], rec["K"])
+        agree += m == b
+        lost.append(ms[m] / ms[b] - 1.0)
+        best.append({"M": rec["M"], "N": rec["N"], "K": rec["K"], "dtype": rec["dtype"], "best_row": b,
+                     "best_ms": ms[b], "model_row": m, "model_ms": ms[m]})
+    gbest = []
+    for rec in data["grouped"]:
+        ms = {int(r): float(t) for r, t in rec["ms"].items() if int(r) in dict((a, 0) for a, _, _ in _model_rows(data))}
+        b = min(ms, key=lambda r: ms[r])
+        m = model_pick(data, F, rec["T"], rec["N"], rec["K"], rec["E"])
+        gbest.append({"E": rec["E"], "T": rec["T"], "N": rec["N"], "K": rec["K"], "dtype": rec["dtype"],
+                      "best_row": b, "best_ms": ms[b], "model_row": m, "model_ms": ms[m]})
+    return {"fit": F, "rows": nrows, "dense_best": best, "grouped_best": gbest,
+            "model_agrees": "%d of %d dense shapes" % (agree, len(best)),
+            "model_time_lost_max": round(max(lost), 4), "model_time_lost_median": round(statistics.median(lost), 4),
+            "packed_ratio": packed_ratio(data), "copy_bytes_per_s": copy_rate(data),
+            "splitk": splitk_fit(data, F)}
+
+
+def splitk_fit(data, F):
+    """Rate at which split partials are written and read back (bytes / s):
+    the extra time of the best split over its kernel time in the model."""
+    vals = []
+    for rec in data["splitk"]:
+        for s, t in rec["ms"].items():
+            s = int(s)
+            if s == 1:
+                continue
+            extra_bytes = 2.0 * s * rec["M"] * rec["N"] * 4
+            # kernel part from the model with the row split-K picks (the model's best of rows 0-2)
+            tk = min(model_seconds(F, bm, bn, r, _cdiv(_cdiv(rec["M"], bm) * _cdiv(rec["N"], bn) * s, data["cus"]),
+                                   rec["K"] / s)
+                     for (r, bm, bn) in _model_rows(data) if r in (0, 1, 2))
+            extra = float(t) * 1e-3 - tk
+            if extra > 0:
+                vals.append(extra_bytes / extra)
+    return {"partial_bytes_per_s": statistics.median(vals) if vals else 4e12}
+
+
+def header_text(data, json_rel):
+    S = summarize(data)
+    F = S["fit"]
+    rows = _model_rows(data)
+    lines = [
+        "// Generated by `python -m tiled_matrix_multiplication_gemm_amd.sweep fit` from %s" % json_rel,
+        "// (timings of every table row on MI355X); do not edit by hand.  The time",
+        "// model of select_config(): t = rounds * (BM * BN * K * kSecPerElemK / rate + kFixedSec),",
+        "// rounds = ceil(tiles / 256); exact shapes of the sweep return their measured best row.",
+        "#pragma once",
+        "",
+        "#include <stdint.h>",
+        "",
+        "namespace mg {",
+        "namespace rates {",
+        "",
+        "struct RowRate {",
+        "    int id, bm, bn;",
+        "    double rate;  // per-CU output rate relative to row %d" % rows[0][0],
+        "};",
+        "inline constexpr RowRate kRows[] = {",
+    ]
+    for (r, bm, bn) in rows:
+        lines.append("    {%d, %d, %d, %.4f}," % (r, bm, bn, F["rate"][str(r)]))
+    lines += ["};",
+              "inline constexpr double kSecPerElemK = %.6e;  // one output element times one k, rate 1" % F["c"],
+              "inline constexpr double kFixedSec = %.6e;     // per tile: fill, drain, epilogue" % F["f"],
+              "inline constexpr double kCopyBytesPerSec = %.6e;  // the blocking copy of A" % S["copy_bytes_per_s"],
+              "inline constexpr double kPartialBytesPerSec = %.6e;  // split-K partials, written and read" %
+              S["splitk"]["partial_bytes_per_s"],
+              "// packed-A time / row-major time, per row (-1: not measured)",
+              "inline constexpr double kPackedRatio[] = {%s};" % ", ".join(
+                  "%.4f" % S["packed_ratio"].get(str(r), -1.0) for r in range(S["rows"])),
+              "",
+              "struct Swept {",
+              "    int64_t M, N, K;",
+              "    int32_t experts;  // 0: dense",
+              "    int32_t row;",
+              "};",
+              "// the measured best row of every swept shape (cached top-1)",
+              "inline constexpr Swept kSwept[] = {"]
+    for b in S["dense_best"]:
+        lines.append("    {%d, %d, %d, 0, %d}," % (b["M"], b["N"], b["K"], b["best_row"]))
+    for b in S["grouped_best"]:
+        lines.append("    {%d, %d, %d, %d, %d}," % (b["T"], b["N"], b["K"], b["E"], b["best_row"]))
+    lines += ["};", "", "}  // namespace rates", "}  // namespace mg", ""]
+    return "\n".join(lines)
 
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("workloads", nargs="*", default=["gemm_8192_bf16", "gemm_1024x1024x2048_f16",
-                                                      "grouped_moe_e32_t8192_k1024_n4096_f16"])
-    ap.add_argument("--rounds", type=int, default=5)
-    ap.add_argument("--reps", type=int, default=10)
-    ap.add_argument("--out", default=None)
+    sub = ap.add_subparsers(dest="what", required=True)
+    a = sub.add_parser("run")
+    a.add_argument("--out", default=DEFAULT_JSON)
+    a.add_argument("--rounds", type=int, default=3)
+    b = sub.add_parser("fit")
+    b.add_argument("--json", default=DEFAULT_JSON)
+    c = sub.add_parser("check")
+    c.add_argument("--json", default=DEFAULT_JSON)
     args = ap.parse_args()
-    import torch
-
-    import tiled_matrix_multiplication_gemm_amd as mg
-
-    lines = ["# table sweep: median kernel time per row over %d round-robin rounds of %d launches"
-             % (args.rounds, args.reps),
-             "# command: python -m tiled_matrix_multiplication_gemm_amd.sweep %s" % " ".join(sys.argv[1:]),
-             "# device: %s" % torch.cuda.get_device_name(0)]
-    ncfg = mg.mg_num_configs()
-    for name in args.workloads:
-        fn, flops = _setup(name)
-        times = {c: [] for c in range(ncfg)}
-        for cid in range(ncfg):  # warm every row once
-            mg.mg_set_config(cid)
-            for _ in range(3):
-                fn()
-        torch.cuda.synchronize()
-        for r in range(args.rounds):
-            order = list(range(ncfg)) if r % 2 == 0 else list(reversed(range(ncfg)))
-            for cid in order:
-                mg.mg_set_config(cid)
-                times[cid].append(_time(fn, args.reps))
-        mg.mg_set_config(-1)
-        for cid in range(ncfg):
-            med = statistics.median(times[cid])
-            d = mg.mg_config_info(cid)
-            lines.append("%-40s row %d %-22s %9.4f ms %8.1f TFLOP/s  (rounds: %s)" % (
-                name, cid, d["name"], med, flops / med / 1e9, " ".join("%.4f" % t for t in times[cid])))
-        print("\n".join(lines[-ncfg:]), flush=True)
-    if args.out:
-        with open(args.out, "w") as f:
-            f.write("\n".join(lines) + "\n")
+    if args.what == "run":
+        run(args.out, args.rounds)
+        return
+    with open(args.json) as f:
+        data = json.load(f)
+    rel = os.path.relpath(args.json, ROOT)
+    text = header_text(data, rel)
+    if args.what == "fit":
+        with open(HEADER, "w") as f:
+            f.write(text)
+        S = summarize(data)
+        print(json.dumps({k: v for k, v in S.items() if k not in ("dense_best", "grouped_best")}, indent=1))
+    else:
+        with open(HEADER) as f:
+            ok = f.read() == text
+        print("mg_rates.h matches the sweep" if ok else "mg_rates.h differs from the sweep")
+        sys.exit(0 if ok else 1)
 
 
 if __name__ == "__main__":
-    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    sys.path.insert(0, ROOT)
     main()
