@@ -25,6 +25,7 @@ Beside the main figure the line carries:
 
 Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 50] [--no-cpu-baseline] [--no-also] [--no-telemetry]
                       [--no-cold]
+       python bench.py --table BENCH.json   (the per-workload report table of a bench line, markdown)
 """
 from __future__ import annotations
 
@@ -162,75 +163,6 @@ def time_cold(fn, reps: int):
     per = sorted(a.elapsed_time(b) for a, b in zip(starts, ends))
     del flush
     return per[len(per) // 2], per[min(len(per) - 1, (9 * len(per)) // 10)]
-
-
-def soak_telemetry(fn, seconds: float = 1.6):
-    """Graphics clock and socket power while `fn` runs back to back.
-
-    Sampled through amdsmi on a background thread during a soak that follows
-    the timed region (never inside it).  The driver's metrics table trails
-    the hardware by up to about a second, so only samples from the second
-    half of the soak are kept.  Returns None where amdsmi is unavailable."""
-    import statistics
-    import threading
-
-    import torch
-
-    try:
-        import amdsmi
-
-        amdsmi.amdsmi_init()
-    except Exception:
-        return None
-    try:
-        handles = amdsmi.amdsmi_get_processor_handles()
-        if len(handles) != 1:
-            return None
-        h = handles[0]
-        limit_w = None
-        try:
-            limit_w = float(amdsmi.amdsmi_get_power_info(h)["power_limit"]) / 1e6  # reported in microwatts
-        except Exception:
-            pass
-        samples = []
-        stop = threading.Event()
-
-        def sample():
-            while not stop.is_set():
-                try:
-                    m = amdsmi.amdsmi_get_gpu_metrics_info(h)
-                    clks = [v for v in (m.get("current_gfxclks") or [m.get("current_gfxclk")])
-                            if isinstance(v, (int, float)) and 0 < v < 65535]
-                    pw = m.get("current_socket_power")
-                    samples.append((time.perf_counter(), sum(clks) / len(clks) if clks else None,
-                                    float(pw) if isinstance(pw, (int, float)) and pw < 65535 else None))
-                except Exception:
-                    pass
-                time.sleep(0.02)
-
-        th = threading.Thread(target=sample, daemon=True)
-        th.start()
-        t0 = time.perf_counter()
-        while time.perf_counter() - t0 < seconds:
-            for _ in range(16):
-                fn()
-            torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        stop.set()
-        th.join()
-        keep = [x for x in samples if x[0] >= t0 + (t1 - t0) / 2]
-        clk = [x[1] for x in keep if x[1] is not None]
-        pw = [x[2] for x in keep if x[2] is not None]
-        return {"gfx_clock_mhz": round(statistics.median(clk), 1) if clk else None,
-                "socket_power_w": round(statistics.median(pw), 1) if pw else None,
-                "power_limit_w": limit_w, "samples": len(keep), "soak_s": round(t1 - t0, 2)}
-    except Exception:
-        return None
-    finally:
-        try:
-            amdsmi.amdsmi_shut_down()
-        except Exception:
-            pass
 
 
 def dense_setup(name, variant="float"):
@@ -484,7 +416,60 @@ def oracle_timing():
     return out
 
 
+PARITY = {  # what the GPU tests check on each workload (tests/test_gpu_parity.py)
+    "C1": "bit-exact / tolerance + Higham bound, full output",
+    "C2": "bit-exact (also a ties stress) / tolerance + Higham, full output",
+    "C3": "bit-exact / tolerance + Higham, full output",
+    "C4": "bit-exact / tolerance + Higham, the 4096 sample + edges and the full output",
+    "C5": "bit-exact / tolerance + Higham, the 4096 sample + edges and the full output",
+}
+
+
+def table(path):
+    """The per-workload report table (markdown) from a bench JSON line."""
+    with open(path) as f:
+        line = json.loads(f.read().strip().splitlines()[-1])
+    a, ow = line["also"], line["cpu_baseline"]["per_workload"]
+    r = line["roofline"]
+    rows = [
+        ("C1", "256³ fp16", "latency", a["gemm_256_f16"], 3.36e7, 393216.0, "gemm_256_f16"),
+        ("C2", "1024×1024×2048 fp16", "MFMA", a["gemm_1024x1024x2048_f16"], 4.295e9, 10485760.0,
+         "gemm_1024x1024x2048_f16"),
+        ("C3", "C2 + bias + ReLU", "MFMA", a["gemm_bias_relu_1024x1024x2048_f16"], 4.295e9, 10487808.0,
+         "gemm_bias_relu_1024x1024x2048_f16"),
+        ("C4", "8192³ bf16", "MFMA (target ≥ 70 %)", {"kernel_ms_mean": r["kernel_ms_mean"], "warm_ms": r["warm_ms"]},
+         1.0995e12, 402653184.0, "gemm_8192_bf16"),
+        ("C5", "grouped MoE, 32 experts, 8192 tokens, 1024→4096 fp16", "HBM (weights)",
+         a["grouped_moe_e32_t8192_k1024_n4096_f16"], 6.872e10, 352321536.0 + 132.0,
+         "grouped_moe_e32_t8192_k1024_n4096_f16"),
+    ]
+    out = ["| cfg | shape / dtype | bound | TFLOP/s (mean ms; warm min / p90) | % of 2516.6 | % of roofline bound | "
+           "HBM GB/s | parity (int / float) | oracle (this host) |", "|---|---|---|---|---|---|---|---|---|"]
+    for cfg, shape, bound, rec, fl, byts, key in rows:
+        ms = rec["kernel_ms_mean"]
+        tf = fl / (ms * 1e-3) / 1e12
+        roof = min(PEAK_MFMA_TFLOPS, fl / byts * PEAK_HBM_GBS / 1e3)
+        o = ow[key]
+        many = [k for k in o if k.startswith("threads_") and k != "threads_1"]
+        if "extrapolated_full_s" in o.get("threads_1", {}):
+            th = many[0] if many else "threads_1"
+            n = th.split("_")[1]
+            orc = "%s core%s: %.3g GFLOP/s on the 4096 sample (extrapolated %.0f s)" % (
+                n, "" if n == "1" else "s", o[th]["gflops"], o[th]["extrapolated_full_s"])
+        else:
+            orc = "%s cores %.3f s, 1 core %.3f s, full output" % (many[0].split("_")[1], o[many[0]]["s"],
+                                                                  o["threads_1"]["s"])
+        w = rec.get("warm_ms", {})
+        out.append("| %s | %s | %s | %.1f (%.4f; %.4f / %.4f) | %.1f %% | %.1f %% | %.0f | %s | %s |" % (
+            cfg, shape, bound, tf, ms, w.get("min", ms), w.get("p90", ms), 100 * tf / PEAK_MFMA_TFLOPS,
+            100 * tf / roof, byts / (ms * 1e-3) / 1e9, PARITY[cfg], orc))
+    return "\n".join(out)
+
+
 def main():
+    if len(sys.argv) == 3 and sys.argv[1] == "--table":
+        print(table(sys.argv[2]))
+        return
     args = parse()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
@@ -531,6 +516,8 @@ def main():
     # The chip lowers its clock to stay within its power limit; the same
     # kernel's rate at the clock it actually ran at is the fraction of the
     # matrix cores' peak scaled to that clock (256 CU x 4096 flop/clk).
+    from tiled_matrix_multiplication_gemm_amd.profiling import soak_telemetry
+
     tel = None if args.no_telemetry else soak_telemetry(main_res["fn"])
     if not args.no_also and not args.no_cold:
         cmed, cp90 = time_cold(main_res["fn"], 20)

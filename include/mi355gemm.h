@@ -348,6 +348,12 @@ mg_status mg_config_info(int id, mg_config_desc* out);
 /* Force configuration `id` for every following call in this process (-1
  * restores the table's choice).  For benchmarking and tuning sweeps. */
 mg_status mg_set_config(int id);
+/* Override the tile raster of every following dense call in this process:
+ * group_m tile rows visited together (the GROUP_M of the Gluon matmul
+ * example; -1 restores the table's, 1..256 otherwise) and the XCD
+ * renumbering of workgroups (1 on, 0 off, -1 the table's).  For the sweep's
+ * measurements; anything else is MG_ERR_INVALID_ARG. */
+mg_status mg_set_raster(int group_m, int xcd_remap);
 /* Configuration id used by the most recent successful call in this process. */
 int mg_last_config(void);
 /* Kernel family of the most recent successful 16-bit GEMM launch in this

@@ -44,7 +44,7 @@ EXPORTED = (
     "mg_prepack_a", "mg_config_bk", "mg_gemm_prepacked", "mg_num_configs", "mg_config_info",
     "mg_set_config", "mg_last_config", "mg_select_config", "mg_conv2d_output_hw", "mg_im2col",
     "mg_conv2d_workspace_bytes", "mg_conv2d", "mg_attention_scores", "mg_splitk_noalloc_max_bytes",
-    "mg_gemm_splitk_noalloc", "mg_last_kernel", "mg_prepack_uses_to_pay",
+    "mg_gemm_splitk_noalloc", "mg_last_kernel", "mg_prepack_uses_to_pay", "mg_set_raster",
 )
 
 
@@ -105,6 +105,8 @@ def lib() -> ctypes.CDLL:
         L.mg_set_config.argtypes = [cint]
         L.mg_last_config.restype = cint
         L.mg_last_config.argtypes = []
+        L.mg_set_raster.restype = cint
+        L.mg_set_raster.argtypes = [cint, cint]
         L.mg_prepack_uses_to_pay.restype = i64
         L.mg_prepack_uses_to_pay.argtypes = [i64, i64, i64, cint]
         L.mg_last_kernel.restype = cint
@@ -401,6 +403,11 @@ def mg_config_info(cid: int) -> dict:
 
 def mg_set_config(cid: int) -> None:
     _check(lib().mg_set_config(cid))
+
+
+def mg_set_raster(group_m: int = -1, xcd_remap: int = -1) -> None:
+    """Process-wide GROUP_M / XCD-renumbering override (-1: the table's)."""
+    _check(lib().mg_set_raster(group_m, xcd_remap))
 
 
 def mg_last_config() -> int:

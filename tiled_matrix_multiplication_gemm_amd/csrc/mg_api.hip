@@ -40,6 +40,8 @@ const mg_config_desc kTable[kNumConfigs] = {
 };
 
 std::atomic<int> g_forced{-1};
+std::atomic<int> g_group_m{-1};  // raster overrides (mg_set_raster); -1: the table's
+std::atomic<int> g_xcd{-1};
 std::atomic<int> g_last{-1};
 std::atomic<int> g_last_kernel{-1};
 
@@ -153,8 +155,9 @@ mg_status launch(int cfg, int dt, bool epi, int mode, KArgs& a, hipStream_t s, i
     }
     if (grid <= 0) return MG_OK;
     if (grid > 0x7fffffff) return MG_ERR_INVALID_ARG;
-    a.group_m = d.group_m;
-    a.xcd_remap = d.xcd_remap;
+    const int gm = g_group_m.load(), xr = g_xcd.load();
+    a.group_m = gm > 0 ? gm : d.group_m;
+    a.xcd_remap = xr >= 0 ? xr : d.xcd_remap;
     mg_status st;
     switch (cfg) {
         case 0: st = launch_row0(dt, epi, mode, ta, tb, a, grid, s); break;
@@ -702,6 +705,13 @@ mg_status mg_set_config(int id) {
 }
 
 int mg_last_config(void) { return g_last.load(); }
+
+mg_status mg_set_raster(int group_m, int xcd_remap) {
+    if (group_m == 0 || group_m < -1 || group_m > 256 || xcd_remap < -1 || xcd_remap > 1) return MG_ERR_INVALID_ARG;
+    g_group_m.store(group_m);
+    g_xcd.store(xcd_remap);
+    return MG_OK;
+}
 
 int mg_last_kernel(void) { return g_last_kernel.load(); }
 

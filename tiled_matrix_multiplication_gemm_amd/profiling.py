@@ -19,6 +19,7 @@ import csv
 import glob
 import hashlib
 import os
+import time
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 COPY_BYTES = 256 * 1024 * 1024  # bytes read and bytes written by the probe's copy kernel
@@ -165,6 +166,80 @@ def write_trace(stats_csv, out, cmd, last=0):
             tt = "%.1f (last %d)" % (t[1], t[0]) if t else "-"
             f.write("%-100s %6s %14.1f %12s %18s\n" % (r["Name"][:100], r["Calls"], float(r["AverageNs"]),
                                                         r["Percentage"], tt))
+
+
+def soak_telemetry(fn, seconds: float = 1.6, with_rate: bool = False):
+    """Graphics clock and socket power while `fn` runs back to back.
+
+    Sampled through amdsmi on a background thread during a soak that follows
+    the timed region (never inside it).  The driver's metrics table trails
+    the hardware by up to about a second, so only samples from the second
+    half of the soak are kept.  Returns None where amdsmi is unavailable."""
+    import statistics
+    import threading
+
+    import torch
+
+    try:
+        import amdsmi
+
+        amdsmi.amdsmi_init()
+    except Exception:
+        return None
+    try:
+        handles = amdsmi.amdsmi_get_processor_handles()
+        if len(handles) != 1:
+            return None
+        h = handles[0]
+        limit_w = None
+        try:
+            limit_w = float(amdsmi.amdsmi_get_power_info(h)["power_limit"]) / 1e6  # reported in microwatts
+        except Exception:
+            pass
+        samples = []
+        stop = threading.Event()
+
+        def sample():
+            while not stop.is_set():
+                try:
+                    m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+                    clks = [v for v in (m.get("current_gfxclks") or [m.get("current_gfxclk")])
+                            if isinstance(v, (int, float)) and 0 < v < 65535]
+                    pw = m.get("current_socket_power")
+                    samples.append((time.perf_counter(), sum(clks) / len(clks) if clks else None,
+                                    float(pw) if isinstance(pw, (int, float)) and pw < 65535 else None))
+                except Exception:
+                    pass
+                time.sleep(0.02)
+
+        th = threading.Thread(target=sample, daemon=True)
+        th.start()
+        t0 = time.perf_counter()
+        calls = 0
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(16):
+                fn()
+            calls += 16
+            torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        stop.set()
+        th.join()
+        keep = [x for x in samples if x[0] >= t0 + (t1 - t0) / 2]
+        clk = [x[1] for x in keep if x[1] is not None]
+        pw = [x[2] for x in keep if x[2] is not None]
+        res = {"gfx_clock_mhz": round(statistics.median(clk), 1) if clk else None,
+               "socket_power_w": round(statistics.median(pw), 1) if pw else None,
+               "power_limit_w": limit_w, "samples": len(keep), "soak_s": round(t1 - t0, 2)}
+        if with_rate:
+            res["ms_per_call"] = (t1 - t0) * 1e3 / calls
+        return res
+    except Exception:
+        return None
+    finally:
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:
+            pass
 
 
 def main():

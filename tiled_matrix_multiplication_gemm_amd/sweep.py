@@ -3,6 +3,7 @@
   python -m tiled_matrix_multiplication_gemm_amd.sweep run [--out profiles/table_sweep.json] [--rounds 3]
   python -m tiled_matrix_multiplication_gemm_amd.sweep fit [--json profiles/table_sweep.json]
   python -m tiled_matrix_multiplication_gemm_amd.sweep check
+  python -m tiled_matrix_multiplication_gemm_amd.sweep energy [--out FILE] [--seconds 2]
 
 The pages tune a GEMM by benchmarking candidate configurations on the target
 and keeping the best one ("Using Triton to optimise GEMM across chips",
@@ -28,6 +29,11 @@ for that exact shape (the cache of the pages' top-1) before it consults the
 model.  The fit and the generated header are both functions of the JSON
 alone; `check` regenerates the header and compares it with the committed
 one.
+
+`energy` (GPU) soaks the 8192^3 bf16 GEMM per variant (tile row, GROUP_M,
+XCD renumbering, input data) and records throughput, graphics clock and
+socket power: the chip runs this GEMM at its power limit, where throughput
+is power divided by energy per flop.
 """
 from __future__ import annotations
 
@@ -209,6 +215,80 @@ def run(out_path, rounds):
     with open(out_path, "w") as f:
         json.dump(res, f, indent=1, sort_keys=True)
     print("wrote", out_path)
+
+
+# (label, row, GROUP_M, XCD renumbering, inputs) of the 8192^3 bf16 GEMM
+ENERGY_VARIANTS = [
+    ("table: 256x256, 8 waves, GROUP_M 8, XCD on", 0, 8, 1, "float"),
+    ("GROUP_M 4", 0, 4, 1, "float"),
+    ("GROUP_M 16", 0, 16, 1, "float"),
+    ("GROUP_M 32", 0, 32, 1, "float"),
+    ("GROUP_M 1 (row-major tile order)", 0, 1, 1, "float"),
+    ("XCD renumbering off", 0, 8, 0, "float"),
+    ("256x256, 4 waves of 128x128 (row 6)", 6, 8, 1, "float"),
+    ("128x256 (row 3)", 3, 8, 1, "float"),
+    ("256x128 (row 4)", 4, 8, 1, "float"),
+    ("inputs: integers in [-4, 4]", 0, 8, 1, "int"),
+    ("inputs: all zeros", 0, 8, 1, "zeros"),
+]
+
+
+def energy(out_path, seconds, cmdline):
+    """Throughput, graphics clock and socket power of the 8192^3 bf16 GEMM per
+    variant (tile row, raster, input data), each soaked back to back for
+    `seconds` with amdsmi sampled beside it; variants in forward then reverse
+    order, the two soaks' medians averaged.  At the power limit the energy
+    per flop is power / throughput."""
+    import numpy as np
+    import torch
+
+    import tiled_matrix_multiplication_gemm_amd as mg
+    from tiled_matrix_multiplication_gemm_amd import inputs, profiling
+
+    c = inputs.dense_workload("gemm_8192_bf16", "float")
+    ci = inputs.dense_workload("gemm_8192_bf16", "int")
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+    data = {"float": (up(c.A), up(c.B)), "int": (up(ci.A), up(ci.B))}
+    data["zeros"] = (torch.zeros_like(data["float"][0]), torch.zeros_like(data["float"][1]))
+    C = torch.empty((8192, 8192), dtype=torch.bfloat16, device="cuda")
+    flops = 2.0 * 8192 ** 3
+    res = {v[0]: [] for v in ENERGY_VARIANTS}
+    for order in (ENERGY_VARIANTS, ENERGY_VARIANTS[::-1]):
+        for (label, row, gm, xcd, kind) in order:
+            A, B = data[kind]
+            mg.mg_set_config(row)
+            mg.mg_set_raster(gm, xcd)
+            try:
+                for _ in range(20):
+                    mg.mg_gemm(A, B, out=C)
+                t = profiling.soak_telemetry(lambda: mg.mg_gemm(A, B, out=C), seconds, with_rate=True)
+            finally:
+                mg.mg_set_config(-1)
+                mg.mg_set_raster(-1, -1)
+            if t is None:
+                raise RuntimeError("amdsmi telemetry is not available")
+            res[label].append(t)
+            print("%-45s %.4f ms %s MHz %s W" % (label, t["ms_per_call"], t["gfx_clock_mhz"], t["socket_power_w"]),
+                  flush=True)
+    lines = ["# 8192^3 bf16 GEMM per variant: back-to-back calls soaked for %.1f s each, variants in forward then"
+             " reverse order (mean of the two soaks); clock and socket power: amdsmi medians over the second half"
+             " of each soak; energy per flop = power / throughput" % seconds,
+             "# command: %s" % cmdline,
+             "# device: %s" % torch.cuda.get_device_name(0),
+             "%-45s %9s %9s %9s %8s %9s" % ("variant", "ms", "TFLOP/s", "MHz", "W", "pJ/flop")]
+    for (label, *_rest) in ENERGY_VARIANTS:
+        v = res[label]
+        ms = sum(x["ms_per_call"] for x in v) / len(v)
+        mhz = sum(x["gfx_clock_mhz"] or 0 for x in v) / len(v)
+        w = sum(x["socket_power_w"] or 0 for x in v) / len(v)
+        tf = flops / (ms * 1e-3) / 1e12
+        lines.append("%-45s %9.4f %9.1f %9.0f %8.0f %9.3f" % (label, ms, tf, mhz, w, w / (tf * 1e12) * 1e12))
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 # ---- the fit (CPU) -------------------------------------------------------------
@@ -409,9 +489,15 @@ def main():
     b.add_argument("--json", default=DEFAULT_JSON)
     c = sub.add_parser("check")
     c.add_argument("--json", default=DEFAULT_JSON)
+    e = sub.add_parser("energy")
+    e.add_argument("--out", default=os.path.join(ROOT, "profiles", "gemm_8192_bf16_energy.txt"))
+    e.add_argument("--seconds", type=float, default=2.0)
     args = ap.parse_args()
     if args.what == "run":
         run(args.out, args.rounds)
+        return
+    if args.what == "energy":
+        energy(args.out, args.seconds, "python -m tiled_matrix_multiplication_gemm_amd.sweep " + " ".join(sys.argv[1:]))
         return
     with open(args.json) as f:
         data = json.load(f)
