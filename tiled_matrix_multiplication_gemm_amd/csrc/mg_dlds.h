@@ -62,10 +62,14 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const char* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p);
 }
 
-template <int BM_, int BN_, int WM_, int WN_, int BK_ = 64, int R_ = 3>
+template <int BM_, int BN_, int WM_, int WN_, int BK_ = 64, int R_ = 3, int PF_ = 1>
 struct DldsCfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
     static constexpr int R = R_;                        // LDS slots in the ring (= slices in flight + 2)
+    // LDS fragment reads run PF k16 steps ahead of the MFMAs (PF + 1 register
+    // sets): a wave with few MFMAs per step needs more than one step of
+    // them to cover the LDS latency
+    static constexpr int PF = PF_;
     static constexpr int NW = WM * WN;                  // waves per workgroup
     static constexpr int NT = NW * 64;
     static constexpr int WTM = BM / WM, WTN = BN / WN;  // output of one wave
@@ -89,6 +93,7 @@ struct DldsCfg {
                                    (WTN / 8 == 4 || WTN / 8 == 8 || WTN / 8 == 16);
     static_assert(BK == 32 || BK == 64, "K slice must be 32 or 64");
     static_assert(R >= 3 && R <= 8, "ring of 3..8 slots");
+    static_assert(PF >= 1 && PF < STEPS && STEPS % (PF + 1) == 0, "prefetch within a slice, register sets divide it");
     static_assert(JA * NW * 1024 == A_BYTES && JB * NW * 1024 == B_BYTES, "slice must split evenly over waves");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32x32");
     static_assert(LDS_BYTES <= 160 * 1024, "gfx950 has 160 KB of LDS per CU");
@@ -520,15 +525,15 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
     };
 
     // ---- main loop over k-slices -------------------------------------------
-    // Ring of R LDS slots; slice t lives in slot t % R.  Within slice t the
-    // fragments of step s+1 are read while the MFMAs of step s issue.  In the
-    // last step the wave waits for its own loads of slice t+1, the workgroup
-    // synchronises (slice t+1 complete everywhere), slice t+R-1 is issued into
-    // the slot of slice t-1, and the first fragments of slice t+1 are read
-    // under the last step's MFMAs.  Every read of slice t-1 was consumed by an
-    // MFMA of slice t-1, before the barrier, so no wave needs to drain its
-    // LDS reads at the barrier.  Up to R-2 slices are in flight while one is
-    // consumed.
+    // Ring of R LDS slots; slice t lives in slot t % R.  The fragments of
+    // k16 step g are read PF steps before its MFMAs, into register set
+    // g % (PF + 1).  Reading the first step of slice t+1 (at step STEPS - PF
+    // of slice t) needs slice t+1 in LDS everywhere: there the wave waits for
+    // its own loads of slice t+1, the workgroup synchronises, and slice
+    // t+R-1 is issued into the slot of slice t-1.  Every read of slice t-1
+    // fed an MFMA of slice t-1 before this barrier, so no wave needs to drain
+    // its LDS reads at the barrier.  Up to R-2 slices are in flight while one
+    // is consumed.
     //
     // Trips of R slices (slice trip + u in slot u, u a compile-time index).
     // While every slice of a trip still has a slice t + R - 1 to issue, the
@@ -536,27 +541,33 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
     // scheduler interleave reads and MFMAs across the slice boundary; the
     // last trips take the general form with run-time conditions.
     constexpr int L = JA + JB;  // loads per wave per slice
-    Frags F0, F1;
+    constexpr int PF = Cfg::PF, NF = PF + 1;
+    Frags F[NF];
     auto slice = [&](const int t, const int u, const bool steady, auto lv) {
 #pragma unroll
         for (int s = 0; s < STEPS; ++s) {
-            Frags& cur = (s & 1) ? F1 : F0;
-            Frags& nxt = (s & 1) ? F0 : F1;
-            if (s + 1 < STEPS) {
-                read_frags(nxt, u, s + 1, lv);
+            Frags& cur = F[s % NF];
+            Frags& nxt = F[(s + PF) % NF];
+            if (s + PF < STEPS) {
+                read_frags(nxt, u, s + PF, lv);
             } else if (steady) {
-                wait_vmcnt<L * (R - 3)>();
-                ring_barrier();
-                issue(t + R - 1, (u + R - 1) % R, false);
-                read_frags(nxt, (u + 1) % R, 0, lv);
+                if (s + PF == STEPS) {
+                    wait_vmcnt<L * (R - 3)>();
+                    ring_barrier();
+                    issue(t + R - 1, (u + R - 1) % R, false);
+                }
+                read_frags(nxt, (u + 1) % R, s + PF - STEPS, lv);
             } else {
-                // slices issued so far: 0 .. min(t+R-2, nk-1); in steady state
-                // the R-3 slices after t+1 stay in flight, near the end wait for all
-                if (t + R - 2 <= nk - 1) wait_vmcnt<L * (R - 3)>();
-                else wait_vmcnt<0>();
-                ring_barrier();
-                if (t + R - 1 < nk) issue(t + R - 1, (u + R - 1) % R, ragged && t + R - 1 == nk - 1);
-                if (t + 1 < nk) read_frags(nxt, (u + 1) % R, 0, lv);
+                if (s + PF == STEPS) {
+                    // slices issued so far: 0 .. min(t+R-2, nk-1); in steady
+                    // state the R-3 slices after t+1 stay in flight, near the
+                    // end wait for all
+                    if (t + R - 2 <= nk - 1) wait_vmcnt<L * (R - 3)>();
+                    else wait_vmcnt<0>();
+                    ring_barrier();
+                    if (t + R - 1 < nk) issue(t + R - 1, (u + R - 1) % R, ragged && t + R - 1 == nk - 1);
+                }
+                if (t + 1 < nk) read_frags(nxt, (u + 1) % R, s + PF - STEPS, lv);
             }
             // K-tail instance: outside the steady trips every step masks its
             // K-major fragments with selects (no branch, so the step stays one
@@ -566,7 +577,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
                 if (!steady) mask_frags(cur, t, s);
             }
             mfma_step(cur, lv);
-            if (steady && s + 1 == STEPS) interleave(std::integral_constant<int, JA + JB>{});
+            if (steady && s + PF == STEPS) interleave(std::integral_constant<int, JA + JB>{});
             else interleave(std::integral_constant<int, 0>{});
         }
     };
@@ -577,7 +588,8 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
         if (pre == R - 1) wait_vmcnt<L * (R - 2)>();  // slice 0 landed, R-2 slices still in flight
         else wait_vmcnt<0>();
         ring_barrier();
-        read_frags(F0, 0, 0, lv);
+#pragma unroll
+        for (int p = 0; p < PF; ++p) read_frags(F[p], 0, p, lv);
         int trip = 0;
         // steady trips: slices trip .. trip+R-1 all satisfy t + R - 1 < nk;
         // a last slice that reaches past K is issued and consumed outside them
