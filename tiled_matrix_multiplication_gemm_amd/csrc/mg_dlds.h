@@ -733,7 +733,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
             if (stage_half(row)) w = u32x4{w[2], w[3], w[0], w[1]};
             const int64_t grow = m0 + wm * Cfg::WTM + row;
             if (interior || (grow < M && col + 8 <= N)) {
-                *(u32x4*)(Cg + grow * args.ldc + col) = w;
+                store_out((u32x4*)(Cg + grow * args.ldc + col), w);
             } else if (grow < M && col < N) {
                 // the chunk that straddles N (N % 8 != 0): its valid elements
 #pragma unroll
@@ -755,7 +755,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
                 for (int q = 0; q < 4; ++q) {
                     const u32x2 w = pack4(acc[i][j], j, q, col0 + 8 * q);
                     if (row_ok && (interior || col0 + 8 * q + 4 <= N)) {
-                        *(u32x2*)(cp + 8 * q) = w;
+                        store_out((u32x2*)(cp + 8 * q), w);
                     } else if (row_ok) {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
@@ -787,7 +787,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* ws, uin
         o[1] = (uint32_t)from_float<DT>(lo[2]) | ((uint32_t)from_float<DT>(lo[3]) << 16);
         o[2] = (uint32_t)from_float<DT>(hi[0]) | ((uint32_t)from_float<DT>(hi[1]) << 16);
         o[3] = (uint32_t)from_float<DT>(hi[2]) | ((uint32_t)from_float<DT>(hi[3]) << 16);
-        *(u32x4*)(C + row * ldc + col) = o;
+        store_out((u32x4*)(C + row * ldc + col), o);
     }
 }
 

@@ -214,7 +214,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_f32_kernel(const KArgs args) {
                         v[t] = (v[t] > 0.0f) ? v[t] : 0.0f;
                     }
                 }
-                if (row < M && col < N) *(f32x4*)(Cg + row * args.ldc + col) = v;
+                if (row < M && col < N) store_out((f32x4*)(Cg + row * args.ldc + col), v);
             }
         }
     }

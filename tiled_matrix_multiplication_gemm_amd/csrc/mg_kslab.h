@@ -256,7 +256,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_kslab_kernel(const KArgs args) {
                 }
                 const uint32_t lo = (uint32_t)from_float<DT>(x[0]) | ((uint32_t)from_float<DT>(x[1]) << 16);
                 const uint32_t hi = (uint32_t)from_float<DT>(x[2]) | ((uint32_t)from_float<DT>(x[3]) << 16);
-                if (row < M && col < N) *(uint2*)(Cg + row * args.ldc + col) = make_uint2(lo, hi);
+                if (row < M && col < N) store_out((u32x2*)(Cg + row * args.ldc + col), u32x2{lo, hi});
             }
         }
 }

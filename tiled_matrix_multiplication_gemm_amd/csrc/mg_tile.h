@@ -204,6 +204,16 @@ __device__ __forceinline__ uint16_t from_float(float v) {
     else return __builtin_bit_cast(uint16_t, (__bf16)v);
 }
 
+// Stores of output tiles: written once and not read again by the kernel,
+// they go out as nontemporal (streaming) stores, which spares the caches'
+// lines for the operands (attention scores, 1 GiB of output: 0.378 ->
+// 0.288 ms; 8192^3 0.788 -> 0.780 ms; grouped MoE 0.1075 -> 0.1057 ms, same
+// process).
+template <class T>
+__device__ __forceinline__ void store_out(T* p, const T& v) {
+    __builtin_nontemporal_store(v, p);
+}
+
 // Workgroups are handed to the 8 XCDs round-robin; renumber them so that
 // each XCD receives one contiguous range of logical tile ids.
 __device__ __forceinline__ int xcd_logical(int b, int total) {
