@@ -619,10 +619,13 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
     // j*32 + 4 (l / 32) + 8 q: one 8-byte load each when the bias is 8-byte
     // aligned (element by element for the group that straddles N); otherwise
     // the epilogue reads the bias element by element.  Loads older than the
-    // ring's only make its waits stricter.
+    // ring's only make its waits stricter.  A wave whose accumulators take
+    // 256 registers has none to spare for the bias (they would spill), so
+    // it reads the bias in the epilogue.
+    constexpr bool kBiasInRegs = FM * FN * 16 < 256;
     [[maybe_unused]] u32x2 bias_v[FN][4];
     [[maybe_unused]] bool bias_pre = false;
-    if constexpr (EPI) {
+    if constexpr (EPI && kBiasInRegs) {
         bias_pre = ((uintptr_t)args.bias & 7) == 0;
 #pragma unroll
         for (int j = 0; j < FN; ++j)
@@ -661,9 +664,9 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
         for (int t = 0; t < 4; ++t) {
             v[t] = c[4 * q + t];
             if constexpr (EPI) {
-                const uint16_t pre = (uint16_t)(bias_v[j][q][t >> 1] >> (16 * (t & 1)));
-                const float bt = bias_pre ? to_float<DT>(pre)
-                                          : ((col + t < N) ? to_float<DT>(args.bias[col + t]) : 0.0f);
+                float bt;
+                if (kBiasInRegs && bias_pre) bt = to_float<DT>((uint16_t)(bias_v[j][q][t >> 1] >> (16 * (t & 1))));
+                else bt = (col + t < N) ? to_float<DT>(args.bias[col + t]) : 0.0f;
                 v[t] = v[t] + bt;
                 v[t] = (v[t] > 0.0f) ? v[t] : 0.0f;
             }

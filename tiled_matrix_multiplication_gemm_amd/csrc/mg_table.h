@@ -19,8 +19,10 @@ namespace mg {
 // shape class in select_config(), which an offline sweep tunes; there is no
 // run-time search.
 // Each row has a general kernel (register-staged loads, any K and N) and,
-// where BK = 64, a direct-to-LDS fast kernel used when K % 64 == 0 and
-// N % 8 == 0.
+// all but row 5, a direct-to-LDS fast kernel that takes any K and N as well
+// (K tails in the separate tail instances).  The general kernel runs only on
+// row 5 and where a tile's operand span does not fit the fast kernel's
+// 31-bit load offsets (leading dimensions of millions of elements).
 using Cfg0 = TileCfg<256, 256, 64, 2, 4>;  // large square problems, eight waves (two per SIMD)
 using Cfg1 = TileCfg<128, 128, 64, 2, 2>;  // mid-size, grouped
 using Cfg2 = TileCfg<64, 64, 64, 2, 2>;    // small problems: enough tiles to fill 256 CUs
