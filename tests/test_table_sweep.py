@@ -126,3 +126,71 @@ def test_layout_planner_gate(data, L):
     # the two workloads' rows measured the blocked A slower: never prepack
     assert L.mg_prepack_uses_to_pay(1024, 1024, 2048, 0) == -1
     assert L.mg_prepack_uses_to_pay(8192, 8192, 8192, 1) == -1
+
+
+def test_counters_cover_every_table_choice(data):
+    """The sweep JSON carries the hardware counters of the row the table
+    picks for each swept shape (`sweep counters`): one entry per shape, its
+    row the measured best, the direct-to-LDS or K-split kernel, and the
+    derived ratios within their ranges."""
+    S = sweep.summarize(data)
+    best = {(b["M"], b["N"], b["K"], 0): b["best_row"] for b in S["dense_best"]}
+    best.update({(b["T"], b["N"], b["K"], b["E"]): b["best_row"] for b in S["grouped_best"]})
+    shapes = data["counters"]["shapes"]
+    assert sorted((c["M"], c["N"], c["K"], c["E"]) for c in shapes) == sorted(best)
+    for c in shapes:
+        assert c["row"] == best[(c["M"], c["N"], c["K"], c["E"])], c
+        assert ("gemm_dlds_kernel" in c["kernel"]) == (c["row"] != 7), c
+        assert 0.0 < c["mfma_busy_fraction"] <= 1.0
+        assert 0.0 <= c["lds_bank_conflict_ratio"] < 1.0
+        assert 0.0 <= c["l2_hit_rate"] <= 1.0
+    assert len(data["counters"]["commands"]) == len(sweep.COUNTER_PASSES)
+
+
+def _pass_rows(kernels_and_counters, other_kernel="elementwise_kernel"):
+    """Counter-collection rows as rocprofv3 writes them: each GEMM dispatch
+    preceded by an unrelated kernel, each counter split over two instances."""
+    rows, did = [], 100
+    for name, cv in kernels_and_counters:
+        did += 1
+        rows.append({"Dispatch_Id": str(did), "Kernel_Name": other_kernel, "Counter_Name": next(iter(cv)),
+                     "Counter_Value": "7"})
+        did += 1
+        for counter, v in cv.items():
+            for half in (0.25 * v, 0.75 * v):
+                rows.append({"Dispatch_Id": str(did), "Kernel_Name": name, "Counter_Name": counter,
+                             "Counter_Value": repr(half)})
+    return rows
+
+
+def test_counter_merge_keeps_the_last_call_and_sums_instances():
+    order = [{"M": 64, "N": 64, "K": 64, "E": 0, "row": 2}, {"M": 128, "N": 128, "K": 64, "E": 0, "row": 1}]
+    assert sweep.COUNTER_CALLS == 2
+    ka, kb = "void mg::gemm_dlds_kernel<A>(mg::KArgs)", "void mg::gemm_dlds_kernel<B>(mg::KArgs)"
+    p0 = _pass_rows([(ka, {"SQ_VALU_MFMA_BUSY_CYCLES": 1.0, "SQ_BUSY_CYCLES": 1.0}),
+                     (ka, {"SQ_VALU_MFMA_BUSY_CYCLES": 1024 * 6.0, "SQ_BUSY_CYCLES": 32 * 10.0}),
+                     (kb, {"SQ_VALU_MFMA_BUSY_CYCLES": 1.0, "SQ_BUSY_CYCLES": 1.0}),
+                     (kb, {"SQ_VALU_MFMA_BUSY_CYCLES": 1024 * 3.0, "SQ_BUSY_CYCLES": 32 * 10.0})])
+    p1 = _pass_rows([(ka, {"SQ_LDS_BANK_CONFLICT": 1.0, "SQ_LDS_IDX_ACTIVE": 1.0}),
+                     (ka, {"SQ_LDS_BANK_CONFLICT": 1.0, "SQ_LDS_IDX_ACTIVE": 8.0}),
+                     (kb, {"SQ_LDS_BANK_CONFLICT": 1.0, "SQ_LDS_IDX_ACTIVE": 1.0}),
+                     (kb, {"SQ_LDS_BANK_CONFLICT": 0.0, "SQ_LDS_IDX_ACTIVE": 8.0})])
+    p2 = _pass_rows([(ka, {"TCC_HIT_sum": 1.0, "TCC_MISS_sum": 1.0}), (ka, {"TCC_HIT_sum": 3.0, "TCC_MISS_sum": 1.0}),
+                     (kb, {"TCC_HIT_sum": 1.0, "TCC_MISS_sum": 1.0}), (kb, {"TCC_HIT_sum": 1.0, "TCC_MISS_sum": 4.0})])
+    a, b = sweep.merge_counter_rows(order, [p0, p1, p2])
+    assert (a["kernel"], b["kernel"]) == (ka, kb)
+    assert a["values"]["SQ_VALU_MFMA_BUSY_CYCLES"] == 6144.0  # both instances, last call
+    assert (a["mfma_busy_fraction"], a["lds_bank_conflict_ratio"], a["l2_hit_rate"]) == (0.6, 0.125, 0.75)
+    assert (b["mfma_busy_fraction"], b["lds_bank_conflict_ratio"], b["l2_hit_rate"]) == (0.3, 0.0, 0.2)
+
+
+def test_counter_merge_refuses_mismatched_passes():
+    order = [{"M": 64, "N": 64, "K": 64, "E": 0, "row": 2}]
+    ka, kb = "void mg::gemm_dlds_kernel<A>(mg::KArgs)", "void mg::gemm_dlds_kernel<B>(mg::KArgs)"
+    one = _pass_rows([(ka, {"TCC_HIT_sum": 1.0})])
+    two = _pass_rows([(ka, {"TCC_HIT_sum": 1.0}), (ka, {"TCC_HIT_sum": 1.0})])
+    other = _pass_rows([(kb, {"TCC_HIT_sum": 1.0}), (kb, {"TCC_HIT_sum": 1.0})])
+    with pytest.raises(RuntimeError):
+        sweep.merge_counter_rows(order, [one])  # one dispatch where two calls were made
+    with pytest.raises(RuntimeError):
+        sweep.merge_counter_rows(order, [two, other])  # the passes ran different kernels

@@ -4,6 +4,7 @@
   python -m tiled_matrix_multiplication_gemm_amd.sweep fit [--json profiles/table_sweep.json]
   python -m tiled_matrix_multiplication_gemm_amd.sweep check
   python -m tiled_matrix_multiplication_gemm_amd.sweep energy [--out FILE] [--seconds 2]
+  python -m tiled_matrix_multiplication_gemm_amd.sweep counters [--json profiles/table_sweep.json]
 
 The pages tune a GEMM by benchmarking candidate configurations on the target
 and keeping the best one ("Using Triton to optimise GEMM across chips",
@@ -30,6 +31,12 @@ model.  The fit and the generated header are both functions of the JSON
 alone; `check` regenerates the header and compares it with the committed
 one.
 
+`counters` (GPU) records the hardware counters behind the table's choices:
+one rocprofv3 --pmc pass per counter group, each running the table's own row
+on every swept shape, and stores per shape the MFMA-busy fraction, the LDS
+bank-conflict ratio and the L2 hit rate in the JSON (key "counters"; the
+generated header does not depend on it).
+
 `energy` (GPU) soaks the 8192^3 bf16 GEMM per variant (tile row, GROUP_M,
 XCD renumbering, input data) and records throughput, graphics clock and
 socket power: the chip runs this GEMM at its power limit, where throughput
@@ -42,6 +49,7 @@ import json
 import math
 import os
 import statistics
+import subprocess
 import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
@@ -215,6 +223,166 @@ def run(out_path, rounds):
     with open(out_path, "w") as f:
         json.dump(res, f, indent=1, sort_keys=True)
     print("wrote", out_path)
+
+
+# ---- counters of the table's choices ----------------------------------------------
+# One rocprofv3 --pmc pass per group (each group is collected in one pass by
+# the hardware); every pass runs the same fixed sequence of GEMMs.
+COUNTER_PASSES = [
+    ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_INSTS_MFMA", "GRBM_GUI_ACTIVE"],
+    ["SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "GRBM_GUI_ACTIVE"],
+    ["TCC_HIT_sum", "TCC_MISS_sum"],
+]
+COUNTER_CALLS = 2  # calls per shape; the counters of the last one are kept
+
+
+def _device_dense(M, N, K, dt):
+    """Random operands drawn on the device, rows padded to 16 bytes (the
+    counters do not depend on the values, and drawing the largest shapes on
+    the host would dominate each pass)."""
+    import torch
+
+    tdt = torch.float16 if dt == F16 else torch.bfloat16
+
+    def mat(rows, cols, scale):
+        ld = (cols + 7) // 8 * 8
+        return (torch.randn((rows, ld), device="cuda") * scale).to(tdt)[:, :cols]
+
+    A, B = mat(M, K, K ** -0.5), mat(K, N, 1.0)
+    C = torch.empty((M, (N + 7) // 8 * 8), dtype=tdt, device="cuda")[:, :N]
+    return A, B, C
+
+
+def counters_run(json_path, order_path):
+    """(GPU, under rocprofv3 --pmc) COUNTER_CALLS calls of every swept shape
+    with the row the table picks, dense shapes then grouped ones in the
+    JSON's order; writes that order with the row and kernel family used."""
+    import numpy as np
+    import torch
+
+    import tiled_matrix_multiplication_gemm_amd as mg
+
+    with open(json_path) as f:
+        data = json.load(f)
+    torch.manual_seed(0)
+    order = []
+    for rec in data["dense"]:
+        M, N, K, dt = rec["M"], rec["N"], rec["K"], rec["dtype"]
+        A, B, C = _device_dense(M, N, K, dt)
+        for _ in range(COUNTER_CALLS):
+            mg.mg_gemm(A, B, out=C)
+        torch.cuda.synchronize()
+        order.append({"M": M, "N": N, "K": K, "dtype": dt, "E": 0, "row": mg.mg_last_config(),
+                      "family": mg.mg_last_kernel()})
+        print("counters: dense %d x %d x %d row %d" % (M, N, K, order[-1]["row"]), flush=True)
+        del A, B, C
+    for rec in data["grouped"]:
+        E, T, N, K, dt = rec["E"], rec["T"], rec["N"], rec["K"], rec["dtype"]
+        tdt = torch.float16 if dt == F16 else torch.bfloat16
+        X = torch.randn((T, K), device="cuda").to(tdt)
+        W = (torch.randn((E, K, N), device="cuda") * 0.02).to(tdt)
+        off = torch.from_numpy(np.concatenate([[0], np.cumsum(rec["counts"])]).astype(np.int32)).cuda()
+        Y = torch.empty((T, N), dtype=tdt, device="cuda")
+        for _ in range(COUNTER_CALLS):
+            mg.mg_grouped_gemm(X, W, off, out=Y)
+        torch.cuda.synchronize()
+        order.append({"M": T, "N": N, "K": K, "dtype": dt, "E": E, "row": mg.mg_last_config(),
+                      "family": mg.mg_last_kernel()})
+        print("counters: grouped E=%d T=%d N=%d K=%d row %d" % (E, T, N, K, order[-1]["row"]), flush=True)
+        del X, W, Y
+    with open(order_path, "w") as f:
+        json.dump(order, f)
+
+
+def derived_counters(v):
+    """MFMA-busy fraction, LDS bank-conflict ratio and L2 hit rate from one
+    dispatch's summed counters (those whose inputs are present)."""
+    from tiled_matrix_multiplication_gemm_amd.profiling import SHADER_ENGINES, SIMDS
+
+    out = {}
+    if v.get("SQ_BUSY_CYCLES") and "SQ_VALU_MFMA_BUSY_CYCLES" in v:
+        out["mfma_busy_fraction"] = round((v["SQ_VALU_MFMA_BUSY_CYCLES"] / SIMDS) /
+                                          (v["SQ_BUSY_CYCLES"] / SHADER_ENGINES), 4)
+    if "SQ_LDS_BANK_CONFLICT" in v and "SQ_LDS_IDX_ACTIVE" in v:
+        out["lds_bank_conflict_ratio"] = round(v["SQ_LDS_BANK_CONFLICT"] / max(v["SQ_LDS_IDX_ACTIVE"], 1.0), 4)
+    if "TCC_HIT_sum" in v and "TCC_MISS_sum" in v:
+        out["l2_hit_rate"] = round(v["TCC_HIT_sum"] / max(v["TCC_HIT_sum"] + v["TCC_MISS_sum"], 1.0), 4)
+    return out
+
+
+def merge_counter_rows(order, passes):
+    """Attach counters to the shapes of `order`.  `passes` holds, per pass,
+    the rows of its counter_collection CSV (dicts with Dispatch_Id,
+    Kernel_Name, Counter_Name, Counter_Value).  The GEMM dispatches of a pass
+    (kernel names holding "gemm_"), in dispatch order, are COUNTER_CALLS per
+    shape of `order`; the last call of each shape is kept.  Every pass must
+    see the same kernels."""
+    vals = [dict() for _ in order]
+    names = [None] * len(order)
+    for rows in passes:
+        disp = {}
+        for r in rows:
+            if "gemm_" not in r["Kernel_Name"]:
+                continue
+            name, v = disp.setdefault(int(r["Dispatch_Id"]), (r["Kernel_Name"], {}))
+            v[r["Counter_Name"]] = v.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        ids = sorted(disp)
+        if len(ids) != COUNTER_CALLS * len(order):
+            raise RuntimeError("%d GEMM dispatches for %d shapes" % (len(ids), len(order)))
+        for i in range(len(order)):
+            name, v = disp[ids[COUNTER_CALLS * (i + 1) - 1]]
+            if names[i] is not None and names[i] != name:
+                raise RuntimeError("passes ran different kernels for shape %d" % i)
+            names[i] = name
+            vals[i].update(v)
+    out = []
+    for o, v, name in zip(order, vals, names):
+        rec = dict(o)
+        rec["kernel"] = name
+        rec["values"] = {k: round(x, 1) for k, x in sorted(v.items())}
+        rec.update(derived_counters(v))
+        out.append(rec)
+    return out
+
+
+def counters(json_path, work_dir, timeout_s):
+    """Run the counter passes as child processes (rocprofv3 wraps the
+    program directly) and merge their counters into the JSON."""
+    from tiled_matrix_multiplication_gemm_amd.profiling import _counter_rows
+
+    os.makedirs(work_dir, exist_ok=True)
+    order_path = os.path.join(work_dir, "counter_order.json")
+    passes, cmds = [], []
+    for i, group in enumerate(COUNTER_PASSES):
+        d = os.path.join(work_dir, "pmc_%d" % i)
+        cmd = ["timeout", "-s", "KILL", str(timeout_s), "rocprofv3", "--pmc", *group, "--output-format", "csv",
+               "-d", d, "-o", "run", "--", sys.executable, "-m", "tiled_matrix_multiplication_gemm_amd.sweep",
+               "counters-run", "--json", json_path, "--order", order_path]
+        shown = " ".join(cmd).replace(sys.executable, "python").replace(ROOT + os.sep, "")
+        print("pass %d: %s" % (i, shown), flush=True)
+        if os.path.exists(order_path):
+            os.remove(order_path)
+        rc = subprocess.run(cmd, cwd=ROOT).returncode
+        # rocprofv3 itself may end abnormally after the program has finished
+        # and written its results; the pass counts if both are there
+        if not os.path.exists(order_path):
+            raise SystemExit("counter pass %d failed (exit %d) before the program finished" % (i, rc))
+        if rc != 0:
+            print("pass %d: profiler exit %d after the program finished; results kept" % (i, rc), flush=True)
+        passes.append(_counter_rows(d))
+        cmds.append(shown)
+    with open(order_path) as f:
+        order = json.load(f)
+    with open(json_path) as f:
+        data = json.load(f)
+    data["counters"] = {"commands": cmds, "calls_per_shape": COUNTER_CALLS,
+                        "shapes": merge_counter_rows(order, passes)}
+    with open(json_path, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+    for r in data["counters"]["shapes"]:
+        print("%6d x %5d x %5d E=%2d row %d  mfma busy %s  lds conflicts %s  l2 hit %s" % (
+            r["M"], r["N"], r["K"], r["E"], r["row"], r.get("mfma_busy_fraction"), r.get("lds_bank_conflict_ratio"),
+            r.get("l2_hit_rate")), flush=True)
 
 
 # (label, row, GROUP_M, XCD renumbering, inputs) of the 8192^3 bf16 GEMM
@@ -492,9 +660,22 @@ def main():
     e = sub.add_parser("energy")
     e.add_argument("--out", default=os.path.join(ROOT, "profiles", "gemm_8192_bf16_energy.txt"))
     e.add_argument("--seconds", type=float, default=2.0)
+    g = sub.add_parser("counters")
+    g.add_argument("--json", default=DEFAULT_JSON)
+    g.add_argument("--work", default=os.path.join(ROOT, "gpurun_out", "sweep_counters"))
+    g.add_argument("--timeout", type=int, default=300)
+    h = sub.add_parser("counters-run")
+    h.add_argument("--json", default=DEFAULT_JSON)
+    h.add_argument("--order", required=True)
     args = ap.parse_args()
     if args.what == "run":
         run(args.out, args.rounds)
+        return
+    if args.what == "counters":
+        counters(os.path.abspath(args.json), os.path.abspath(args.work), args.timeout)
+        return
+    if args.what == "counters-run":
+        counters_run(args.json, args.order)
         return
     if args.what == "energy":
         energy(args.out, args.seconds, "python -m tiled_matrix_multiplication_gemm_amd.sweep " + " ".join(sys.argv[1:]))
