@@ -10,8 +10,10 @@ launch stream, whose mean is the kernel time used for the roofline.
 Beside the main figure the line carries:
   roofline      the GEMM kernel against the dense bf16 MFMA peak (and against
                 that peak scaled to the graphics clock the chip ran at);
-  telemetry     graphics clock and socket power (amdsmi) over a short soak
-                of the same call after the timed region;
+  telemetry     graphics and memory clocks, socket power, hotspot temperature
+                (amdsmi) over a short soak of the same call after the timed
+                region;
+  device        name, architecture, compute units, memory, L2 and LDS sizes;
   cold_*        kernel time (median, p90) with the caches flushed by a
                 512 MiB write before each call (not with --no-also);
   cpu_baseline  the CPU oracle timed on this host on a bounded sample of the
@@ -141,6 +143,21 @@ def spread(per):
     """min / median / p90 of a sorted list of per-call times (ms)."""
     return {"min": round(per[0], 5), "median": round(per[len(per) // 2], 5),
             "p90": round(per[min(len(per) - 1, (9 * len(per)) // 10)], 5)}
+
+
+def device_info():
+    """What the runtime reports about the GPU the line was measured on."""
+    import torch
+
+    p = torch.cuda.get_device_properties(0)
+    info = {"name": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
+            "memory_gib": round(p.total_memory / 2 ** 30, 1)}
+    for key, attr in (("l2_bytes", "L2_cache_size"), ("lds_bytes_per_block", "shared_memory_per_block"),
+                      ("warp_size", "warp_size"), ("clock_khz", "clock_rate")):
+        v = getattr(p, attr, None)
+        if isinstance(v, int):
+            info[key] = v
+    return info
 
 
 def time_graph(fn, out, calls: int = 50, replays: int = 20):
@@ -568,6 +585,7 @@ def main():
         line["roofline"]["cold_kernel_ms_median"] = round(cmed, 4)
         line["roofline"]["cold_kernel_ms_p90"] = round(cp90, 4)
     line["telemetry"] = tel
+    line["device"] = device_info()
     if tel and tel.get("gfx_clock_mhz"):
         peak_clk = 256 * 4096 * tel["gfx_clock_mhz"] * 1e6 / 1e12
         line["roofline"]["peak_at_clock"] = round(peak_clk, 1)

@@ -169,7 +169,8 @@ def write_trace(stats_csv, out, cmd, last=0):
 
 
 def soak_telemetry(fn, seconds: float = 1.6, with_rate: bool = False):
-    """Graphics clock and socket power while `fn` runs back to back.
+    """Graphics and memory clocks, socket power and hotspot temperature while
+    `fn` runs back to back.
 
     Sampled through amdsmi on a background thread during a soak that follows
     the timed region (never inside it).  The driver's metrics table trails
@@ -206,8 +207,12 @@ def soak_telemetry(fn, seconds: float = 1.6, with_rate: bool = False):
                     clks = [v for v in (m.get("current_gfxclks") or [m.get("current_gfxclk")])
                             if isinstance(v, (int, float)) and 0 < v < 65535]
                     pw = m.get("current_socket_power")
+                    uclk = m.get("current_uclk")
+                    hot = m.get("temperature_hotspot")
                     samples.append((time.perf_counter(), sum(clks) / len(clks) if clks else None,
-                                    float(pw) if isinstance(pw, (int, float)) and pw < 65535 else None))
+                                    float(pw) if isinstance(pw, (int, float)) and pw < 65535 else None,
+                                    float(uclk) if isinstance(uclk, (int, float)) and 0 < uclk < 65535 else None,
+                                    float(hot) if isinstance(hot, (int, float)) and 0 < hot < 65535 else None))
                 except Exception:
                     pass
                 time.sleep(0.02)
@@ -227,8 +232,12 @@ def soak_telemetry(fn, seconds: float = 1.6, with_rate: bool = False):
         keep = [x for x in samples if x[0] >= t0 + (t1 - t0) / 2]
         clk = [x[1] for x in keep if x[1] is not None]
         pw = [x[2] for x in keep if x[2] is not None]
+        uclk = [x[3] for x in keep if x[3] is not None]
+        hot = [x[4] for x in keep if x[4] is not None]
         res = {"gfx_clock_mhz": round(statistics.median(clk), 1) if clk else None,
+               "mem_clock_mhz": round(statistics.median(uclk), 1) if uclk else None,
                "socket_power_w": round(statistics.median(pw), 1) if pw else None,
+               "hotspot_c": round(statistics.median(hot), 1) if hot else None,
                "power_limit_w": limit_w, "samples": len(keep), "soak_s": round(t1 - t0, 2)}
         if with_rate:
             res["ms_per_call"] = (t1 - t0) * 1e3 / calls
