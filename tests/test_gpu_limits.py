@@ -1,0 +1,147 @@
+"""Sizes at the library's limits, against the oracle.
+
+* An output of more than 2^31 elements (65537 x 32776 fp16, K = 64): 64-bit
+  output addressing in the direct-to-LDS kernel's epilogue.  Integer inputs
+  make every output exact, so besides the seeded 4096-element sample and the
+  edge set (checked against the oracle) every row sum and every column sum
+  of the output is compared with the exact sums A (B 1) and (1^T A) B,
+  computed here from the inputs in int64: a wrong, missing or doubled
+  element anywhere changes its row's and its column's sum.
+* Leading strides whose tile spans do not fit the direct-to-LDS kernel's
+  31-bit per-tile load offsets: the problem falls back to the general
+  kernel (row-major operands), or is refused with
+  MG_ERR_UNSUPPORTED_LAYOUT (a transposed operand, which only the
+  direct-to-LDS kernel reads); an output stride that puts rows more than
+  2^31 elements from the base stays on the direct-to-LDS kernel (its stores
+  are 64-bit addressed).
+"""
+import numpy as np
+import pytest
+
+import tiled_matrix_multiplication_gemm_amd as mg
+from oracle import compare
+from tiled_matrix_multiplication_gemm_amd import inputs
+from tests.gpu_util import (CANARY, F16, announce, assert_bitexact, to_dev, to_host, torch_dtype)
+
+pytestmark = pytest.mark.gpu
+
+# Leading stride (elements) beyond the direct-to-LDS kernel's reach for
+# every row: a 64-row (or 64-k-row) tile span of it is more than 2^31 bytes.
+HUGE_LD = (1 << 24) + 8
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    mg.lib()
+    yield
+    mg.mg_set_config(-1)
+    torch.cuda.empty_cache()
+
+
+def exact(bits):
+    """fp16 bit patterns of integers -> int64 values."""
+    return np.asarray(bits).view(np.float16).astype(np.int64)
+
+
+def test_output_beyond_2_31_elements(orc):
+    import torch
+
+    M, N, K = 65537, 32776, 64
+    assert M * N > 2 ** 31
+    c = inputs.integer_dense(M, N, K, F16, 9101, name="beyond_2_31")
+    announce("dense %dx%dx%d fp16 integer (output > 2^31 elements)" % (M, N, K))
+    A, B = to_dev(c.A, F16), to_dev(c.B, F16)
+    guard = 4096
+    buf = torch.full((guard + M * N + guard,), CANARY, dtype=torch.int16, device="cuda")
+    C = buf[guard: guard + M * N].view(torch_dtype(F16)).view(M, N)
+    mg.mg_gemm(A, B, out=C)
+    torch.cuda.synchronize()
+    assert mg.mg_last_kernel() == "gemm_dlds_kernel"
+    assert bool((buf[:guard] == CANARY).all()) and bool((buf[guard + M * N:] == CANARY).all()), \
+        "write outside the output"
+    del A, B
+    rows, cols = compare.sample_positions(M, N, 4096, 9102)
+    er, ec = compare.edge_positions(M, N)
+    rows, cols = np.concatenate([rows, er]), np.concatenate([cols, ec])
+    got_s = to_host(C[torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()])
+    _, ref_q = orc.gemm_sampled(c.A, c.B, F16, rows, cols)
+    assert_bitexact(got_s, ref_q, F16, "sample + edges")
+    # every row and column sum (|C| <= 16 K = 1024: every output is an exact fp16 integer)
+    Ai, Bi = exact(c.A), exact(c.B)
+    want_rows = Ai @ Bi.sum(axis=1)
+    want_cols = Ai.sum(axis=0) @ Bi
+    got_cols = np.zeros(N, dtype=np.int64)
+    step = 4096
+    for r0 in range(0, M, step):
+        blk = to_host(C[r0: r0 + step]).view(np.float16).astype(np.float64)
+        assert np.all(np.isfinite(blk)), "non-finite output in rows %d.." % r0
+        assert np.array_equal(blk.sum(axis=1).astype(np.int64), want_rows[r0: r0 + step]), "row sums, rows %d.." % r0
+        got_cols += blk.sum(axis=0).astype(np.int64)
+    assert np.array_equal(got_cols, want_cols), "column sums"
+
+
+def strided_dev(bits, ld, dt):
+    """bits [R, C] on the device as a view with row stride ld."""
+    import torch
+
+    R, Cc = bits.shape
+    store = torch.empty((R - 1) * ld + Cc, dtype=torch_dtype(dt), device="cuda")
+    v = store.as_strided((R, Cc), (ld, 1))
+    v.copy_(to_dev(bits, dt))
+    return v
+
+
+@pytest.mark.parametrize("which", ["a", "b"])
+def test_operand_stride_beyond_the_direct_kernel_falls_back(orc, which):
+    import torch
+
+    M, N, K = 100, 136, 72
+    c = inputs.integer_dense(M, N, K, F16, 9200 + (which == "b"), epilogue=True, name="huge_ld")
+    announce("dense %dx%dx%d, ld%s = %d (general kernel)" % (M, N, K, which, HUGE_LD))
+    A = strided_dev(c.A, HUGE_LD, F16) if which == "a" else to_dev(c.A, F16)
+    B = strided_dev(c.B, HUGE_LD, F16) if which == "b" else to_dev(c.B, F16)
+    out = mg.mg_gemm_bias_relu(A, B, to_dev(c.bias, F16))
+    torch.cuda.synchronize()
+    assert mg.mg_last_kernel() == "gemm_tile_kernel"
+    _, ref_q = orc.gemm(c.A, c.B, F16, bias=c.bias, relu=True)
+    assert_bitexact(to_host(out), ref_q, F16, "ld%s = %d" % (which, HUGE_LD))
+    del A, B, out
+    torch.cuda.empty_cache()
+
+
+def test_output_stride_beyond_2_31_elements_stays_direct(orc):
+    import torch
+
+    M, N, K = 200, 136, 128
+    c = inputs.integer_dense(M, N, K, F16, 9300, name="huge_ldc")
+    announce("dense %dx%dx%d, ldc = %d (rows past 2^31 elements)" % (M, N, K, HUGE_LD))
+    assert (M - 1) * HUGE_LD > 2 ** 31
+    store = torch.full(((M - 1) * HUGE_LD + N,), CANARY, dtype=torch.int16, device="cuda")
+    C = store.view(torch_dtype(F16)).as_strided((M, N), (HUGE_LD, 1))
+    mg.mg_gemm(to_dev(c.A, F16), to_dev(c.B, F16), out=C)
+    torch.cuda.synchronize()
+    assert mg.mg_last_kernel() == "gemm_dlds_kernel"
+    _, ref_q = orc.gemm(c.A, c.B, F16)
+    assert_bitexact(to_host(C), ref_q, F16, "ldc = %d" % HUGE_LD)
+    # the gap after each row is untouched (sampled: the first 64 elements of every gap)
+    gaps = store.as_strided((M - 1, 64), (HUGE_LD, 1), N)
+    assert bool((gaps == CANARY).all()), "write between rows"
+    del C, store
+    torch.cuda.empty_cache()
+
+
+def test_transposed_operand_beyond_the_direct_kernel_is_refused():
+    import torch
+
+    M, N, K = 64, 64, 64
+    announce("dense %dx%dx%d, A transposed with ld = %d (refused)" % (M, N, K, HUGE_LD))
+    At = torch.zeros((K - 1) * HUGE_LD + M, dtype=torch.float16, device="cuda").as_strided((K, M), (HUGE_LD, 1))
+    B = torch.zeros((K, N), dtype=torch.float16, device="cuda")
+    with pytest.raises(RuntimeError, match="UNSUPPORTED_LAYOUT"):
+        mg.mg_gemm(At.t(), B)
+    del At
+    torch.cuda.empty_cache()
