@@ -14,6 +14,8 @@
   direct-to-LDS kernel reads); an output stride that puts rows more than
   2^31 elements from the base stays on the direct-to-LDS kernel (its stores
   are 64-bit addressed).
+* Grouped weights of more than 2^31 elements (160 experts of 4096 x 4096):
+  the experts whose weights start past that point, against the oracle.
 """
 import numpy as np
 import pytest
@@ -145,3 +147,37 @@ def test_transposed_operand_beyond_the_direct_kernel_is_refused():
         mg.mg_gemm(At.t(), B)
     del At
     torch.cuda.empty_cache()
+
+
+def test_grouped_weights_beyond_2_31_elements(orc):
+    """160 experts of 4096 x 4096 weights (2.7e9 elements): the weights of the
+    last experts start beyond 2^31 elements from the base.  Tokens go to
+    experts 0, 1, 130 and 159 only (130 and 159 lie past the limit); every
+    output row is checked bit-exact against the dense oracle of its expert
+    (the grouped oracle is the per-expert dense one)."""
+    import torch
+
+    E, K, N = 160, 4096, 4096
+    live = {0: 40, 1: 1, 130: 257, 159: 33}
+    assert 130 * K * N > 2 ** 31
+    counts = np.zeros(E, dtype=np.int64)
+    for e, n in live.items():
+        counts[e] = n
+    off = inputs.offsets_from_counts(counts)
+    T = int(off[-1])
+    rng = np.random.default_rng(9400)
+    X = inputs.to_bits(rng.integers(-4, 5, size=(T, K)).astype(np.float64), F16)
+    Wl = {e: inputs.to_bits(rng.integers(-4, 5, size=(K, N)).astype(np.float64), F16) for e in live}
+    announce("grouped E=%d K=%d N=%d T=%d, weights beyond 2^31 elements" % (E, K, N, T))
+    W = torch.zeros((E, K, N), dtype=torch_dtype(F16), device="cuda")
+    for e, w in Wl.items():
+        W[e].copy_(to_dev(w, F16))
+    Y = mg.mg_grouped_gemm(to_dev(X, F16), W, torch.from_numpy(off.astype(np.int32)).cuda())
+    torch.cuda.synchronize()
+    got = to_host(Y)
+    del W, Y
+    torch.cuda.empty_cache()
+    for e in live:
+        r0, r1 = int(off[e]), int(off[e + 1])
+        _, ref_q = orc.gemm(X[r0:r1], Wl[e], F16)
+        assert_bitexact(got[r0:r1], ref_q, F16, "expert %d" % e)
