@@ -74,9 +74,13 @@ const char* mg_status_string(mg_status status);
  * row stride of each operand must be a multiple of 8 and at least its row
  * length; any other stride pattern is MG_ERR_UNSUPPORTED_LAYOUT.  Any M, N
  * and K are accepted in either layout (the direct-to-LDS kernels zero-fill
- * a K tail and mask the N tail); a transposed operand is refused
- * (MG_ERR_UNSUPPORTED_LAYOUT) only under a configuration forced with
- * mg_set_config() that has no direct-to-LDS kernel.
+ * a K tail and mask the N tail).  A transposed operand is refused
+ * (MG_ERR_UNSUPPORTED_LAYOUT) in two cases.  The first is a configuration,
+ * forced with mg_set_config(), that has no direct-to-LDS kernel.  The
+ * second is a row stride so large (about 2^24 elements or more) that a
+ * 64-row span of the operand passes the direct-to-LDS kernel's 31-bit
+ * load offsets.  Row-major operands with such strides run on the general
+ * kernel.
  *
  * fp32 (in_dtype == out_dtype == MG_F32; the 4096^3 fp32 row of the FlagOS
  * cross-chip page's benchmark table, section 3.4): fp32 inputs on the fp32
@@ -187,8 +191,11 @@ mg_status mg_gemm_splitk_noalloc(const void* A, const void* B, void* C, int64_t 
  *    stride stride_wk.  stride_we must be a multiple of 8.
  * Y: T x N, row stride stride_ym.
  * expert_offsets: DEVICE array of E+1 int32 with o_0 = 0, o_E = T and
- *    o_e <= o_{e+1}.  It is read by the kernel and is NOT validated (a
- *    violation is undefined behaviour).  Experts with no rows write nothing.
+ *    o_e <= o_{e+1}.  It is read by the kernel and is not validated.  As
+ *    the kernel reads the offsets, it clamps each into [0, T] and raises
+ *    it to at least the previous one.  Offsets that break the rules
+ *    therefore leave some rows of Y unspecified, but never cause an access
+ *    outside X, W and Y.  Experts with no rows write nothing.
  * dtype is both the input and the output type.
  */
 mg_status mg_grouped_gemm(const void* X, const void* W, void* Y, const int32_t* expert_offsets,

@@ -16,6 +16,9 @@
   are 64-bit addressed).
 * Grouped weights of more than 2^31 elements (160 experts of 4096 x 4096):
   the experts whose weights start past that point, against the oracle.
+* Grouped expert offsets that break the rules: nothing outside Y is
+  written, and the result is the product over the partition the kernel
+  clamps them to.
 """
 import numpy as np
 import pytest
@@ -181,3 +184,42 @@ def test_grouped_weights_beyond_2_31_elements(orc):
         r0, r1 = int(off[e]), int(off[e + 1])
         _, ref_q = orc.gemm(X[r0:r1], Wl[e], F16)
         assert_bitexact(got[r0:r1], ref_q, F16, "expert %d" % e)
+
+
+@pytest.mark.parametrize("E", [12, 70])
+def test_grouped_offsets_out_of_order_stay_inside_the_buffers(orc, E):
+    """Expert offsets that break the rules (negative, decreasing, past T):
+    the kernel clamps each offset into [0, T] and raises it to at least the
+    previous one, so it computes the grouped product for that clamped
+    partition (checked against the oracle), leaves every row outside it
+    untouched, and writes nothing outside Y.  Both ways of reading the
+    offsets are covered (held in lanes below 64 experts, read from memory
+    above)."""
+    import torch
+
+    T, N, K = 700, 136, 128
+    rng = np.random.default_rng(9500 + E)
+    raw = rng.integers(-100, T + 200, size=E + 1).astype(np.int64)
+    raw[0] = 30  # rows 0..29 belong to no expert
+    clamped = np.empty_like(raw)
+    a = min(max(int(raw[0]), 0), T)
+    clamped[0] = a
+    for e in range(E):
+        b = min(max(int(raw[e + 1]), a), T)
+        clamped[e + 1] = b
+        a = b
+    assert clamped[-1] < T or clamped[0] > 0  # some rows lie outside the partition
+    X = inputs.to_bits(rng.integers(-4, 5, size=(T, K)).astype(np.float64), F16)
+    W = inputs.to_bits(rng.integers(-4, 5, size=(E, K, N)).astype(np.float64), F16)
+    announce("grouped E=%d T=%d with offsets out of order" % (E, T))
+    from tests.gpu_util import Guarded
+
+    out = Guarded(T, N, F16)
+    mg.mg_grouped_gemm(to_dev(X, F16), to_dev(W, F16), torch.from_numpy(raw.astype(np.int32)).cuda(), out=out.mat)
+    torch.cuda.synchronize()
+    assert out.guards_intact(), "write outside Y"
+    got = out.result()
+    lo, hi = int(clamped[0]), int(clamped[-1])
+    assert np.all(got[:lo] == CANARY) and np.all(got[hi:] == CANARY), "rows outside the partition written"
+    _, ref_q = orc.grouped_gemm(X[lo:hi], W, clamped - lo, F16)
+    assert_bitexact(got[lo:hi], ref_q, F16, "clamped partition")
