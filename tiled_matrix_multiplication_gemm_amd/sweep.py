@@ -387,17 +387,17 @@ def counters(json_path, work_dir, timeout_s):
 
 # (label, row, GROUP_M, XCD renumbering, inputs) of the 8192^3 bf16 GEMM
 ENERGY_VARIANTS = [
-    ("table: 256x256, 8 waves, GROUP_M 8, XCD on", 0, 8, 1, "float"),
-    ("GROUP_M 4", 0, 4, 1, "float"),
+    ("table: 256x256, 8 waves, GROUP_M 4, XCD on", 0, 4, 1, "float"),
+    ("GROUP_M 8", 0, 8, 1, "float"),
     ("GROUP_M 16", 0, 16, 1, "float"),
     ("GROUP_M 32", 0, 32, 1, "float"),
     ("GROUP_M 1 (row-major tile order)", 0, 1, 1, "float"),
-    ("XCD renumbering off", 0, 8, 0, "float"),
-    ("256x256, 4 waves of 128x128 (row 6)", 6, 8, 1, "float"),
-    ("128x256 (row 3)", 3, 8, 1, "float"),
-    ("256x128 (row 4)", 4, 8, 1, "float"),
-    ("inputs: integers in [-4, 4]", 0, 8, 1, "int"),
-    ("inputs: all zeros", 0, 8, 1, "zeros"),
+    ("XCD renumbering off", 0, 4, 0, "float"),
+    ("256x256, 4 waves of 128x128 (row 6)", 6, 4, 1, "float"),
+    ("128x256 (row 3)", 3, 4, 1, "float"),
+    ("256x128 (row 4)", 4, 4, 1, "float"),
+    ("inputs: integers in [-4, 4]", 0, 4, 1, "int"),
+    ("inputs: all zeros", 0, 4, 1, "zeros"),
 ]
 
 
