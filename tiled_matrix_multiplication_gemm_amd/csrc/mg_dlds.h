@@ -136,8 +136,11 @@ __device__ __forceinline__ int swz_b(int krow) {
 // Both give lane l the k values 16s + 8 (l / 32) + {0..7} of line l % 32 in
 // the same order, so any pairing of the two layouts feeds the MFMA.  A slice
 // is E*BK*2 bytes either way, loaded as 1 KB direct loads split over the NW
-// waves; lines (K-major) or 8-element chunks (MN-major) past the extent are
-// clamped to the last valid ones.
+// waves.  K-major lines past the extent take an offset past the buffer
+// resource's range, which the hardware answers with zeros without touching
+// memory (the ragged last M-tile of an expert then streams only its real
+// rows); MN-major 8-element chunks past it are clamped to the last valid
+// chunk.
 template <int E, int BK, int NW>
 struct OpKM {
     static constexpr int CH = BK / 8, LINE = BK * 2, BYTES = E * LINE, J = BYTES / 1024 / NW;
@@ -152,8 +155,8 @@ struct OpKM {
     __device__ static uint32_t load_off(int w, int j, int lane, int64_t e0, int64_t ext, int64_t ld) {
         int line, c;
         load_pos(w, j, lane, line, c);
-        const int64_t r = (e0 + line < ext ? line : ext - 1 - e0);
-        return (uint32_t)((r * ld + 8 * c) * 2);
+        if (e0 + line >= ext) return 0x80000000u;
+        return (uint32_t)(((int64_t)line * ld + 8 * c) * 2);
     }
     // first k (within the slice) of the chunk that load j of wave w, lane l fetches
     __device__ static int load_k(int w, int j, int lane) {
