@@ -712,8 +712,11 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
 #pragma unroll
         for (int u = 0; u < R; ++u)
             if (wave / Cfg::STAGE_PER_SLOT == u) stage = slot_ptr(u) + (wave % Cfg::STAGE_PER_SLOT) * Cfg::STAGE_BYTES;
+        // 32-row blocks wholly past M (edge tiles, an expert's ragged last
+        // tile) are neither staged nor read back: nothing of them is stored
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
+            if (i >= live) break;
             const int row = i * 32 + (lane & 31);
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
@@ -734,6 +737,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
         const int64_t col = n0 + wn * Cfg::WTN + ch * 8;
 #pragma unroll
         for (int it = 0; it < Cfg::WTM / ROWS_PER_LOAD; ++it) {
+            if (it * ROWS_PER_LOAD >= live * 32) break;
             const int row = it * ROWS_PER_LOAD + rsub;
             u32x4 w = *(const lds_u32x4_t*)(stage + row * RB + (ch ^ stage_swz(row)) * 16);
             if (stage_half(row)) w = u32x4{w[2], w[3], w[0], w[1]};
