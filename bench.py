@@ -19,9 +19,9 @@ Beside the main figure the line carries:
   cpu_baseline  the CPU oracle timed on this host on a bounded sample of the
                 same workload (whole output rows), scaled to TFLOP/s;
   also          the same measurement for the 256^3 and 1024x1024x2048 fp16
-                GEMMs (these also replayed from a HIP graph of 50 launches, the
-                kernel time without the host's launch overhead), the fused
-                bias+ReLU form, the grouped MoE GEMM, the 4096^3 fp32
+                GEMMs, the fused bias+ReLU form and the grouped MoE GEMM
+                (these also replayed from a HIP graph of 50 or 20 launches,
+                the kernel time without the host's launch overhead), the 4096^3 fp32
                 GEMM (against the fp32 matrix peak), a 3x3 convolution on the
                 GEMM (implicit im2col; batch 32, 56x56, 64 -> 64 channels,
                 fp16) and attention scores Q K^T (128 heads, 2048 x 2048,
@@ -266,7 +266,9 @@ def grouped_setup(name, variant="float"):
     X, W = upload(c.X, c.dtype), upload(c.W, c.dtype)
     off = torch.from_numpy(c.offsets.astype(np.int32)).cuda()
     Y = torch.empty((c.T, c.N), dtype=X.dtype, device="cuda")
-    return c, (lambda: mg.mg_grouped_gemm(X, W, off, out=Y))
+    fn = lambda: mg.mg_grouped_gemm(X, W, off, out=Y)  # noqa: E731
+    fn.out = Y
+    return c, fn
 
 
 def measure_grouped(name, steps, warmup):
@@ -616,6 +618,13 @@ def main():
                        "hbm_gbs_compulsory": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
                        "kernel_ms_mean": round(r["kernel_ms"], 5), "warm_ms": r["spread"],
                        "tile_config": r["tile_config"]}
+        gms = time_graph(r["fn"], r["fn"].out, calls=20)
+        if gms:
+            gach = r["flops"] / (gms * 1e-3) / 1e12
+            ggbs = r["compulsory_bytes"] / (gms * 1e-3) / 1e9
+            also[gname].update({"graph_kernel_ms": round(gms, 5), "graph_kernel_tflops": round(gach, 2),
+                                "graph_hbm_gbs_compulsory": round(ggbs, 1),
+                                "graph_frac_hbm_peak": round(ggbs / PEAK_HBM_GBS, 4)})
         if not args.no_cold:
             cmed, cp90 = time_cold(r["fn"], 20)
             also[gname]["cold_kernel_ms_median"] = round(cmed, 5)
