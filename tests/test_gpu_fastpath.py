@@ -8,8 +8,9 @@ and fp16 subnormal inputs, against the oracle over every output element.
 * Prepacked A ([ceil(K/BK), M, BK], the yfxerp page's layout planner,
   section 3.2) on the same kernel, on the 1024x1024x2048 and 8192^3 shapes
   and a K tail.
-* fp16 subnormal inputs (A = k 2^-24, k in -4..4): exact in fp32, so the
-  bit-exact gate shows whether the matrix cores keep fp16 subnormals rather
+* fp16 and bf16 subnormal inputs (A = k 2^-24 or k 2^-133, k in -4..4):
+  exact in fp32, so the
+  bit-exact gate shows whether the matrix cores keep subnormals rather
   than flushing them (a flush would zero every product).
 """
 import numpy as np
@@ -139,3 +140,17 @@ def test_fp16_subnormal_inputs_bitexact(orc, M, N, K):
     _, ref_q = orc.gemm(c.A, c.B, F16)
     assert np.count_nonzero(ref_q & 0x7FFF) > 0.9 * ref_q.size
     assert_bitexact(got, ref_q, F16, "fp16 subnormal")
+
+
+@pytest.mark.parametrize("M,N,K", [(1024, 1024, 2048), (256, 256, 64), (300, 200, 129)])
+def test_bf16_subnormal_inputs_bitexact(orc, M, N, K):
+    """The same with bf16 subnormals (k 2^-133): the fp32 accumulators then
+    hold values near and below fp32's smallest normal, 2^-126, so a flush of
+    fp32 denormals would show as well as a flush of the inputs."""
+    c = inputs.subnormal_dense(M, N, K, 9400 + K, dtype=BF16)
+    assert np.all((c.A & 0x7F80) == 0)  # zero or subnormal
+    announce("bf16 subnormal inputs M=%d N=%d K=%d" % (M, N, K))
+    got = run(c)
+    _, ref_q = orc.gemm(c.A, c.B, BF16)
+    assert np.count_nonzero(ref_q & 0x7FFF) > 0.9 * ref_q.size
+    assert_bitexact(got, ref_q, BF16, "bf16 subnormal")

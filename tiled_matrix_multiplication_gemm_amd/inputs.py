@@ -107,16 +107,19 @@ def integer_dense(M, N, K, dtype, seed, lo=-4, hi=4, epilogue=False, name="custo
                      None if bias is None else to_bits(bias, dtype), relu=epilogue, integer=True)
 
 
-def subnormal_dense(M, N, K, seed, name="subnormal") -> DenseCase:
-    """fp16 A whose entries are k * 2^-24 with k uniform on -4..4 (zero and
-    the four smallest subnormals of either sign), B integers on -4..4.  Every
-    product and partial sum is an integer multiple of 2^-24 below 2^24 of
-    them, exact in fp32, so one rounding of the exact sum is the only
-    correct fp16 output (subnormal itself when |sum| < 2^-14)."""
+def subnormal_dense(M, N, K, seed, dtype=F16, name="subnormal") -> DenseCase:
+    """A whose entries are k * u with k uniform on -4..4 and u the smallest
+    subnormal of the type (2^-24 for fp16, 2^-133 for bf16): zero and the
+    four smallest subnormals of either sign.  B integers on -4..4.  Every
+    product and partial sum is an integer multiple of u below 2^24 of them,
+    exact in fp32 (whose own subnormals reach down to 2^-149), so one
+    rounding of the exact sum is the only correct output (subnormal itself
+    when small enough)."""
     rng = np.random.default_rng(seed)
-    A = rng.integers(-4, 5, size=(M, K)).astype(np.float64) * 2.0 ** -24
+    u = 2.0 ** -24 if dtype == F16 else 2.0 ** -133
+    A = rng.integers(-4, 5, size=(M, K)).astype(np.float64) * u
     B = rng.integers(-4, 5, size=(K, N)).astype(np.float64)
-    return DenseCase(name, M, N, K, F16, to_bits(A, F16), to_bits(B, F16), integer=True)
+    return DenseCase(name, M, N, K, dtype, to_bits(A, dtype), to_bits(B, dtype), integer=True)
 
 
 def dense_f32(M, N, K, seed, integer=False, epilogue=False, name="f32"):
