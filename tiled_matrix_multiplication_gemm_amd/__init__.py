@@ -133,35 +133,46 @@ def _check(status: int) -> None:
         raise RuntimeError(lib().mg_status_string(status).decode())
 
 
-def _dtype_code(t) -> int:
-    import torch
+# Per-call helpers.  They run before every launch, so torch objects they
+# need are looked up once (dtype codes, the raw-stream accessor) and devices
+# are compared as integers.
+_DTYPE_CODES = None
+_RAW_STREAM = None
 
-    if t.dtype == torch.float16:
-        return MG_F16
-    if t.dtype == torch.bfloat16:
-        return MG_BF16
-    if t.dtype == torch.float32:
-        return MG_F32
-    raise RuntimeError("MG_ERR_UNSUPPORTED_DTYPE: tensor dtype %s is not float16/bfloat16/float32" % t.dtype)
+
+def _dtype_code(t) -> int:
+    global _DTYPE_CODES
+    if _DTYPE_CODES is None:
+        import torch
+
+        _DTYPE_CODES = {torch.float16: MG_F16, torch.bfloat16: MG_BF16, torch.float32: MG_F32}
+    code = _DTYPE_CODES.get(t.dtype)
+    if code is None:
+        raise RuntimeError("MG_ERR_UNSUPPORTED_DTYPE: tensor dtype %s is not float16/bfloat16/float32" % t.dtype)
+    return code
 
 
 def _stream(t):
     """torch's current HIP stream on t's device, as a raw handle."""
-    import torch
+    global _RAW_STREAM
+    if _RAW_STREAM is None:
+        import torch
 
-    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
-    if raw is not None:
-        return raw(t.device.index)
-    return torch.cuda.current_stream(t.device).cuda_stream
+        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        _RAW_STREAM = raw if raw is not None else (lambda d: torch.cuda.current_stream(d).cuda_stream)
+    return _RAW_STREAM(t.get_device())
 
 
 def _require_gpu(*ts):
     """Every tensor on the GPU, all on the first one's device."""
+    dev = None
     for t in ts:
         if not t.is_cuda:
             raise RuntimeError("mi355gemm operates on GPU tensors only (got a %s tensor)" % t.device)
-    for t in ts[1:]:
-        if t.device != ts[0].device:
+        d = t.get_device()
+        if dev is None:
+            dev = d
+        elif d != dev:
             raise RuntimeError("MG_ERR_INVALID_ARG: tensors on different devices (%s, %s)" % (ts[0].device, t.device))
 
 
@@ -176,7 +187,7 @@ def _check_out(out, shape, like):
     and a unit inner stride (the C ABI sees only a pointer and row strides,
     so a smaller or differently typed buffer would be overrun or misread)."""
     _require_gpu(like, out)
-    if tuple(out.shape) != tuple(shape):
+    if out.shape != shape:
         raise RuntimeError("MG_ERR_INVALID_ARG: out has shape %s, expected %s" % (tuple(out.shape), tuple(shape)))
     if out.dtype != like.dtype:
         raise RuntimeError("MG_ERR_UNSUPPORTED_DTYPE: out is %s, expected %s" % (out.dtype, like.dtype))
@@ -186,8 +197,6 @@ def _check_out(out, shape, like):
 
 def mg_gemm(a, b, out=None):
     """out[M,N] = a[M,K] @ b[K,N] (fp16/bf16, fp32 accumulation)."""
-    import torch
-
     _require_gpu(a, b)
     M, K = a.shape
     K2, N = b.shape
@@ -195,18 +204,19 @@ def mg_gemm(a, b, out=None):
         raise RuntimeError("MG_ERR_INVALID_ARG: inner dimensions differ (%d vs %d)" % (K, K2))
     _same_dtype(a, b)
     if out is None:
+        import torch
+
         out = torch.empty((M, N), dtype=a.dtype, device=a.device)
     _check_out(out, (M, N), a)
-    _check(lib().mg_gemm(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, a.stride(0), a.stride(1),
-                         b.stride(0), b.stride(1), out.stride(0), out.stride(1), _dtype_code(a), _dtype_code(out),
-                         _stream(a)))
+    sa, sb, so = a.stride(), b.stride(), out.stride()
+    code = _dtype_code(a)
+    _check(lib().mg_gemm(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, sa[0], sa[1], sb[0], sb[1],
+                         so[0], so[1], code, code, _stream(a)))
     return out
 
 
 def mg_gemm_bias_relu(a, b, bias, out=None):
     """out = ReLU(a @ b + bias) in one kernel."""
-    import torch
-
     _require_gpu(a, b, bias)
     M, K = a.shape
     K2, N = b.shape
@@ -214,11 +224,14 @@ def mg_gemm_bias_relu(a, b, bias, out=None):
         raise RuntimeError("MG_ERR_INVALID_ARG: shapes a[M,K], b[K,N], contiguous bias[N] expected")
     _same_dtype(a, b, bias)
     if out is None:
+        import torch
+
         out = torch.empty((M, N), dtype=a.dtype, device=a.device)
     _check_out(out, (M, N), a)
+    sa, sb, so = a.stride(), b.stride(), out.stride()
+    code = _dtype_code(a)
     _check(lib().mg_gemm_bias_relu(a.data_ptr(), b.data_ptr(), bias.data_ptr(), out.data_ptr(), M, N, K,
-                                   a.stride(0), a.stride(1), b.stride(0), b.stride(1), out.stride(0),
-                                   out.stride(1), _dtype_code(a), _dtype_code(out), _stream(a)))
+                                   sa[0], sa[1], sb[0], sb[1], so[0], so[1], code, code, _stream(a)))
     return out
 
 
