@@ -368,10 +368,12 @@ int mg_last_config(void);
  * kernel, 2 = direct-to-LDS K-split kernel; -1 before any launch. */
 int mg_last_kernel(void);
 /* Configuration the table selects for a problem of this shape: dense when
- * `grouped` is 0, else a grouped problem of `grouped` experts over M = T
- * rows.  The table's model and its per-shape cache are generated by the
- * offline sweep (mg_rates.h from profiles/table_sweep.json). */
-int mg_select_config(int64_t M, int64_t N, int64_t K, mg_dtype dtype, int grouped);
+ * `grouped` is 0 (a batched product of `batch` entries of M x N x K when
+ * batch > 1, as mg_gemm_batched and mg_attention_scores launch it), else a
+ * grouped problem of `grouped` experts over M = T rows (batch ignored).  The
+ * table's model and its per-shape cache are generated by the offline sweep
+ * (mg_rates.h from profiles/table_sweep.json). */
+int mg_select_config(int64_t M, int64_t N, int64_t K, mg_dtype dtype, int grouped, int64_t batch);
 
 #ifdef __cplusplus
 }

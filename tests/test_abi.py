@@ -221,14 +221,14 @@ def test_config_table(L):
 
 def test_table_selection_for_the_workloads(L):
     sel = lambda *a: L.mg_select_config(*a)
-    big = mg.mg_config_info(sel(8192, 8192, 8192, BF16, 0))
+    big = mg.mg_config_info(sel(8192, 8192, 8192, BF16, 0, 1))
     assert big["bm"] * big["bn"] >= 128 * 128
-    mid = mg.mg_config_info(sel(1024, 1024, 2048, F16, 0))
+    mid = mg.mg_config_info(sel(1024, 1024, 2048, F16, 0, 1))
     # a 1024 x 1024 output must still give every CU at least one tile
     assert (1024 // mid["bm"]) * (1024 // mid["bn"]) >= 128
     for cid in range(L.mg_num_configs()):
         assert L.mg_set_config(cid) == OK
-        assert L.mg_select_config(8192, 8192, 8192, BF16, 0) == cid
+        assert L.mg_select_config(8192, 8192, 8192, BF16, 0, 1) == cid
     assert L.mg_set_config(-1) == OK
 
 

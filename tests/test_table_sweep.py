@@ -46,9 +46,19 @@ def test_every_swept_shape_takes_its_measured_best_row(data, L):
         ms = {int(r): t for r, t in next(r for r in data["dense"] if (r["M"], r["N"], r["K"]) ==
                                          (b["M"], b["N"], b["K"]))["ms"].items()}
         assert ms[b["best_row"]] == min(ms[r] for r in ms if r in (0, 1, 2, 3, 4, 6, 8))
-        assert L.mg_select_config(b["M"], b["N"], b["K"], b["dtype"], 0) == b["best_row"], b
+        assert L.mg_select_config(b["M"], b["N"], b["K"], b["dtype"], 0, 1) == b["best_row"], b
     for b in S["grouped_best"]:
-        assert L.mg_select_config(b["T"], b["N"], b["K"], b["dtype"], b["E"]) == b["best_row"], b
+        assert L.mg_select_config(b["T"], b["N"], b["K"], b["dtype"], b["E"], 1) == b["best_row"], b
+    assert S["batched_best"], "the sweep times batched (attention-score) shapes"
+    for b in S["batched_best"]:
+        ms = next(r for r in data["batched"] if (r["batch"], r["M"], r["N"], r["K"]) ==
+                  (b["batch"], b["M"], b["N"], b["K"]))["ms"]
+        assert float(ms[str(b["best_row"])]) == min(float(t) for r, t in ms.items() if int(r) in (0, 1, 2, 3, 4, 6, 8))
+        assert L.mg_select_config(b["M"], b["N"], b["K"], b["dtype"], 0, b["batch"]) == b["best_row"], b
+        # the same shape as one dense problem is not the cached batched one
+        assert L.mg_select_config(b["M"], b["N"], b["K"], b["dtype"], 0, 1) == sweep.model_pick(
+            data, sweep.fit(data), b["M"], b["N"], b["K"]) or (b["M"], b["N"], b["K"]) in {
+            (d["M"], d["N"], d["K"]) for d in data["dense"]}
 
 
 OFF_SWEEP = [(8192, 4096, 4096), (777, 1300, 960), (100000, 96, 2048), (64, 64, 64), (2560, 2560, 2560),
@@ -58,13 +68,13 @@ OFF_SWEEP = [(8192, 4096, 4096), (777, 1300, 960), (100000, 96, 2048), (64, 64, 
 @pytest.mark.parametrize("M,N,K", OFF_SWEEP)
 def test_off_sweep_shapes_take_the_models_choice(data, L, M, N, K):
     F = sweep.fit(data)
-    assert L.mg_select_config(M, N, K, 0, 0) == sweep.model_pick(data, F, M, N, K)
+    assert L.mg_select_config(M, N, K, 0, 0, 1) == sweep.model_pick(data, F, M, N, K)
 
 
 @pytest.mark.parametrize("E,T,N,K", [(4, 1000, 512, 256), (128, 65536, 2048, 1024), (32, 8192, 1024, 4096)])
 def test_grouped_shapes_take_the_models_choice(data, L, E, T, N, K):
     F = sweep.fit(data)
-    assert L.mg_select_config(T, N, K, 0, E) == sweep.model_pick(data, F, T, N, K, E)
+    assert L.mg_select_config(T, N, K, 0, E, 1) == sweep.model_pick(data, F, T, N, K, E)
 
 
 def _py_splitk_choose(data, M, N, K):
@@ -113,7 +123,7 @@ def test_layout_planner_gate(data, L):
     for (M, N, K) in [(1024, 1024, 2048), (8192, 8192, 8192), (4096, 4096, 4096), (2048, 2048, 2048),
                       (12544, 256, 2304), (65536, 64, 1152), (777, 1300, 960)]:
         got = L.mg_prepack_uses_to_pay(M, N, K, 0)
-        row = L.mg_select_config(M, N, K, 0, 0)
+        row = L.mg_select_config(M, N, K, 0, 0, 1)
         if ratio.get(row, -1.0) <= 0.0 or ratio[row] >= 1.0:
             assert got == -1, (M, N, K, row)
             continue
@@ -134,12 +144,14 @@ def test_counters_cover_every_table_choice(data):
     row the measured best, the direct-to-LDS or K-split kernel, and the
     derived ratios within their ranges."""
     S = sweep.summarize(data)
-    best = {(b["M"], b["N"], b["K"], 0): b["best_row"] for b in S["dense_best"]}
-    best.update({(b["T"], b["N"], b["K"], b["E"]): b["best_row"] for b in S["grouped_best"]})
+    best = {(b["M"], b["N"], b["K"], 0, 1): b["best_row"] for b in S["dense_best"]}
+    best.update({(b["T"], b["N"], b["K"], b["E"], 1): b["best_row"] for b in S["grouped_best"]})
+    best.update({(b["M"], b["N"], b["K"], 0, b["batch"]): b["best_row"] for b in S["batched_best"]})
     shapes = data["counters"]["shapes"]
-    assert sorted((c["M"], c["N"], c["K"], c["E"]) for c in shapes) == sorted(best)
+    key = lambda c: (c["M"], c["N"], c["K"], c["E"], c.get("B", 1))  # noqa: E731
+    assert sorted(key(c) for c in shapes) == sorted(best)
     for c in shapes:
-        assert c["row"] == best[(c["M"], c["N"], c["K"], c["E"])], c
+        assert c["row"] == best[key(c)], c
         assert ("gemm_dlds_kernel" in c["kernel"]) == (c["row"] != 7), c
         assert 0.0 < c["mfma_busy_fraction"] <= 1.0
         assert 0.0 <= c["lds_bank_conflict_ratio"] < 1.0

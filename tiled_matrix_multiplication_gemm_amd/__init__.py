@@ -112,7 +112,7 @@ def lib() -> ctypes.CDLL:
         L.mg_last_kernel.restype = cint
         L.mg_last_kernel.argtypes = []
         L.mg_select_config.restype = cint
-        L.mg_select_config.argtypes = [i64, i64, i64, cint, cint]
+        L.mg_select_config.argtypes = [i64, i64, i64, cint, cint, i64]
         shp = ctypes.POINTER(Conv2dShape)
         L.mg_conv2d_output_hw.restype = cint
         L.mg_conv2d_output_hw.argtypes = [shp, ctypes.POINTER(i64), ctypes.POINTER(i64)]
@@ -397,9 +397,9 @@ def mg_prepack_uses_to_pay(M: int, N: int, K: int, dtype: int = MG_F16) -> int:
     return int(lib().mg_prepack_uses_to_pay(M, N, K, dtype))
 
 
-def mg_select_config(M: int, N: int, K: int, dtype: int = MG_F16, grouped: int = 0) -> int:
+def mg_select_config(M: int, N: int, K: int, dtype: int = MG_F16, grouped: int = 0, batch: int = 1) -> int:
     """The table's row for a dense problem, or a grouped one of `grouped` experts."""
-    return int(lib().mg_select_config(M, N, K, dtype, int(grouped)))
+    return int(lib().mg_select_config(M, N, K, dtype, int(grouped), int(batch)))
 
 
 def mg_num_configs() -> int:

@@ -34,7 +34,7 @@ constexpr mg_config_desc describe(int id, const char* name) {
 const mg_config_desc kTable[kNumConfigs] = {
     describe<Cfg0, Fast0>(0, "t256x256_w2x4_k32r5"), describe<Cfg1, Fast1>(1, "t128x128_w2x2"),
     describe<Cfg2, Fast2>(2, "t64x64_w2x2"),   describe<Cfg3, Fast3>(3, "t128x256_w2x2"),
-    describe<Cfg4, Fast4>(4, "t256x128_w2x2"), describe<Cfg5, void>(5, "t128x128k32_w2x2"),
+    describe<Cfg4, Fast4>(4, "t256x128_w4x2_2cu"), describe<Cfg5, void>(5, "t128x128k32_w2x2"),
     describe<Cfg6, Fast6>(6, "t256x256_w2x2_k32r5"), describe<Cfg7, Fast7>(7, "t64x64_ksplit4"),
     describe<Cfg8, Fast8>(8, "t256x64_w4x2"),
 };
@@ -54,9 +54,11 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // time per tile fitted by the offline sweep (mg_rates.h, generated from
 // profiles/table_sweep.json).  A shape the sweep timed takes the row that
 // measured fastest on it (the cached top-1 of "Using Triton to optimise GEMM
-// across chips", section 3.3).  Grouped problems count the tiles of E
-// experts with T / E rows each (the host does not read the device offsets);
-// a batched product counts the tiles of every entry.
+// across chips", section 3.3); swept shapes are keyed by the expert count
+// (grouped) and the batch count (batched products such as attention scores)
+// as well.  Grouped problems count the tiles of E experts with T / E rows
+// each (the host does not read the device offsets); a batched product counts
+// the tiles of every entry.
 double model_seconds(const rates::RowRate& r, int64_t tiles, int64_t K) {
     return (double)cdiv(tiles, 256) * ((double)r.bm * r.bn * (double)K * rates::kSecPerElemK / r.rate +
                                        rates::kFixedSec);
@@ -70,10 +72,9 @@ int64_t tiles_of(const rates::RowRate& r, int64_t M, int64_t N, int64_t experts,
 int select_config(int64_t M, int64_t N, int64_t K, int64_t experts, int64_t batch = 1) {
     int forced = g_forced.load();
     if (forced >= 0) return forced;
-    if (batch <= 1) {
-        for (const rates::Swept& sw : rates::kSwept)
-            if (sw.M == M && sw.N == N && sw.K == K && sw.experts == experts) return sw.row;
-    }
+    const int64_t b = batch > 1 ? batch : 1;
+    for (const rates::Swept& sw : rates::kSwept)
+        if (sw.M == M && sw.N == N && sw.K == K && sw.experts == experts && sw.batch == b) return sw.row;
     int best = rates::kRows[0].id;
     double best_t = -1.0;
     for (const rates::RowRate& r : rates::kRows) {
@@ -715,9 +716,9 @@ mg_status mg_set_raster(int group_m, int xcd_remap) {
 
 int mg_last_kernel(void) { return g_last_kernel.load(); }
 
-int mg_select_config(int64_t M, int64_t N, int64_t K, mg_dtype dtype, int grouped) {
+int mg_select_config(int64_t M, int64_t N, int64_t K, mg_dtype dtype, int grouped, int64_t batch) {
     (void)dtype;
-    return select_config(M, N, K, grouped > 0 ? grouped : 0);
+    return select_config(M, N, K, grouped > 0 ? grouped : 0, grouped > 0 ? 1 : batch);
 }
 
 mg_status mg_conv2d_output_hw(const mg_conv2d_shape* shape, int64_t* out_h, int64_t* out_w) {

@@ -15,7 +15,8 @@ done once, offline:
 
 `run` (GPU) times every row on a grid of shapes -- the five workloads,
 squares, tall-skinny and wide outputs, large K, shapes off the tile grid,
-grouped (MoE) problems -- forcing each row through mg_set_config and visiting
+grouped (MoE) problems, batched attention-score products -- forcing each row
+through mg_set_config and visiting
 the rows round-robin so that clock drift does not favour the rows measured
 last; it also times split-K counts on the under-filled shapes, the prepacked
 A against the row-major A, and a plain copy (HBM rate).  Raw times go to a
@@ -25,11 +26,14 @@ JSON file.
 t = rounds * (BM * BN * K * c / rate_row + f), rounds = ceil(tiles / 256),
 one tile per CU at a time -- and writes csrc/mg_rates.h: the fitted per-row
 rates, c and f, the copy rate, the prepacked/plain time ratio per row, and
-the measured best row of every swept shape, which select_config() returns
-for that exact shape (the cache of the pages' top-1) before it consults the
-model.  The fit and the generated header are both functions of the JSON
-alone; `check` regenerates the header and compares it with the committed
-one.
+the measured best row of every swept shape (grouped shapes keyed by their
+expert count, batched ones by their entry count), which select_config()
+returns for that exact shape (the cache of the pages' top-1) before it
+consults the model.  The model counts one tile per CU at a time; rows that
+run two workgroups per CU win where it cannot see it (epilogue-bound
+batched products) and are picked there through the cache.  The fit and the
+generated header are both functions of the JSON alone; `check` regenerates
+the header and compares it with the committed one.
 
 `counters` (GPU) records the hardware counters behind the table's choices:
 one rocprofv3 --pmc pass per counter group, each running the table's own row
@@ -72,6 +76,10 @@ DENSE_SHAPES = [
 # (E, T, N, K, dtype): grouped problems, balanced routing drawn like the MoE workload
 GROUPED_SHAPES = [(32, 8192, 4096, 1024, F16), (8, 2048, 1024, 1024, F16), (64, 16384, 1408, 2048, BF16),
                   (16, 4096, 2048, 512, F16)]
+# (heads, Lq, Lk, d, dtype): attention-score products Q K^T, one batched
+# launch over the heads (B given transposed)
+BATCHED_SHAPES = [(128, 2048, 2048, 128, BF16), (256, 1024, 1024, 64, F16), (64, 4096, 4096, 128, BF16),
+                  (32, 512, 512, 64, F16)]
 SPLIT_SHAPES = [(256, 256, 65536, BF16), (512, 512, 32768, BF16), (1024, 1024, 16384, F16),
                 (128, 4096, 16384, BF16), (2048, 2048, 16384, BF16), (1024, 1024, 2048, F16)]
 PACKED_SHAPES = [(1024, 1024, 2048, F16), (4096, 4096, 4096, BF16), (8192, 8192, 8192, BF16)]
@@ -134,8 +142,8 @@ def run(out_path, rounds):
 
     rows = [r for r in range(mg.mg_num_configs())]
     res = {"device": torch.cuda.get_device_name(0), "rounds": rounds, "cus": CUS,
-           "rows": {str(r): mg.mg_config_info(r) for r in rows}, "dense": [], "grouped": [], "splitk": [],
-           "packed": []}
+           "rows": {str(r): mg.mg_config_info(r) for r in rows}, "dense": [], "grouped": [], "batched": [],
+           "splitk": [], "packed": []}
     for (M, N, K, dt) in DENSE_SHAPES:
         A, B, C = _dense_tensors(M, N, K, dt, 11 + M % 97 + N % 89 + K % 83)
         times = {r: [] for r in rows}
@@ -174,6 +182,26 @@ def run(out_path, rounds):
         res["grouped"].append(rec)
         print("grouped E=%d T=%d N=%d K=%d: %s" % (E, T, N, K, rec["ms"]), flush=True)
         del X, W, Y
+    for (H, Lq, Lk, d, dt) in BATCHED_SHAPES:
+        tdt = torch.float16 if dt == F16 else torch.bfloat16
+        q = (torch.randn((H, Lq, d), device="cuda") * d ** -0.25).to(tdt)
+        k = (torch.randn((H, Lk, d), device="cuda") * d ** -0.25).to(tdt)
+        S = torch.empty((H, Lq, Lk), dtype=tdt, device="cuda")
+        times = {r: [] for r in rows}
+        for rnd in range(rounds):
+            for r in (rows if rnd % 2 == 0 else rows[::-1]):
+                mg.mg_set_config(r)
+                try:
+                    times[r].append(_time(lambda: mg.mg_attention_scores(q, k, out=S)))
+                except RuntimeError:
+                    pass  # a row without a direct-to-LDS kernel refuses the transposed K
+                finally:
+                    mg.mg_set_config(-1)
+        rec = {"batch": H, "M": Lq, "N": Lk, "K": d, "dtype": dt,
+               "ms": {str(r): round(statistics.median(v), 5) for r, v in times.items() if v}}
+        res["batched"].append(rec)
+        print("batched %d x %d x %d x %d: %s" % (H, Lq, Lk, d, rec["ms"]), flush=True)
+        del q, k, S
     for (M, N, K, dt) in SPLIT_SHAPES:
         A, B, C = _dense_tensors(M, N, K, dt, 77 + K % 101)
         ms = {}
@@ -272,7 +300,7 @@ def counters_run(json_path, order_path):
         for _ in range(COUNTER_CALLS):
             mg.mg_gemm(A, B, out=C)
         torch.cuda.synchronize()
-        order.append({"M": M, "N": N, "K": K, "dtype": dt, "E": 0, "row": mg.mg_last_config(),
+        order.append({"M": M, "N": N, "K": K, "dtype": dt, "E": 0, "B": 1, "row": mg.mg_last_config(),
                       "family": mg.mg_last_kernel()})
         print("counters: dense %d x %d x %d row %d" % (M, N, K, order[-1]["row"]), flush=True)
         del A, B, C
@@ -286,10 +314,23 @@ def counters_run(json_path, order_path):
         for _ in range(COUNTER_CALLS):
             mg.mg_grouped_gemm(X, W, off, out=Y)
         torch.cuda.synchronize()
-        order.append({"M": T, "N": N, "K": K, "dtype": dt, "E": E, "row": mg.mg_last_config(),
+        order.append({"M": T, "N": N, "K": K, "dtype": dt, "E": E, "B": 1, "row": mg.mg_last_config(),
                       "family": mg.mg_last_kernel()})
         print("counters: grouped E=%d T=%d N=%d K=%d row %d" % (E, T, N, K, order[-1]["row"]), flush=True)
         del X, W, Y
+    for rec in data.get("batched", []):
+        H, Lq, Lk, d, dt = rec["batch"], rec["M"], rec["N"], rec["K"], rec["dtype"]
+        tdt = torch.float16 if dt == F16 else torch.bfloat16
+        q = (torch.randn((H, Lq, d), device="cuda") * d ** -0.25).to(tdt)
+        k = (torch.randn((H, Lk, d), device="cuda") * d ** -0.25).to(tdt)
+        S = torch.empty((H, Lq, Lk), dtype=tdt, device="cuda")
+        for _ in range(COUNTER_CALLS):
+            mg.mg_attention_scores(q, k, out=S)
+        torch.cuda.synchronize()
+        order.append({"M": Lq, "N": Lk, "K": d, "dtype": dt, "E": 0, "B": H, "row": mg.mg_last_config(),
+                      "family": mg.mg_last_kernel()})
+        print("counters: batched %d x %d x %d x %d row %d" % (H, Lq, Lk, d, order[-1]["row"]), flush=True)
+        del q, k, S
     with open(order_path, "w") as f:
         json.dump(order, f)
 
@@ -380,9 +421,9 @@ def counters(json_path, work_dir, timeout_s):
     with open(json_path, "w") as f:
         json.dump(data, f, indent=1, sort_keys=True)
     for r in data["counters"]["shapes"]:
-        print("%6d x %5d x %5d E=%2d row %d  mfma busy %s  lds conflicts %s  l2 hit %s" % (
-            r["M"], r["N"], r["K"], r["E"], r["row"], r.get("mfma_busy_fraction"), r.get("lds_bank_conflict_ratio"),
-            r.get("l2_hit_rate")), flush=True)
+        print("%6d x %5d x %5d E=%2d B=%3d row %d  mfma busy %s  lds conflicts %s  l2 hit %s" % (
+            r["M"], r["N"], r["K"], r["E"], r.get("B", 1), r["row"], r.get("mfma_busy_fraction"),
+            r.get("lds_bank_conflict_ratio"), r.get("l2_hit_rate")), flush=True)
 
 
 # (label, row, GROUP_M, XCD renumbering, inputs) of the 8192^3 bf16 GEMM
@@ -571,7 +612,13 @@ def summarize(data):
         m = model_pick(data, F, rec["T"], rec["N"], rec["K"], rec["E"])
         gbest.append({"E": rec["E"], "T": rec["T"], "N": rec["N"], "K": rec["K"], "dtype": rec["dtype"],
                       "best_row": b, "best_ms": ms[b], "model_row": m, "model_ms": ms[m]})
-    return {"fit": F, "rows": nrows, "dense_best": best, "grouped_best": gbest,
+    bbest = []
+    for rec in data.get("batched", []):
+        ms = {int(r): float(t) for r, t in rec["ms"].items() if int(r) in dict((a, 0) for a, _, _ in _model_rows(data))}
+        b = min(ms, key=lambda r: ms[r])
+        bbest.append({"batch": rec["batch"], "M": rec["M"], "N": rec["N"], "K": rec["K"], "dtype": rec["dtype"],
+                      "best_row": b, "best_ms": ms[b]})
+    return {"fit": F, "rows": nrows, "dense_best": best, "grouped_best": gbest, "batched_best": bbest,
             "model_agrees": "%d of %d dense shapes" % (agree, len(best)),
             "model_time_lost_max": round(max(lost), 4), "model_time_lost_median": round(statistics.median(lost), 4),
             "packed_ratio": packed_ratio(data), "copy_bytes_per_s": copy_rate(data),
@@ -635,14 +682,17 @@ def header_text(data, json_rel):
               "struct Swept {",
               "    int64_t M, N, K;",
               "    int32_t experts;  // 0: dense",
+              "    int64_t batch;    // entries of a batched product (1: one)",
               "    int32_t row;",
               "};",
               "// the measured best row of every swept shape (cached top-1)",
               "inline constexpr Swept kSwept[] = {"]
     for b in S["dense_best"]:
-        lines.append("    {%d, %d, %d, 0, %d}," % (b["M"], b["N"], b["K"], b["best_row"]))
+        lines.append("    {%d, %d, %d, 0, 1, %d}," % (b["M"], b["N"], b["K"], b["best_row"]))
     for b in S["grouped_best"]:
-        lines.append("    {%d, %d, %d, %d, %d}," % (b["T"], b["N"], b["K"], b["E"], b["best_row"]))
+        lines.append("    {%d, %d, %d, %d, 1, %d}," % (b["T"], b["N"], b["K"], b["E"], b["best_row"]))
+    for b in S["batched_best"]:
+        lines.append("    {%d, %d, %d, 0, %d, %d}," % (b["M"], b["N"], b["K"], b["batch"], b["best_row"]))
     lines += ["};", "", "}  // namespace rates", "}  // namespace mg", ""]
     return "\n".join(lines)
 
