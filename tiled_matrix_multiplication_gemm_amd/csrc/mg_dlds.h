@@ -700,11 +700,16 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
         constexpr int CH = Cfg::WTN / 8;  // 16-byte chunks per staged row
         constexpr int RB = Cfg::WTN * 2;  // bytes per staged row
         auto stage_swz = [](int row) { return (row ^ (row >> 3)) & (CH - 1); };
-        // The 32 lanes one ds_write_b64 serves together hold rows 0..31 of a
-        // block at the same 8-byte half of their chunks; swapping the halves
-        // of every other group of rows (bit HS of the row) puts them in
-        // distinct banks.  The read-back swaps them back.
-        constexpr int HS = CH == 4 ? 2 : 4;
+        // A ds_write_b64 is served 16 lanes at a time over 128 bytes of
+        // banks (what the bank-conflict counter shows): rows 0..15 of a block,
+        // all at the same 8-byte half of their chunks.  The chunk swizzle
+        // separates them except for pairs of rows that differ in bit
+        // HS = log2(CH) (alone for CH = 4, together with bit 0 for CH = 8),
+        // so swapping the halves of the rows whose bit HS is set puts all 16
+        // in distinct banks.  (Bit 4 for CH = 8 left a two-way conflict on
+        // every write.)
+        // The read-back swaps them back.
+        constexpr int HS = CH == 4 ? 2 : 3;
         auto stage_half = [](int row) { return (row >> HS) & 1; };
         wait_vmcnt<0>();
         ring_barrier();  // every wave is out of the K loop: the ring is free
