@@ -80,7 +80,9 @@ const char* mg_status_string(mg_status status);
  * second is a row stride so large (about 2^24 elements or more) that a
  * 64-row span of the operand passes the direct-to-LDS kernel's 31-bit
  * load offsets.  Row-major operands with such strides run on the general
- * kernel.
+ * kernel.  The output tiles of one call (BM x BN each, counted over every
+ * batch entry or split where the entry point has them) must number below
+ * 2^31, else MG_ERR_INVALID_ARG.
  *
  * fp32 (in_dtype == out_dtype == MG_F32; the 4096^3 fp32 row of the FlagOS
  * cross-chip page's benchmark table, section 3.4): fp32 inputs on the fp32
@@ -196,7 +198,9 @@ mg_status mg_gemm_splitk_noalloc(const void* A, const void* B, void* C, int64_t 
  *    it to at least the previous one.  Offsets that break the rules
  *    therefore leave some rows of Y unspecified, but never cause an access
  *    outside X, W and Y.  Experts with no rows write nothing.
- * dtype is both the input and the output type.
+ * dtype is both the input and the output type.  T and E must be below 2^31,
+ * and so must the tiles the launch is sized for, (ceil(T / BM) + E) times
+ * the column tiles (else MG_ERR_INVALID_ARG).
  */
 mg_status mg_grouped_gemm(const void* X, const void* W, void* Y, const int32_t* expert_offsets,
                           int64_t E, int64_t T, int64_t N, int64_t K,

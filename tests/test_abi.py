@@ -173,6 +173,24 @@ def test_grouped_rejects_bad_arguments(L, kw, status):
     assert grouped(L, **kw) == status
 
 
+def test_tile_counts_beyond_31_bits_are_refused(L):
+    """Launches are sized in 64 bits and refused (MG_ERR_INVALID_ARG, before
+    any HIP call) when their tile count does not fit 31 bits, however the
+    count would wrap if narrowed first: a square output of 2^36 rows and
+    columns (2^56 tiles), a tile-row count alone past 2^31 (M = 2^45), fp32
+    and batched forms, and grouped launches whose token count, expert count
+    or column count push the worst-case tile count past 2^31."""
+    big = 1 << 36
+    assert gemm(L, M=big, N=big, sbk=big, scm=big) == INVALID
+    assert gemm(L, M=1 << 45) == INVALID
+    assert gemm(L, M=1 << 45, din=2, dout=2) == INVALID
+    assert gemm_batched(L, batch=(1 << 31) - 1, M=4096, N=4096, sbk=4096, scm=4096, sab=0, sbb=0,
+                        scb=4096 * 4096) == INVALID
+    t = (1 << 31) - 1
+    assert grouped(L, E=t, T=t) == INVALID
+    assert grouped(L, E=2, T=t, N=big, swk=big, swe=64 * big, sym=big) == INVALID
+
+
 def test_grouped_empty_is_noop(L):
     assert grouped(L, T=0, X=None, Y=None, off=None) == OK
     assert grouped(L, E=0, T=0, X=None, W=None, Y=None, off=None) == OK

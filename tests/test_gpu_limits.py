@@ -19,6 +19,9 @@
 * Grouped expert offsets that break the rules: nothing outside Y is
   written, and the result is the product over the partition the kernel
   clamps them to.
+* The largest token count the grouped entry point takes (T = 2^31 - 1),
+  with one expert holding all but 100 of them: the device-side count of
+  that expert's row tiles must not overflow 32 bits.
 """
 import numpy as np
 import pytest
@@ -223,3 +226,41 @@ def test_grouped_offsets_out_of_order_stay_inside_the_buffers(orc, E):
     assert np.all(got[:lo] == CANARY) and np.all(got[hi:] == CANARY), "rows outside the partition written"
     _, ref_q = orc.grouped_gemm(X[lo:hi], W, clamped - lo, F16)
     assert_bitexact(got[lo:hi], ref_q, F16, "clamped partition")
+
+
+def test_grouped_largest_token_count(orc):
+    """T = 2^31 - 1 tokens (K = N = 8): expert 0 takes rows 0..99, expert 1
+    the other 2^31 - 101.  X repeats a seeded block of P = 65521 rows (a
+    prime, so a row offset error lands on a different block row), copied on
+    the device; the oracle reads the same block on the host, so none of its
+    inputs comes back from the device.  Checked bit-exact against the
+    oracle: 4096 sampled rows, the rows around the expert boundary and the
+    last 300 rows (Y starts as the canary, so a tile that is never run
+    shows up)."""
+    import torch
+
+    T, K, N, P = 2 ** 31 - 1, 8, 8, 65521
+    rng = np.random.default_rng(9600)
+    blk = inputs.to_bits(rng.integers(-4, 5, size=(P, K)).astype(np.float64), F16)
+    W = inputs.to_bits(rng.integers(-4, 5, size=(2, K, N)).astype(np.float64), F16)
+    off = np.array([0, 100, T], dtype=np.int64)
+    announce("grouped T = 2^31 - 1, K = N = 8, experts of 100 and 2^31 - 101 rows")
+    X = torch.empty((T, K), dtype=torch.float16, device="cuda")
+    q = T // P
+    blk_d = to_dev(blk, F16)
+    X[: q * P].view(q, P, K).copy_(blk_d.unsqueeze(0).expand(q, P, K))
+    X[q * P:].copy_(blk_d[: T - q * P])
+    del blk_d
+    Y = torch.full((T, N), CANARY, dtype=torch.int16, device="cuda").view(torch.float16)
+    mg.mg_grouped_gemm(X, to_dev(W, F16), torch.from_numpy(off.astype(np.int32)).cuda(), out=Y)
+    torch.cuda.synchronize()
+    del X
+    rows = np.unique(np.concatenate([rng.integers(0, T, size=4096), np.arange(0, 3), np.arange(97, 103),
+                                     np.arange(T - 300, T)]))
+    got = to_host(Y[torch.from_numpy(rows).cuda()])
+    del Y
+    torch.cuda.empty_cache()
+    for e in range(2):
+        sel = (rows >= off[e]) & (rows < off[e + 1])
+        _, ref_q = orc.gemm(blk[rows[sel] % P], W[e], F16)
+        assert_bitexact(got[sel], ref_q, F16, "expert %d" % e)

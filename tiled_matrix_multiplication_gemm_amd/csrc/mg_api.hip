@@ -144,18 +144,19 @@ mg_status check_dtype(mg_dtype in, mg_dtype out) {
 // ---- launch --------------------------------------------------------------------
 mg_status launch(int cfg, int dt, bool epi, int mode, KArgs& a, hipStream_t s, int ta = 0, int tb = 0) {
     const mg_config_desc& d = kTable[cfg];
-    a.tiles_n = (int32_t)cdiv(a.N, d.bn);
-    int64_t grid;
-    if (mode == MODE_GROUPED) {
-        a.tiles_m = 0;
-        grid = (cdiv(a.M, d.bm) + a.E) * a.tiles_n;
-    } else {
-        a.tiles_m = (int32_t)cdiv(a.M, d.bm);
-        grid = (int64_t)a.tiles_m * a.tiles_n * (a.batch > 1 ? a.batch : 1);
-        if (mode == MODE_SPLITK) grid = (int64_t)a.tiles_m * a.tiles_n * a.splits;
-    }
+    // tile counts in 64 bits, checked before they are narrowed: grouped
+    // launches size the grid for the worst case, one partial tile per expert
+    const int64_t tn = cdiv(a.N, d.bn);
+    const int64_t tm = cdiv(a.M, d.bm) + (mode == MODE_GROUPED ? a.E : 0);
+    if (tn > 0x7fffffff || tm > 0x7fffffff || tm * tn > 0x7fffffff) return MG_ERR_INVALID_ARG;
+    int64_t grid = tm * tn;
+    if (mode == MODE_SPLITK) grid *= a.splits;
+    else if (mode != MODE_GROUPED && a.batch > 1) grid *= a.batch;
     if (grid <= 0) return MG_OK;
     if (grid > 0x7fffffff) return MG_ERR_INVALID_ARG;
+    a.tiles_n = (int32_t)tn;
+    a.tiles_m = mode == MODE_GROUPED ? 0 : (int32_t)tm;
+    a.grid = (int32_t)grid;
     const int gm = g_group_m.load(), xr = g_xcd.load();
     a.group_m = gm > 0 ? gm : d.group_m;
     a.xcd_remap = xr >= 0 ? xr : d.xcd_remap;
@@ -213,13 +214,15 @@ mg_status gemm_f32(const void* A, const void* B, const void* bias, void* C, int6
     a.bias = (const uint16_t*)bias;
     a.M = M; a.N = N; a.K = K;
     a.lda = sam; a.ldb = sbk; a.ldc = scm;
-    a.tiles_m = (int32_t)cdiv(M, kF32TileM[tile]);
-    a.tiles_n = (int32_t)cdiv(N, kF32TileN[tile]);
+    const int64_t tm = cdiv(M, kF32TileM[tile]), tn = cdiv(N, kF32TileN[tile]);
+    if (tm > 0x7fffffff || tn > 0x7fffffff || tm * tn > 0x7fffffff) return MG_ERR_INVALID_ARG;
+    const int64_t grid = tm * tn;
+    a.tiles_m = (int32_t)tm;
+    a.tiles_n = (int32_t)tn;
+    a.grid = (int32_t)grid;
     a.group_m = kGroupM;
     a.xcd_remap = 1;
     a.batch = 1;
-    const int64_t grid = (int64_t)a.tiles_m * a.tiles_n;
-    if (grid > 0x7fffffff) return MG_ERR_INVALID_ARG;
     if (dry) return MG_OK;
     return launch_f32(tile, epi, a, grid, stream);
 }

@@ -10,9 +10,9 @@ using CfgF32S = F32Cfg<kF32TileM[1], kF32TileN[1], 2, 2, kF32SliceK, 6>;
 template <class Cfg>
 static void launch_cfg_f32(bool epi, const KArgs& a, int64_t grid, hipStream_t s) {
     if (epi)
-        hipLaunchKernelGGL((gemm_f32_kernel<Cfg, true>), dim3((unsigned)grid), dim3(Cfg::NT), 0, s, a);
+        hipLaunchKernelGGL((gemm_f32_kernel<Cfg, true>), tile_grid(grid, Cfg::NT), dim3(Cfg::NT), 0, s, a);
     else
-        hipLaunchKernelGGL((gemm_f32_kernel<Cfg, false>), dim3((unsigned)grid), dim3(Cfg::NT), 0, s, a);
+        hipLaunchKernelGGL((gemm_f32_kernel<Cfg, false>), tile_grid(grid, Cfg::NT), dim3(Cfg::NT), 0, s, a);
 }
 
 mg_status launch_f32(int tile, bool epi, const KArgs& a, int64_t grid, hipStream_t s) {

@@ -10,14 +10,14 @@ namespace mg {
 template <class C, int DT, bool EPI, int MODE>
 mg_status launch_cfg(const KArgs& a, int64_t grid, hipStream_t stream) {
     (void)hipGetLastError();  // clear a stale error so the check below is ours
-    hipLaunchKernelGGL((gemm_tile_kernel<C, DT, EPI, MODE>), dim3((unsigned)grid), dim3(C::NT), 0, stream, a);
+    hipLaunchKernelGGL((gemm_tile_kernel<C, DT, EPI, MODE>), tile_grid(grid, C::NT), dim3(C::NT), 0, stream, a);
     return hipGetLastError() == hipSuccess ? MG_OK : MG_ERR_HIP;
 }
 
 template <class F, int DT, bool EPI, int MODE, bool TA = false, bool TB = false, bool KT = false>
 mg_status launch_fast(const KArgs& a, int64_t grid, hipStream_t stream) {
     (void)hipGetLastError();
-    hipLaunchKernelGGL((gemm_dlds_kernel<F, DT, EPI, MODE, TA, TB, KT>), dim3((unsigned)grid), dim3(F::NT), 0, stream,
+    hipLaunchKernelGGL((gemm_dlds_kernel<F, DT, EPI, MODE, TA, TB, KT>), tile_grid(grid, F::NT), dim3(F::NT), 0, stream,
                        a);
     return hipGetLastError() == hipSuccess ? MG_OK : MG_ERR_HIP;
 }
@@ -41,7 +41,7 @@ mg_status launch_general(bool epi, int mode, const KArgs& a, int64_t grid, hipSt
 template <class F, int DT, bool EPI>
 mg_status launch_slab(const KArgs& a, int64_t grid, hipStream_t stream) {
     (void)hipGetLastError();
-    hipLaunchKernelGGL((gemm_kslab_kernel<F, DT, EPI>), dim3((unsigned)grid), dim3(F::NT), 0, stream, a);
+    hipLaunchKernelGGL((gemm_kslab_kernel<F, DT, EPI>), tile_grid(grid, F::NT), dim3(F::NT), 0, stream, a);
     return hipGetLastError() == hipSuccess ? MG_OK : MG_ERR_HIP;
 }
 

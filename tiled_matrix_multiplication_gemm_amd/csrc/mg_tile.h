@@ -56,8 +56,26 @@ struct KArgs {
     int32_t group_m;
     int32_t xcd_remap;
     int32_t dry;             // host only: 1 = validate the launch, enqueue nothing
+    int32_t grid;            // workgroups that hold tiles (grouped: an upper bound)
     ConvArgs conv;           // MODE_CONV only
 };
+
+// A dispatch counts at most 2^32 - 1 work-items in each grid dimension, so a
+// tile launch of more workgroups than that allows in x is laid out as rows
+// of tile_row(NT) workgroups (a multiple of 8, one per XCD) over gridDim.y.
+// Workgroup ids are linear, x fastest (the order the dispatcher hands them
+// out); the ids past the tile count in the last row return at once.  The
+// padded count stays below 2^32 since the host keeps the tile count below
+// 2^31.  The row width depends on the workgroup size alone, so the kernels
+// take it as a constant instead of reading the grid's shape.
+__host__ __device__ constexpr unsigned tile_row(int nt) { return (0xffffffffu / (unsigned)nt) & ~7u; }
+inline dim3 tile_grid(int64_t grid, int nt) {
+    const int64_t row = tile_row(nt);
+    if (grid <= row) return dim3((unsigned)grid);
+    return dim3((unsigned)row, (unsigned)((grid + row - 1) / row));
+}
+template <int NT>
+__device__ __forceinline__ unsigned tile_block() { return blockIdx.x + blockIdx.y * tile_row(NT); }
 
 // Grouped GEMM: which tile workgroup `logical` computes.  Tiles run expert by
 // expert; within an expert, column slab by column slab, with the expert's row
@@ -93,7 +111,7 @@ __device__ __forceinline__ int grouped_tiles_walk(const KArgs& args, Off off) {
     for (int e = 0; e < args.E; ++e) {
         int b = off(e + 1);
         b = b < a ? a : (b > T ? T : b);
-        total += (b - a + BM - 1) / BM;
+        total += (int)(((unsigned)(b - a) + (BM - 1u)) / BM);  // unsigned: b - a may reach 2^31 - 1
         a = b;
     }
     return total * args.tiles_n;
@@ -108,7 +126,7 @@ __device__ __forceinline__ bool grouped_tile_walk(const KArgs& args, Off off, in
     for (e = 0; e < args.E; ++e) {
         int b = off(e + 1);
         b = b < a ? a : (b > T ? T : b);
-        const int mt = (b - a + BM - 1) / BM;
+        const int mt = (int)(((unsigned)(b - a) + (BM - 1u)) / BM);
         const int cnt = mt * args.tiles_n;
         if (logical < base + cnt) {
             const int local = logical - base;
@@ -239,7 +257,10 @@ __device__ __forceinline__ void batch_entry(const KArgs& args, int& logical, con
 
 // Grouped tile order: GROUP_M tile rows at a time, column by column within
 // the group (the Gluon matmul example's program-id mapping).
+// group_m is clamped to tiles_m (one group either way), which keeps
+// group_m * tiles_n within the grid's tile count and so within 31 bits.
 __device__ __forceinline__ void grouped_order(int pid, int tiles_m, int tiles_n, int group_m, int& pm, int& pn) {
+    group_m = min(group_m, tiles_m);
     int per_group = group_m * tiles_n;
     int group = pid / per_group;
     int first = group * group_m;
@@ -263,14 +284,15 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_tile_kernel(const KArgs args) {
     const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
 
     // ---- which tile -------------------------------------------------------
-    int total = (int)gridDim.x;
+    const unsigned b = tile_block<NT>();
+    int total = args.grid;
     [[maybe_unused]] GroupOffsets go{0, false};
     if constexpr (MODE == MODE_GROUPED) {
         go = load_group_offsets(args);
         total = grouped_tiles<BM>(args, go);
-        if ((int)blockIdx.x >= total) return;
     }
-    int logical = args.xcd_remap ? xcd_logical(blockIdx.x, total) : (int)blockIdx.x;
+    if (b >= (unsigned)total) return;
+    int logical = args.xcd_remap ? xcd_logical((int)b, total) : (int)b;
     const uint16_t* Ag = args.A;
     const uint16_t* Bg = args.B;
     uint16_t* Cg = args.C;
