@@ -20,8 +20,11 @@
   written, and the result is the product over the partition the kernel
   clamps them to.
 * The largest token count the grouped entry point takes (T = 2^31 - 1),
-  with one expert holding all but 100 of them: the device-side count of
-  that expert's row tiles must not overflow 32 bits.
+  with one expert holding all but 100 of them, and a dense output of
+  2^31 - 1 rows on a fast and a general row: the device-side count of an
+  expert's row tiles must not overflow 32 bits, and launches of more
+  workgroups than one grid dimension holds must run every tile (checked
+  on every output row).
 """
 import numpy as np
 import pytest
@@ -228,39 +231,104 @@ def test_grouped_offsets_out_of_order_stay_inside_the_buffers(orc, E):
     assert_bitexact(got[lo:hi], ref_q, F16, "clamped partition")
 
 
-def test_grouped_largest_token_count(orc):
-    """T = 2^31 - 1 tokens (K = N = 8): expert 0 takes rows 0..99, expert 1
-    the other 2^31 - 101.  X repeats a seeded block of P = 65521 rows (a
-    prime, so a row offset error lands on a different block row), copied on
-    the device; the oracle reads the same block on the host, so none of its
-    inputs comes back from the device.  Checked bit-exact against the
-    oracle: 4096 sampled rows, the rows around the expert boundary and the
-    last 300 rows (Y starts as the canary, so a tile that is never run
-    shows up)."""
+P_BLOCK = 65521  # rows of the repeated input block: a prime, so a row offset error lands on another block row
+
+
+def periodic_rows(P, K, seed):
+    """A seeded P x K block of small integers, and a device matrix of T rows
+    whose row r is block row r % P (filled by copies on the device)."""
+    rng = np.random.default_rng(seed)
+    return rng, inputs.to_bits(rng.integers(-4, 5, size=(P, K)).astype(np.float64), F16)
+
+
+def fill_periodic(X, blk):
     import torch
 
-    T, K, N, P = 2 ** 31 - 1, 8, 8, 65521
-    rng = np.random.default_rng(9600)
-    blk = inputs.to_bits(rng.integers(-4, 5, size=(P, K)).astype(np.float64), F16)
+    T, K = X.shape
+    P = blk.shape[0]
+    q = T // P
+    d = to_dev(blk, F16)
+    X[: q * P].view(q, P, K).copy_(d.unsqueeze(0).expand(q, P, K))
+    X[q * P:].copy_(d[: T - q * P])
+
+
+def assert_periodic_output(Y, r0, r1, E, label, chunk=1 << 26):
+    """Every row r in [r0, r1) of the device matrix Y must equal row r % P
+    of E (the oracle's product of the repeated block; fp16 bit patterns).
+    The comparison runs on the device, chunk by chunk, against E repeated."""
+    import torch
+
+    P, N = E.shape
+    Ed = torch.from_numpy(np.ascontiguousarray(E).view(np.int16)).cuda()
+    big = Ed.repeat((chunk + P - 1) // P + 1, 1)
+    Yi = Y.view(torch.int16)
+    for a in range(r0, r1, chunk):
+        b = min(a + chunk, r1)
+        ph = a % P
+        got = Yi[a:b]
+        want = big[ph: ph + (b - a)]
+        if not torch.equal(got, want):
+            bad = (got != want).any(dim=1).nonzero()
+            first = a + int(bad[0])
+            raise AssertionError("%s: %d rows differ in rows %d..%d, first %d (got %s, want %s)" % (
+                label, int(bad.numel()), a, b, first, to_host(Yi[first]).tolist(),
+                E[first % P].tolist()))
+
+
+@pytest.mark.parametrize("row", [2, 5])
+def test_dense_output_rows_past_2_31(orc, row):
+    """M = 2^31 - 1 rows, N = K = 8, forced onto the 64 x 64 direct-to-LDS
+    row (33.5 million workgroups) and the general kernel's 128 x 128 row
+    (16.8 million): both launches pass the 2^32 work-items one grid
+    dimension holds, so they run as several rows of workgroups.  A repeats
+    a seeded block of P rows, so C repeats the oracle's product of that
+    block; every row of C is compared with it (C starts as the canary, so a
+    tile that never runs shows up)."""
+    import torch
+
+    M, N, K, P = 2 ** 31 - 1, 8, 8, P_BLOCK
+    rng, blk = periodic_rows(P, K, 9700 + row)
+    B = inputs.to_bits(rng.integers(-4, 5, size=(K, N)).astype(np.float64), F16)
+    announce("dense M = 2^31 - 1, N = K = 8 on row %d" % row)
+    A = torch.empty((M, K), dtype=torch.float16, device="cuda")
+    fill_periodic(A, blk)
+    C = torch.full((M, N), CANARY, dtype=torch.int16, device="cuda").view(torch.float16)
+    mg.mg_set_config(row)
+    try:
+        mg.mg_gemm(A, to_dev(B, F16), out=C)
+        torch.cuda.synchronize()
+    finally:
+        mg.mg_set_config(-1)
+    assert mg.mg_last_config() == row
+    del A
+    _, E = orc.gemm(blk, B, F16)
+    assert_periodic_output(C, 0, M, E, "row %d" % row)
+    del C
+    torch.cuda.empty_cache()
+
+
+def test_grouped_largest_token_count(orc):
+    """T = 2^31 - 1 tokens (K = N = 8): expert 0 takes rows 0..99, expert 1
+    the other 2^31 - 101 (8.4 million workgroups: a launch past 2^32
+    work-items).  X repeats a seeded block of P rows, copied on the device;
+    the oracle multiplies the same block on the host, so none of its inputs
+    comes back from the device, and every row of Y is compared with the
+    oracle's product for its expert (Y starts as the canary)."""
+    import torch
+
+    T, K, N, P = 2 ** 31 - 1, 8, 8, P_BLOCK
+    rng, blk = periodic_rows(P, K, 9600)
     W = inputs.to_bits(rng.integers(-4, 5, size=(2, K, N)).astype(np.float64), F16)
     off = np.array([0, 100, T], dtype=np.int64)
     announce("grouped T = 2^31 - 1, K = N = 8, experts of 100 and 2^31 - 101 rows")
     X = torch.empty((T, K), dtype=torch.float16, device="cuda")
-    q = T // P
-    blk_d = to_dev(blk, F16)
-    X[: q * P].view(q, P, K).copy_(blk_d.unsqueeze(0).expand(q, P, K))
-    X[q * P:].copy_(blk_d[: T - q * P])
-    del blk_d
+    fill_periodic(X, blk)
     Y = torch.full((T, N), CANARY, dtype=torch.int16, device="cuda").view(torch.float16)
     mg.mg_grouped_gemm(X, to_dev(W, F16), torch.from_numpy(off.astype(np.int32)).cuda(), out=Y)
     torch.cuda.synchronize()
     del X
-    rows = np.unique(np.concatenate([rng.integers(0, T, size=4096), np.arange(0, 3), np.arange(97, 103),
-                                     np.arange(T - 300, T)]))
-    got = to_host(Y[torch.from_numpy(rows).cuda()])
+    for e in range(2):
+        _, E = orc.gemm(blk, W[e], F16)
+        assert_periodic_output(Y, int(off[e]), int(off[e + 1]), E, "expert %d" % e)
     del Y
     torch.cuda.empty_cache()
-    for e in range(2):
-        sel = (rows >= off[e]) & (rows < off[e + 1])
-        _, ref_q = orc.gemm(blk[rows[sel] % P], W[e], F16)
-        assert_bitexact(got[sel], ref_q, F16, "expert %d" % e)

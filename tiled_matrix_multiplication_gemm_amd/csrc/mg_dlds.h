@@ -278,15 +278,15 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_dlds_kernel(const KArgs args) {
     const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
 
     // ---- which tile (same order as the general kernel) --------------------
-    const unsigned b = tile_block<Cfg::NT>();
+    const unsigned wg = tile_block<Cfg::NT>();
     int total = args.grid;
     [[maybe_unused]] GroupOffsets go{0, false};
     if constexpr (MODE == MODE_GROUPED) {
         go = load_group_offsets(args);
         total = grouped_tiles<BM>(args, go);
     }
-    if (b >= (unsigned)total) return;
-    int logical = args.xcd_remap ? xcd_logical((int)b, total) : (int)b;
+    if (wg >= (unsigned)total) return;
+    int logical = args.xcd_remap ? xcd_logical((int)wg, total) : (int)wg;
     const uint16_t* Ag = args.A;
     const uint16_t* Bg = args.B;
     uint16_t* Cg = args.C;

@@ -71,9 +71,9 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_f32_kernel(const KArgs args) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
 
-    const unsigned b = tile_block<Cfg::NT>();
-    if (b >= (unsigned)args.grid) return;
-    int logical = args.xcd_remap ? xcd_logical((int)b, args.grid) : (int)b;
+    const unsigned wg = tile_block<Cfg::NT>();
+    if (wg >= (unsigned)args.grid) return;
+    int logical = args.xcd_remap ? xcd_logical((int)wg, args.grid) : (int)wg;
     const float* Ag = (const float*)args.A;
     const float* Bg = (const float*)args.B;
     float* Cg = (float*)args.C;

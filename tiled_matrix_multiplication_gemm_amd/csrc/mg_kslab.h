@@ -72,9 +72,9 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_kslab_kernel(const KArgs args) {
     const int lane = tid & 63;
     const int wave = tid >> 6;
 
-    const unsigned b = tile_block<Cfg::NT>();
-    if (b >= (unsigned)args.grid) return;
-    int logical = args.xcd_remap ? xcd_logical((int)b, args.grid) : (int)b;
+    const unsigned wg = tile_block<Cfg::NT>();
+    if (wg >= (unsigned)args.grid) return;
+    int logical = args.xcd_remap ? xcd_logical((int)wg, args.grid) : (int)wg;
     const uint16_t* Ag = args.A;
     const uint16_t* Bg = args.B;
     uint16_t* Cg = args.C;
