@@ -386,6 +386,9 @@ mg_status launch_im2col(const mg_conv2d_shape* s, const ConvGeom& g, const void*
     int64_t rows = 2048 / per_row;
     rows = rows < 1 ? 1 : (rows > kIm2colMaxRows ? kIm2colMaxRows : rows);
     a.rows_per_block = (int32_t)rows;
+    // one grid dimension holds at most 2^32 - 1 work-items (reached only by
+    // column buffers of several hundred GiB)
+    if (cdiv(g.M, rows) * kIm2colThreads > 0xffffffffLL) return MG_ERR_INVALID_ARG;
     const dim3 grid((unsigned)cdiv(g.M, rows), tap ? (unsigned)g.taps : 1u);
     (void)hipGetLastError();
     if (tap) {

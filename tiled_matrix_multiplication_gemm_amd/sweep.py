@@ -19,8 +19,10 @@ grouped (MoE) problems, batched attention-score products -- forcing each row
 through mg_set_config and visiting
 the rows round-robin so that clock drift does not favour the rows measured
 last; it also times split-K counts on the under-filled shapes, the prepacked
-A against the row-major A, and a plain copy (HBM rate).  Raw times go to a
-JSON file.
+A against the row-major A, and a plain copy (HBM rate).  Each time is a
+batch of back-to-back calls captured in a HIP graph and replayed, so the
+host's cost per call does not hide the kernels' differences on small
+shapes.  Raw times go to a JSON file.
 
 `fit` (CPU) fits the time model of select_config() to those times -- per row
 t = rounds * (BM * BN * K * c / rate_row + f), rounds = ceil(tiles / 256),
@@ -88,8 +90,11 @@ SPLITS = [1, 2, 4, 8, 16]
 
 # ---- GPU side -------------------------------------------------------------------
 def _time(fn, target_ms=4.0, rounds=1):
-    """Median per-call ms over `rounds` batches of back-to-back calls (HIP
-    events around each batch, so launch gaps are those of a stream of calls)."""
+    """Median per-call ms over `rounds` replays of a HIP graph that holds a
+    batch of back-to-back calls (HIP events around each replay).  The graph
+    keeps the host's cost per call, which at small sizes is larger than the
+    kernel, out of the comparison between rows; every timed call writes into
+    buffers allocated beforehand, so the captured calls allocate nothing."""
     import torch
 
     fn()
@@ -101,14 +106,26 @@ def _time(fn, target_ms=4.0, rounds=1):
     torch.cuda.synchronize()
     one = max(s.elapsed_time(e), 1e-3)
     reps = int(min(200, max(3, target_ms / one)))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()  # a call on the capture stream before capturing
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
     out = []
     for _ in range(rounds):
         s.record()
-        for _ in range(reps):
-            fn()
+        g.replay()
         e.record()
         torch.cuda.synchronize()
         out.append(s.elapsed_time(e) / reps)
+    del g
     return statistics.median(out)
 
 
