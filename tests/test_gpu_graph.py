@@ -1,5 +1,9 @@
 """The entry points under HIP graph capture (torch.cuda.graph on the caller's
-stream): every replay must give the eager result bit for bit.
+stream): every replay must give the eager result bit for bit.  Covered:
+the plain, bias+ReLU, grouped, batched (with a broadcast operand) and fp32
+GEMMs, the attention scores, both forms of the convolution (implicit GEMM,
+and im2col into a caller's workspace followed by the GEMM) and the
+allocation-free split-K.
 
 The library makes no allocation and no memset on the stream, so a captured
 call is just its kernels.  The allocation-free split-K exists for callers
@@ -100,3 +104,34 @@ def test_splitk_noalloc_in_a_graph(M, N, K, splits):
     torch.cuda.synchronize()
     replay_and_check([lambda: mg.mg_gemm_splitk_noalloc(A, B, splits=splits, out=C)], [C])
     assert torch.equal(C, ref), "the graph's result differs from the workspace form"
+
+
+def test_batched_attention_conv_and_fp32_in_one_graph():
+    import torch
+
+    announce("graph: batched (broadcast B), attention scores, conv implicit + im2col, fp32 gemm")
+    g = torch.Generator(device="cuda").manual_seed(8300)
+    def rnd(*shape, dtype=torch.float16, scale=0.1):
+        return (torch.randn(*shape, device="cuda", generator=g) * scale).to(dtype)
+    a3 = rnd(6, 300, 136, dtype=torch.bfloat16)
+    b3 = rnd(1, 136, 264, dtype=torch.bfloat16).expand(6, 136, 264)  # one B for every entry (stride 0)
+    c3 = torch.empty((6, 300, 264), dtype=torch.bfloat16, device="cuda")
+    q = rnd(8, 384, 64)
+    k = rnd(8, 320, 64)
+    s = torch.empty((8, 384, 320), dtype=torch.float16, device="cuda")
+    x1, w1 = rnd(2, 17, 15, 64), rnd(3, 3, 64, 64)      # C % 32 == 0: implicit GEMM, no workspace
+    y1 = torch.empty((2, 17, 15, 64), dtype=torch.float16, device="cuda")
+    x2, w2 = rnd(2, 13, 11, 40), rnd(3, 3, 40, 48)      # C = 40: im2col into the workspace, then the GEMM
+    y2 = torch.empty((2, 13, 11, 48), dtype=torch.float16, device="cuda")
+    shape2 = mg.conv2d_shape(x2.shape, (3, 3), 48, 1, 1, 1)
+    need = mg.mg_conv2d_workspace_bytes(shape2, mg.MG_F16)
+    assert need > 0, "the C = 40 case should take the im2col path"
+    ws = torch.empty((need,), dtype=torch.uint8, device="cuda")
+    assert mg.mg_conv2d_workspace_bytes(mg.conv2d_shape(x1.shape, (3, 3), 64, 1, 1, 1), mg.MG_F16) == 0
+    af, bf = rnd(200, 96, dtype=torch.float32, scale=1.0), rnd(96, 132, dtype=torch.float32, scale=1.0)
+    cf = torch.empty((200, 132), dtype=torch.float32, device="cuda")
+    replay_and_check([lambda: mg.mg_gemm_batched(a3, b3, out=c3),
+                      lambda: mg.mg_attention_scores(q, k, out=s),
+                      lambda: mg.mg_conv2d(x1, w1, 1, 1, 1, out=y1),
+                      lambda: mg.mg_conv2d(x2, w2, 1, 1, 1, workspace=ws, out=y2),
+                      lambda: mg.mg_gemm(af, bf, out=cf)], [c3, s, y1, y2, cf])
