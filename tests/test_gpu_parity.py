@@ -94,8 +94,8 @@ SMALL = [(1, 1, 1), (7, 33, 129), (33, 7, 1000), (129, 129, 33), (65, 200, 72),
          (300, 257, 130), (1000, 7, 33), (256, 384, 200), (513, 129, 257),
          (64, 64, 64), (1, 8, 64), (65, 200, 128), (129, 136, 64), (300, 264, 192), (513, 520, 256),
          (70, 72, 32), (96, 40, 96)]
-NUM_CONFIGS = 9
-DIRECT_ROWS = [0, 1, 2, 3, 4, 6, 8]  # rows with the pipelined direct-to-LDS kernel
+NUM_CONFIGS = 10
+DIRECT_ROWS = [0, 1, 2, 3, 4, 6, 8, 9]  # rows with the pipelined direct-to-LDS kernel
 
 
 def test_config_count_matches_library():

@@ -36,7 +36,7 @@ const mg_config_desc kTable[kNumConfigs] = {
     describe<Cfg2, Fast2>(2, "t64x64_w2x2"),   describe<Cfg3, Fast3>(3, "t128x256_w2x2"),
     describe<Cfg4, Fast4>(4, "t256x128_w4x2_2cu"), describe<Cfg5, void>(5, "t128x128k32_w2x2"),
     describe<Cfg6, Fast6>(6, "t256x256_w2x2_k32r5"), describe<Cfg7, Fast7>(7, "t64x64_ksplit4"),
-    describe<Cfg8, Fast8>(8, "t256x64_w4x2"),
+    describe<Cfg8, Fast8>(8, "t256x64_w4x2"),  describe<Cfg9, Fast9>(9, "t256x64_w4x1_2cu"),
 };
 
 std::atomic<int> g_forced{-1};
@@ -171,6 +171,7 @@ mg_status launch(int cfg, int dt, bool epi, int mode, KArgs& a, hipStream_t s, i
         case 6: st = launch_row6(dt, epi, mode, ta, tb, a, grid, s); break;
         case 7: st = launch_row7(dt, epi, mode, ta, tb, a, grid, s); break;
         case 8: st = launch_row8(dt, epi, mode, ta, tb, a, grid, s); break;
+        case 9: st = launch_row9(dt, epi, mode, ta, tb, a, grid, s); break;
         default: return MG_ERR_BAD_CONFIG;
     }
     if (st == MG_OK && !a.dry) g_last.store(cfg);
@@ -481,7 +482,7 @@ int64_t mg_prepack_uses_to_pay(int64_t M, int64_t N, int64_t K, mg_dtype dtype) 
     (void)dtype;
     if (M <= 0 || N <= 0 || K <= 0) return -1;
     const int cfg = select_config(M, N, K, 0);
-    if (cfg < 0 || cfg >= kNumConfigs) return -1;
+    if (cfg < 0 || cfg >= kNumConfigs || cfg >= (int)(sizeof(rates::kPackedRatio) / sizeof(double))) return -1;
     const double ratio = rates::kPackedRatio[cfg];
     if (ratio <= 0.0 || ratio >= 1.0) return -1;
     double t_plain = -1.0;
