@@ -535,7 +535,7 @@ def main():
         return
     args = parse()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
+        print("bench.py runs on one GPU only: the library has no multi-GPU path (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
     import torch
 
