@@ -75,7 +75,11 @@ def pmc_probe(name):
 
     from tiled_matrix_multiplication_gemm_amd import inputs
 
-    if name in inputs.GROUPED_WORKLOADS:
+    if name == CONV_NAME:
+        fn = conv_setup()[0]
+    elif name == ATTN_NAME:
+        fn = attention_setup()[0]
+    elif name in inputs.GROUPED_WORKLOADS:
         c, fn = grouped_setup(name)
     else:
         c, fn = dense_setup(name)
@@ -305,6 +309,46 @@ def cpu_baseline(case, target_s: float):
                                                                                        case.K, dt)}
 
 
+CONV_NAME = "conv3x3_n32_56x56_c64_k64_f16"
+ATTN_NAME = "attention_scores_h128_l2048_d128_bf16"
+
+
+def conv_setup():
+    """The 3x3 convolution workload (implicit GEMM) on the device: the call,
+    its flops, its compulsory HBM bytes (input, weights and output once) and
+    the workspace its configuration needs."""
+    import torch
+
+    import tiled_matrix_multiplication_gemm_amd as mg
+    from tiled_matrix_multiplication_gemm_amd import inputs
+
+    w = inputs.CONV_WORKLOAD
+    cc = inputs.conv_case(w["Nb"], w["H"], w["W"], w["C"], w["OC"], w["KH"], w["KW"], w["dtype"], w["seed_float"],
+                          w["stride"], w["pad"], w["dil"])
+    x, wt = upload(cc.x, cc.dtype), upload(cc.w, cc.dtype)
+    y = torch.empty((w["Nb"], w["H"], w["W"], w["OC"]), dtype=x.dtype, device="cuda")
+    M, K = w["Nb"] * w["H"] * w["W"], w["KH"] * w["KW"] * w["C"]
+    ws = mg.mg_conv2d_workspace_bytes(mg.conv2d_shape(x.shape, 3, w["OC"], 1, 1, 1), cc.dtype)
+    return (lambda: mg.mg_conv2d(x, wt, w["stride"], w["pad"], w["dil"], out=y), 2.0 * M * K * w["OC"],
+            2.0 * (x.numel() + wt.numel() + y.numel()), ws)
+
+
+def attention_setup():
+    """The attention-score workload (Q K^T for every head) on the device: the
+    call, its flops and its compulsory HBM bytes."""
+    import torch
+
+    import tiled_matrix_multiplication_gemm_amd as mg
+    from tiled_matrix_multiplication_gemm_amd import inputs
+
+    a = inputs.ATTENTION_WORKLOAD
+    ac = inputs.attention_case(a["heads"], a["L"], a["L"], a["d"], a["dtype"], a["seed_float"])
+    q, k = upload(ac.Q, ac.dtype), upload(ac.K, ac.dtype)
+    S = torch.empty((a["heads"], a["L"], a["L"]), dtype=q.dtype, device="cuda")
+    return (lambda: mg.mg_attention_scores(q, k, out=S), 2.0 * a["heads"] * a["L"] * a["L"] * a["d"],
+            2.0 * (q.numel() + k.numel() + S.numel()), 0)
+
+
 def measure_consumers(steps, warmup):
     """fp32 GEMM, convolution and attention-score workloads: kernel time from
     HIP events, TFLOP/s, and compulsory HBM bytes per second."""
@@ -327,38 +371,26 @@ def measure_consumers(steps, warmup):
                             "kernel_ms_mean": round(mean_ms, 5)}
     del A, B, C
     # 3x3 convolution, implicit GEMM
-    w = inputs.CONV_WORKLOAD
-    cc = inputs.conv_case(w["Nb"], w["H"], w["W"], w["C"], w["OC"], w["KH"], w["KW"], w["dtype"], w["seed_float"],
-                          w["stride"], w["pad"], w["dil"])
-    x, wt = upload(cc.x, cc.dtype), upload(cc.w, cc.dtype)
-    y = torch.empty((w["Nb"], w["H"], w["W"], w["OC"]), dtype=x.dtype, device="cuda")
-    fn = lambda: mg.mg_conv2d(x, wt, w["stride"], w["pad"], w["dil"], out=y)
+    fn, fl, byts, cfg_ws = conv_setup()
     wall, mean_ms, _ = time_calls(fn, steps, warmup)
-    M, K = w["Nb"] * w["H"] * w["W"], w["KH"] * w["KW"] * w["C"]
-    fl = 2.0 * M * K * w["OC"]
-    byts = 2.0 * (x.numel() + wt.numel() + y.numel())
     ach = fl / (mean_ms * 1e-3) / 1e12
     gbs = byts / (mean_ms * 1e-3) / 1e9
-    out["conv3x3_n32_56x56_c64_k64_f16"] = {
+    out[CONV_NAME] = {
         "kernel_tflops": round(ach, 2), "frac_mfma_peak": round(ach / PEAK_MFMA_TFLOPS, 4),
         "hbm_gbs_compulsory": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
         "kernel_ms_mean": round(mean_ms, 5), "tile_config": mg.mg_config_info(mg.mg_last_config())["name"],
-        "workspace_bytes": mg.mg_conv2d_workspace_bytes(mg.conv2d_shape(x.shape, 3, w["OC"], 1, 1, 1), cc.dtype)}
-    del x, wt, y
+        "workspace_bytes": cfg_ws, "compulsory_bytes": byts, "traffic": stored_traffic(CONV_NAME)}
+    del fn
     # attention scores
-    a = inputs.ATTENTION_WORKLOAD
-    ac = inputs.attention_case(a["heads"], a["L"], a["L"], a["d"], a["dtype"], a["seed_float"])
-    q, k = upload(ac.Q, ac.dtype), upload(ac.K, ac.dtype)
-    S = torch.empty((a["heads"], a["L"], a["L"]), dtype=q.dtype, device="cuda")
-    wall, mean_ms, _ = time_calls(lambda: mg.mg_attention_scores(q, k, out=S), steps, warmup)
-    fl = 2.0 * a["heads"] * a["L"] * a["L"] * a["d"]
-    byts = 2.0 * (q.numel() + k.numel() + S.numel())
+    fn, fl, byts, _ = attention_setup()
+    wall, mean_ms, _ = time_calls(fn, steps, warmup)
     ach = fl / (mean_ms * 1e-3) / 1e12
     gbs = byts / (mean_ms * 1e-3) / 1e9
-    out["attention_scores_h128_l2048_d128_bf16"] = {
+    out[ATTN_NAME] = {
         "kernel_tflops": round(ach, 2), "frac_mfma_peak": round(ach / PEAK_MFMA_TFLOPS, 4),
         "hbm_gbs_compulsory": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
-        "kernel_ms_mean": round(mean_ms, 5), "tile_config": mg.mg_config_info(mg.mg_last_config())["name"]}
+        "kernel_ms_mean": round(mean_ms, 5), "tile_config": mg.mg_config_info(mg.mg_last_config())["name"],
+        "compulsory_bytes": byts, "traffic": stored_traffic(ATTN_NAME)}
     return out
 
 
