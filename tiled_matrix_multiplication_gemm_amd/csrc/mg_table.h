@@ -35,7 +35,11 @@ using Cfg6 = TileCfg<256, 256, 64, 2, 4>;  // general fallback keeps eight waves
 // three steps ahead (1024 x 1024 x 2048: 0.0089 -> 0.0085 ms)
 using Fast0 = DldsCfg<256, 256, 2, 4, 32, 5>;
 using Fast1 = DldsCfg<128, 128, 2, 2, 64, 3, 3>;
-using Fast2 = DldsCfg<64, 64, 2, 2, 64, 6, 3>;
+// a ring of 5 at 80 KB, so that two workgroups share a CU wherever there are
+// more tiles than CUs (one more slot bought nothing, and cost the second
+// workgroup: 1000^3 0.0124 -> 0.0105 ms, a 14 x 14 x 256 convolution layer
+// 0.0203 -> 0.0146 ms, 1024 x 1024 x 2048 unchanged)
+using Fast2 = DldsCfg<64, 64, 2, 2, 64, 5, 3>;
 using Fast3 = DldsCfg<128, 256, 2, 2, 32, 4>;
 // two workgroups per CU (eight waves of 64 x 64, 118-122 registers, a ring of
 // 3 at 72 KB): one workgroup's epilogue runs beside the other's K loop, which
