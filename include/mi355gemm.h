@@ -149,8 +149,10 @@ mg_status mg_gemm_batched(const void* A, const void* B, void* C, int64_t batch,
  * a workspace that is null or too small is MG_ERR_INVALID_ARG.
  */
 size_t mg_splitk_workspace_bytes(int64_t M, int64_t N, int64_t splits);
-/* A split count for mg_gemm_splitk() from a time model of this library on
- * MI355X (1 means: use mg_gemm()).  Host only; no HIP call. */
+/* A split count for mg_gemm_splitk() (1 means: use mg_gemm()): for a shape
+ * the offline sweep timed, the count that measured fastest on MI355X;
+ * otherwise the count of least time in the library's time model.  Host
+ * only; no HIP call. */
 int64_t mg_splitk_choose(int64_t M, int64_t N, int64_t K);
 mg_status mg_gemm_splitk(const void* A, const void* B, void* C, void* workspace, size_t workspace_bytes,
                          int64_t splits, int64_t M, int64_t N, int64_t K,

@@ -32,8 +32,8 @@ constexpr mg_config_desc describe(int id, const char* name) {
 }
 
 const mg_config_desc kTable[kNumConfigs] = {
-    describe<Cfg0, Fast0>(0, "t256x256_w2x4_k32r5"), describe<Cfg1, Fast1>(1, "t128x128_w2x2"),
-    describe<Cfg2, Fast2>(2, "t64x64_w2x2"),   describe<Cfg3, Fast3>(3, "t128x256_w2x2"),
+    describe<Cfg0, Fast0>(0, "t256x256_w2x4_k32r5"), describe<Cfg1, Fast1>(1, "t128x128_w2x2_2cu"),
+    describe<Cfg2, Fast2>(2, "t64x64_w2x2_2cu"),   describe<Cfg3, Fast3>(3, "t128x256_w2x2"),
     describe<Cfg4, Fast4>(4, "t256x128_w4x2_2cu"), describe<Cfg5, void>(5, "t128x128k32_w2x2"),
     describe<Cfg6, Fast6>(6, "t256x256_w2x2_k32r5"), describe<Cfg7, Fast7>(7, "t64x64_ksplit4"),
     describe<Cfg8, Fast8>(8, "t256x64_w4x2"),  describe<Cfg9, Fast9>(9, "t256x64_w4x1_2cu"),
@@ -60,8 +60,10 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // each (the host does not read the device offsets); a batched product counts
 // the tiles of every entry.
 double model_seconds(const rates::RowRate& r, int64_t tiles, int64_t K) {
-    return (double)cdiv(tiles, 256) * ((double)r.bm * r.bn * (double)K * rates::kSecPerElemK / r.rate +
-                                       rates::kFixedSec);
+    // each CU works through ceil(tiles / 256) tiles; a row holding `occ`
+    // workgroups per CU pays the fixed time once per `occ` of them
+    return (double)cdiv(tiles, 256) * (double)r.bm * r.bn * (double)K * rates::kSecPerElemK / r.rate +
+           (double)cdiv(tiles, 256 * (int64_t)r.occ) * rates::kFixedSec;
 }
 
 int64_t tiles_of(const rates::RowRate& r, int64_t M, int64_t N, int64_t experts, int64_t batch) {
@@ -453,10 +455,13 @@ mg_status mg_gemm_batched(const void* A, const void* B, void* C, int64_t batch, 
 }
 
 int64_t mg_splitk_choose(int64_t M, int64_t N, int64_t K) {
-    // the split count of least modelled time (mg_rates.h: the rows' fitted
-    // tile times and the measured rate of writing and reading the fp32
+    // a shape the sweep timed split takes its measured best count; others
+    // the count of least modelled time (mg_rates.h: the rows' fitted tile
+    // times and the measured rate of writing and reading the fp32
     // partials); a split must win by 5 %, and runs keep at least 256 of K
     if (M <= 0 || N <= 0 || K <= 0) return 1;
+    for (const rates::SweptSplit& sw : rates::kSweptSplit)
+        if (sw.M == M && sw.N == N && sw.K == K) return sw.splits;
     int64_t best_s = 1;
     double best_t = 0.0;
     for (int64_t s = 1; s <= 64; s *= 2) {

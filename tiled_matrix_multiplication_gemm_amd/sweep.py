@@ -25,15 +25,18 @@ host's cost per call does not hide the kernels' differences on small
 shapes.  Raw times go to a JSON file.
 
 `fit` (CPU) fits the time model of select_config() to those times -- per row
-t = rounds * (BM * BN * K * c / rate_row + f), rounds = ceil(tiles / 256),
-one tile per CU at a time -- and writes csrc/mg_rates.h: the fitted per-row
+t = ceil(tiles / 256) * BM * BN * K * c / rate_row + ceil(tiles / (256 occ)) * f,
+where occ is the number of the row's workgroups one CU holds (its LDS ring
+in half the CU's LDS: two), whose K loops hide each other's fill and
+epilogue -- and writes csrc/mg_rates.h: the fitted per-row
 rates, c and f, the copy rate, the prepacked/plain time ratio per row, and
 the measured best row of every swept shape (grouped shapes keyed by their
 expert count, batched ones by their entry count), which select_config()
 returns for that exact shape (the cache of the pages' top-1) before it
-consults the model.  The model counts one tile per CU at a time; rows that
-run two workgroups per CU win where it cannot see it (epilogue-bound
-batched products) and are picked there through the cache.  The fit and the
+consults the model, and likewise the measured best split count of every
+shape timed split, which mg_splitk_choose() returns before its model.  Where the model still misjudges a row (the
+epilogue-bound batched products, whose two-workgroup row gains more than
+the hidden fixed time), the cache picks the measured best.  The fit and the
 generated header are both functions of the JSON alone; `check` regenerates
 the header and compares it with the committed one.
 
@@ -522,6 +525,16 @@ def _cdiv(a, b):
     return -(-a // b)
 
 
+LDS_PER_CU = 160 * 1024
+
+
+def _occupancy(data, r):
+    """Workgroups of row r that one CU runs at once: as many of its LDS rings
+    as fit in the CU's 160 KB, at most two (the waves of every row fit the
+    registers of two workgroups)."""
+    return max(1, min(2, LDS_PER_CU // int(data["rows"][str(r)]["direct_lds_bytes"])))
+
+
 def _model_rows(data):
     """Rows the model chooses among: those with a pipelined direct-to-LDS kernel."""
     out = []
@@ -540,37 +553,41 @@ def grouped_tiles(T, E, N, bm, bn):
 
 def fit(data):
     """Per-row relative rates, the seconds per output element and k of a
-    256 x 256 tile (c) and the fixed time per tile (f), fitted to the dense
-    times by alternating least squares on relative error."""
+    256 x 256 tile (c) and the fixed time per round of tiles (f), fitted to
+    the dense times by alternating least squares on relative error.  Each CU
+    works through ceil(tiles / CUs) tiles; a row that holds two workgroups
+    per CU pays the fixed time (ring fill, epilogue) once per two of them,
+    since the other workgroup's K loop runs beside it."""
     rows = _model_rows(data)
-    obs = []  # (row, bm, bn, rounds, K, seconds)
+    obs = []  # (row, bm, bn, tiles per CU, rounds, K, seconds)
     for rec in data["dense"]:
         for (r, bm, bn) in rows:
             t = rec["ms"].get(str(r))
             if t is None:
                 continue
             tiles = _cdiv(rec["M"], bm) * _cdiv(rec["N"], bn)
-            obs.append((r, bm, bn, _cdiv(tiles, data["cus"]), rec["K"], float(t) * 1e-3))
+            obs.append((r, bm, bn, _cdiv(tiles, data["cus"]), _cdiv(tiles, data["cus"] * _occupancy(data, r)),
+                        rec["K"], float(t) * 1e-3))
     rate = {r: 1.0 for (r, _, _) in rows}
     c, f = 0.205e-3 / (65536.0 * 8192.0), 3e-6
     for _ in range(50):
-        # c, f by weighted linear least squares on t / rounds = x c + f, weights 1 / t
-        sxx = sx = s1 = sxy = sy = 0.0
-        for (r, bm, bn, rnd, K, t) in obs:
-            x = bm * bn * K / rate[r]
-            y = t / rnd
-            w = 1.0 / (y * y)
-            sxx += w * x * x
-            sx += w * x
-            s1 += w
-            sxy += w * x * y
-            sy += w * y
-        det = sxx * s1 - sx * sx
-        c = (sxy * s1 - sx * sy) / det
-        f = max(0.0, (sxx * sy - sx * sxy) / det)
+        # c, f by weighted linear least squares on t = a c + b f (a: work, b: rounds), weights 1 / t^2
+        saa = sab = sbb = sat = sbt = 0.0
+        for (r, bm, bn, per_cu, rnd, K, t) in obs:
+            a = per_cu * bm * bn * K / rate[r]
+            w = 1.0 / (t * t)
+            saa += w * a * a
+            sab += w * a * rnd
+            sbb += w * rnd * rnd
+            sat += w * a * t
+            sbt += w * rnd * t
+        det = saa * sbb - sab * sab
+        c = (sat * sbb - sab * sbt) / det
+        f = max(0.0, (saa * sbt - sab * sat) / det)
         # rates: median over shapes of the implied rate (row 0 fixed at 1)
         for (r, _, _) in rows:
-            imp = [bm * bn * K * c / max(t / rnd - f, 1e-9) for (rr, bm, bn, rnd, K, t) in obs if rr == r]
+            imp = [per_cu * bm * bn * K * c / max(t - rnd * f, 1e-9)
+                   for (rr, bm, bn, per_cu, rnd, K, t) in obs if rr == r]
             rate[r] = statistics.median(imp) if imp else 1.0
         base = rate[rows[0][0]]
         for r in rate:
@@ -578,15 +595,18 @@ def fit(data):
     return {"rate": {str(r): round(rate[r], 4) for r in rate}, "c": c, "f": f}
 
 
-def model_seconds(F, bm, bn, r, rounds, K):
-    return rounds * (bm * bn * K * F["c"] / F["rate"][str(r)] + F["f"])
+def model_seconds(F, data, r, bm, bn, tiles, K):
+    """Modelled time of `tiles` tiles of row r with K-deep products."""
+    cus = data["cus"]
+    return (_cdiv(tiles, cus) * bm * bn * K * F["c"] / F["rate"][str(r)] +
+            _cdiv(tiles, cus * _occupancy(data, r)) * F["f"])
 
 
 def model_pick(data, F, M, N, K, E=0):
     best, best_t = None, None
     for (r, bm, bn) in _model_rows(data):
         tiles = grouped_tiles(M, E, N, bm, bn) if E else _cdiv(M, bm) * _cdiv(N, bn)
-        t = model_seconds(F, bm, bn, r, _cdiv(tiles, data["cus"]), K)
+        t = model_seconds(F, data, r, bm, bn, tiles, K)
         if best_t is None or t < best_t:
             best, best_t = r, t
     return best
@@ -635,7 +655,12 @@ def summarize(data):
         b = min(ms, key=lambda r: ms[r])
         bbest.append({"batch": rec["batch"], "M": rec["M"], "N": rec["N"], "K": rec["K"], "dtype": rec["dtype"],
                       "best_row": b, "best_ms": ms[b]})
+    sbest = []
+    for rec in data.get("splitk", []):
+        ms = {int(s): float(t) for s, t in rec["ms"].items()}
+        sbest.append({"M": rec["M"], "N": rec["N"], "K": rec["K"], "splits": min(ms, key=lambda s: ms[s])})
     return {"fit": F, "rows": nrows, "dense_best": best, "grouped_best": gbest, "batched_best": bbest,
+            "splitk_best": sbest,
             "model_agrees": "%d of %d dense shapes" % (agree, len(best)),
             "model_time_lost_max": round(max(lost), 4), "model_time_lost_median": round(statistics.median(lost), 4),
             "packed_ratio": packed_ratio(data), "copy_bytes_per_s": copy_rate(data),
@@ -653,8 +678,7 @@ def splitk_fit(data, F):
                 continue
             extra_bytes = 2.0 * s * rec["M"] * rec["N"] * 4
             # kernel part from the model with the row split-K picks (the model's best of rows 0-2)
-            tk = min(model_seconds(F, bm, bn, r, _cdiv(_cdiv(rec["M"], bm) * _cdiv(rec["N"], bn) * s, data["cus"]),
-                                   rec["K"] / s)
+            tk = min(model_seconds(F, data, r, bm, bn, _cdiv(rec["M"], bm) * _cdiv(rec["N"], bn) * s, rec["K"] / s)
                      for (r, bm, bn) in _model_rows(data) if r in (0, 1, 2))
             extra = float(t) * 1e-3 - tk
             if extra > 0:
@@ -669,8 +693,9 @@ def header_text(data, json_rel):
     lines = [
         "// Generated by `python -m tiled_matrix_multiplication_gemm_amd.sweep fit` from %s" % json_rel,
         "// (timings of every table row on MI355X); do not edit by hand.  The time",
-        "// model of select_config(): t = rounds * (BM * BN * K * kSecPerElemK / rate + kFixedSec),",
-        "// rounds = ceil(tiles / 256); exact shapes of the sweep return their measured best row.",
+        "// model of select_config(): t = ceil(tiles / 256) * BM * BN * K * kSecPerElemK / rate",
+        "// + ceil(tiles / (256 * occ)) * kFixedSec, occ = workgroups per CU; exact shapes of the",
+        "// sweep return their measured best row.",
         "#pragma once",
         "",
         "#include <stdint.h>",
@@ -680,15 +705,16 @@ def header_text(data, json_rel):
         "",
         "struct RowRate {",
         "    int id, bm, bn;",
+        "    int occ;      // workgroups one CU runs at once",
         "    double rate;  // per-CU output rate relative to row %d" % rows[0][0],
         "};",
         "inline constexpr RowRate kRows[] = {",
     ]
     for (r, bm, bn) in rows:
-        lines.append("    {%d, %d, %d, %.4f}," % (r, bm, bn, F["rate"][str(r)]))
+        lines.append("    {%d, %d, %d, %d, %.4f}," % (r, bm, bn, _occupancy(data, r), F["rate"][str(r)]))
     lines += ["};",
               "inline constexpr double kSecPerElemK = %.6e;  // one output element times one k, rate 1" % F["c"],
-              "inline constexpr double kFixedSec = %.6e;     // per tile: fill, drain, epilogue" % F["f"],
+              "inline constexpr double kFixedSec = %.6e;     // per round of tiles: fill, drain, epilogue" % F["f"],
               "inline constexpr double kCopyBytesPerSec = %.6e;  // the blocking copy of A" % S["copy_bytes_per_s"],
               "inline constexpr double kPartialBytesPerSec = %.6e;  // split-K partials, written and read" %
               S["splitk"]["partial_bytes_per_s"],
@@ -710,6 +736,15 @@ def header_text(data, json_rel):
         lines.append("    {%d, %d, %d, %d, 1, %d}," % (b["T"], b["N"], b["K"], b["E"], b["best_row"]))
     for b in S["batched_best"]:
         lines.append("    {%d, %d, %d, 0, %d, %d}," % (b["M"], b["N"], b["K"], b["batch"], b["best_row"]))
+    lines += ["};", "",
+              "struct SweptSplit {",
+              "    int64_t M, N, K;",
+              "    int32_t splits;",
+              "};",
+              "// the measured best split count of every shape the sweep timed split (cached top-1)",
+              "inline constexpr SweptSplit kSweptSplit[] = {"]
+    for b in S["splitk_best"]:
+        lines.append("    {%d, %d, %d, %d}," % (b["M"], b["N"], b["K"], b["splits"]))
     lines += ["};", "", "}  // namespace rates", "}  // namespace mg", ""]
     return "\n".join(lines)
 
