@@ -127,6 +127,25 @@ def test_small_ragged_shapes_every_config(orc, cfg, dtype):
                 assert mg.mg_last_kernel() == expect, (cfg, M, N, K, mg.mg_last_kernel())
 
 
+# Rows whose rings fit two workgroups in a CU's LDS, forced on ragged shapes
+# of more than two tiles per CU, so that every CU runs two of them at once
+# (the small shapes above leave most CUs with one).
+TWO_PER_CU = [(1, 4096, 4104, 136, F16, True), (2, 2050, 2040, 264, BF16, False),
+              (4, 4100, 4100, 96, BF16, True), (9, 131080, 72, 200, F16, False)]
+
+
+@pytest.mark.parametrize("cfg,M,N,K,dtype,epi", TWO_PER_CU)
+def test_rows_with_two_workgroups_per_cu(orc, cfg, M, N, K, dtype, epi):
+    import torch
+
+    tiles = -(-M // mg.mg_config_info(cfg)["bm"]) * -(-N // mg.mg_config_info(cfg)["bn"])
+    assert tiles > 2 * 256
+    c = inputs.integer_dense(M, N, K, dtype, 7100 + cfg, epilogue=epi, name="two_per_cu")
+    check_full(orc, c, cfg)
+    assert mg.mg_last_config() == cfg and mg.mg_last_kernel() == "gemm_dlds_kernel"
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("pads", [(8, 0, 0), (0, 16, 0), (0, 0, 8), (24, 8, 40)])
 def test_leading_strides_larger_than_rows(orc, pads):
     c = inputs.integer_dense(130, 70, 90, F16, 77, epilogue=True, name="strided")
