@@ -77,10 +77,11 @@ DENSE_SHAPES = [
     (12544, 256, 2304, F16), (256, 16384, 4096, F16), (128, 4096, 16384, BF16),  # tall-skinny and wide
     (256, 256, 65536, BF16), (512, 512, 32768, BF16), (1024, 1024, 16384, F16),  # large K
     (4096, 4096, 4100, F16), (8192, 8190, 8192, BF16), (1000, 1000, 1000, F16), (3000, 5000, 4096, BF16),
+    (4096, 11008, 4096, BF16), (4096, 4096, 11008, BF16), (512, 4096, 4096, BF16),  # MLP projections
 ]
 # (E, T, N, K, dtype): grouped problems, balanced routing drawn like the MoE workload
 GROUPED_SHAPES = [(32, 8192, 4096, 1024, F16), (8, 2048, 1024, 1024, F16), (64, 16384, 1408, 2048, BF16),
-                  (16, 4096, 2048, 512, F16)]
+                  (16, 4096, 2048, 512, F16), (8, 8192, 14336, 4096, BF16)]
 # (heads, Lq, Lk, d, dtype): attention-score products Q K^T, one batched
 # launch over the heads (B given transposed)
 BATCHED_SHAPES = [(128, 2048, 2048, 128, BF16), (256, 1024, 1024, 64, F16), (64, 4096, 4096, 128, BF16),
