@@ -11,6 +11,7 @@ the split-K count and the layout planner's decision follow the same model.
 import json
 import math
 import os
+import re
 
 import pytest
 
@@ -38,6 +39,20 @@ def L():
 def test_header_is_generated_from_the_json(data):
     with open(sweep.HEADER) as f:
         assert f.read() == sweep.header_text(data, os.path.relpath(sweep.DEFAULT_JSON, sweep.ROOT))
+
+
+def test_occupancy_follows_the_lds_ring(data):
+    """The model counts two workgroups per CU for exactly the rows whose
+    direct-to-LDS ring fits in half of a CU's 160 KB, and the generated
+    header carries the same counts."""
+    occ = {r: sweep._occupancy(data, r) for r, _, _ in sweep._model_rows(data)}
+    for r, o in occ.items():
+        lds = int(data["rows"][str(r)]["direct_lds_bytes"])
+        assert o == (2 if 2 * lds <= 160 * 1024 else 1), (r, lds, o)
+    assert {r for r, o in occ.items() if o == 2} == {1, 2, 4, 9}
+    text = open(os.path.join(ROOT, "tiled_matrix_multiplication_gemm_amd", "csrc", "mg_rates.h")).read()
+    for r, o in occ.items():
+        assert re.search(r"\{%d, \d+, \d+, %d, [0-9.]+\}," % (r, o), text), (r, o)
 
 
 def test_every_swept_shape_takes_its_measured_best_row(data, L):
