@@ -122,7 +122,7 @@ CONV_CASES = [
     # (Nb, H, W, C, OC, KH, KW, stride, pad, dil, dtype, weights)
     (2, 17, 17, 64, 64, 3, 3, (1, 1), (1, 1), (1, 1), F16, "hwio"),     # K = 576: direct GEMM rows
     (1, 20, 18, 32, 128, 3, 3, (2, 2), (1, 1), (1, 1), BF16, "hwio"),
-    (2, 15, 15, 3, 64, 7, 7, (2, 2), (3, 3), (1, 1), F16, "hwio"),      # K = 147: general GEMM row
+    (2, 15, 15, 3, 64, 7, 7, (2, 2), (3, 3), (1, 1), F16, "hwio"),      # C = 3 < one slice: im2col, then a K tail
     (2, 9, 9, 64, 32, 1, 1, (1, 1), (0, 0), (1, 1), F16, "hwio"),       # 1x1: the input is A
     (1, 12, 12, 16, 32, 1, 1, (2, 2), (0, 0), (1, 1), BF16, "hwio"),    # 1x1 stride 2: im2col
     (1, 14, 13, 16, 16, 3, 3, (1, 1), (2, 2), (2, 2), F16, "hwio"),     # dilation

@@ -88,8 +88,8 @@ def assert_higham(got, ref, absdot, case):
     assert ratio <= 1.0, "%s: error exceeds the fp32 summation bound (max ratio %.3g)" % (case.name, ratio)
 
 
-# general-kernel shapes (K % 64 != 0 or N % 8 != 0) and direct-to-LDS shapes
-# (K % 64 == 0, N % 8 == 0) with ragged M and N edges
+# shapes with K and N tails (K % 64 != 0 or N % 8 != 0) and shapes of whole
+# slices (K % 64 == 0, N % 8 == 0), with ragged M and N edges
 SMALL = [(1, 1, 1), (7, 33, 129), (33, 7, 1000), (129, 129, 33), (65, 200, 72),
          (300, 257, 130), (1000, 7, 33), (256, 384, 200), (513, 129, 257),
          (64, 64, 64), (1, 8, 64), (65, 200, 128), (129, 136, 64), (300, 264, 192), (513, 520, 256),
@@ -631,8 +631,8 @@ def test_grouped_skewed_counts_full(orc, dtype, K):
 @pytest.mark.parametrize("K", [128, 72])
 def test_grouped_many_experts(orc, E, K):
     # below 64 experts the kernels read the offsets from lanes of one vector
-    # load, from 64 on one by one from memory: both walks, on the fast (K =
-    # 128) and the general (K = 72) kernel, with empty and ragged experts
+    # load, from 64 on one by one from memory: both walks, on whole K slices
+    # (K = 128) and with a K tail (K = 72), with empty and ragged experts
     rng = np.random.default_rng(E)
     counts = rng.integers(0, 40, size=E)
     counts[::7] = 0

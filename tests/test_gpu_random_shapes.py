@@ -8,12 +8,18 @@ log-uniformly (M up to 2^17, N up to 2^14, K up to about 5800), within
 bounds that keep each case to a few seconds of oracle time, and about half
 the cases are integer-valued (bit-exact gate), the rest random floats
 (1e-2 gate plus Higham's bound).  Every output element is compared.
+
+Grouped launches get the same treatment: 1 to about 160 experts, up to
+about 23000 tokens split by a Dirichlet-multinomial draw (concentration
+0.2, 1 or 20: from a few experts holding almost every token, with many
+empty ones, to near-equal counts), N and K log-uniform.
 """
 import numpy as np
 import pytest
 
 import tiled_matrix_multiplication_gemm_amd as mg
 from tiled_matrix_multiplication_gemm_amd import inputs
+from tests.gpu_util import Guarded, announce, assert_bitexact, assert_tolerance, to_dev
 from tests.test_gpu_parity import check_full
 
 SEED = 3
@@ -71,3 +77,75 @@ def test_random_shape_auto_row(orc, _gpu, case):
         c = inputs.random_dense(M, N, K, dtype, seed, epilogue=epi, name="random")
     check_full(orc, c)
     assert mg.mg_last_kernel() == "gemm_dlds_kernel", (M, N, K, mg.mg_last_kernel())
+
+
+GROUPED_SEED = 7
+GROUPED_COUNT = 24
+
+
+def draw_grouped_cases(seed=GROUPED_SEED, count=GROUPED_COUNT):
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < count:
+        E = int(np.exp2(rng.uniform(0, 7.3)))
+        T = int(np.exp2(rng.uniform(0, 14.5)))
+        N = int(np.exp2(rng.uniform(3, 12.5)))
+        K = int(np.exp2(rng.uniform(3, 11.5)))
+        if T * N * K > 4e9 or E * K * N > 3e7 or T * K > 2e7 or T * N > 3e7:
+            continue
+        alpha = float(rng.choice([0.2, 1.0, 20.0]))
+        counts = rng.multinomial(T, rng.dirichlet([alpha] * E))
+        dtype = int(rng.integers(0, 2))
+        integer = bool(rng.integers(0, 2))
+        cases.append((E, T, N, K, tuple(int(c) for c in counts), dtype, integer, int(rng.integers(0, 2**31))))
+    return cases
+
+
+GROUPED_CASES = draw_grouped_cases()
+
+
+def test_grouped_draws_spread_over_rows_and_counts():
+    """Several rows; count vectors with empty experts and with experts of more
+    than one 256-row tile; and launches of 64 or more experts."""
+    rows = {mg.mg_select_config(T, N, K, dt, E) for E, T, N, K, _, dt, *_ in GROUPED_CASES}
+    assert len(rows) >= 4 and rows <= {0, 1, 2, 3, 4, 6, 8, 9}, sorted(rows)
+    assert any(0 in g[4] for g in GROUPED_CASES)
+    assert any(g[0] >= 64 for g in GROUPED_CASES)  # offsets walked from memory, not from lanes
+    assert any(max(g[4]) > 256 for g in GROUPED_CASES)
+
+
+def run_grouped_padded(c):
+    """The grouped launch with X rows, W rows and Y rows padded to multiples
+    of 8 elements (the library's stride rule), the padding of Y guarded."""
+    import torch
+
+    up8 = lambda n: (n + 7) // 8 * 8
+    xp = np.zeros((c.T, up8(c.K)), dtype=np.uint16)
+    xp[:, :c.K] = c.X
+    wp = np.zeros((c.E, c.K, up8(c.N)), dtype=np.uint16)
+    wp[:, :, :c.N] = c.W
+    X = to_dev(xp, c.dtype)[:, :c.K]
+    W = to_dev(wp, c.dtype)[:, :, :c.N]
+    off = torch.from_numpy(c.offsets.astype(np.int32)).cuda()
+    out = Guarded(c.T, c.N, c.dtype, ld=up8(c.N))
+    mg.mg_grouped_gemm(X, W, off, out=out.mat)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", GROUPED_CASES, ids=lambda c: "E%d_T%d_%dx%d_%s_%s" % (
+    c[0], c[1], c[2], c[3], "bf16" if c[5] else "f16", "int" if c[6] else "float"))
+def test_random_grouped_auto_row(orc, _gpu, case):
+    E, T, N, K, counts, dtype, integer, seed = case
+    c = inputs.random_grouped(E=E, T=T, K=K, N=N, dtype=dtype, seed=seed, counts=np.array(counts), integer=integer,
+                              name="random grouped")
+    announce("grouped E=%d T=%d N=%d K=%d dt=%d int=%s max count %d" % (E, T, N, K, dtype, integer, max(counts)))
+    out = run_grouped_padded(c)
+    assert out.guards_intact(), "write outside the output"
+    ref, ref_q = orc.grouped_gemm(c.X, c.W, c.offsets, dtype)
+    if integer:
+        assert_bitexact(out.result(), ref_q, dtype, c.name)
+    else:
+        assert_tolerance(out.result(), ref, dtype, c.name)
+    assert mg.mg_last_kernel() == "gemm_dlds_kernel", (E, T, N, K, mg.mg_last_kernel())
