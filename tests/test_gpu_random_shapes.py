@@ -12,7 +12,9 @@ the cases are integer-valued (bit-exact gate), the rest random floats
 Grouped launches get the same treatment: 1 to about 160 experts, up to
 about 23000 tokens split by a Dirichlet-multinomial draw (concentration
 0.2, 1 or 20: from a few experts holding almost every token, with many
-empty ones, to near-equal counts), N and K log-uniform.
+empty ones, to near-equal counts), N and K log-uniform.  Split-K takes the
+library's own split count and workspace, and batched products share A or B
+across entries (batch stride 0) in some of the cases.
 """
 import numpy as np
 import pytest
@@ -149,3 +151,128 @@ def test_random_grouped_auto_row(orc, _gpu, case):
     else:
         assert_tolerance(out.result(), ref, dtype, c.name)
     assert mg.mg_last_kernel() == "gemm_dlds_kernel", (E, T, N, K, mg.mg_last_kernel())
+
+
+# ---- split-K with the library's split count, and batched products ----------------
+SPLITK_SEED = 5
+SPLITK_COUNT = 16
+
+
+def draw_splitk_cases(seed=SPLITK_SEED, count=SPLITK_COUNT):
+    """Under-filled outputs over long K: M and N of 16 to 2048 (N a multiple
+    of 8, as split-K requires), K of 512 to 32768."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < count:
+        M = int(np.exp2(rng.uniform(4, 11)))
+        N = int(np.exp2(rng.uniform(4, 11))) // 8 * 8
+        K = int(np.exp2(rng.uniform(9, 15)))
+        if M * N * K > 3e9 or M * K > 2e7 or K * N > 2e7:
+            continue
+        cases.append((M, N, K, int(rng.integers(0, 2)), bool(rng.integers(0, 2)), int(rng.integers(0, 2**31))))
+    return cases
+
+
+SPLITK_CASES = draw_splitk_cases()
+
+
+def test_splitk_draws_take_several_split_counts():
+    splits = {mg.mg_splitk_choose(M, N, K) for M, N, K, *_ in SPLITK_CASES}
+    assert len(splits) >= 3 and max(splits) > 1, sorted(splits)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", SPLITK_CASES, ids=lambda c: "%dx%dx%d_%s_%s" % (
+    c[0], c[1], c[2], "bf16" if c[3] else "f16", "int" if c[4] else "float"))
+def test_random_splitk_chosen_splits(orc, _gpu, case):
+    import torch
+
+    M, N, K, dtype, integer, seed = case
+    gen = inputs.integer_dense if integer else inputs.random_dense
+    c = gen(M, N, K, dtype, seed, name="random splitk")
+    splits = mg.mg_splitk_choose(M, N, K)
+    announce("splitk %dx%dx%d dt=%d int=%s splits=%d" % (M, N, K, dtype, integer, splits))
+    up8 = lambda n: (n + 7) // 8 * 8
+    ap = np.zeros((M, up8(K)), dtype=np.uint16)
+    ap[:, :K] = c.A
+    A = to_dev(ap, dtype)[:, :K]
+    B = to_dev(c.B, dtype)
+    out = Guarded(M, N, dtype)
+    mg.mg_gemm_splitk(A, B, out=out.mat)  # split count and workspace chosen by the library
+    torch.cuda.synchronize()
+    assert out.guards_intact(), "write outside the output"
+    ref, ref_q = orc.gemm(c.A, c.B, dtype)
+    if integer:
+        assert_bitexact(out.result(), ref_q, dtype, c.name)
+    else:
+        assert_tolerance(out.result(), ref, dtype, c.name)
+
+
+BATCHED_SEED = 9
+BATCHED_COUNT = 16
+
+
+def draw_batched_cases(seed=BATCHED_SEED, count=BATCHED_COUNT):
+    """1 to 128 entries of 64 to 2048 rows and columns over K of 32 to 512
+    (the shapes of attention scores and of small per-head products), with A
+    or B shared by every entry (batch stride 0) in about a third of the
+    cases each."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < count:
+        nb = int(np.exp2(rng.uniform(0, 7)))
+        M, N = (int(np.exp2(rng.uniform(6, 11))) for _ in range(2))
+        K = int(np.exp2(rng.uniform(5, 9)))
+        if nb * M * N * K > 3e9 or nb * (M * K + K * N + M * N) > 3e7:
+            continue
+        share = str(rng.choice(["none", "a", "b"]))
+        cases.append((nb, M, N, K, share, int(rng.integers(0, 2)), bool(rng.integers(0, 2)),
+                      int(rng.integers(0, 2**31))))
+    return cases
+
+
+BATCHED_CASES = draw_batched_cases()
+
+
+def test_batched_draws_spread_over_rows():
+    rows = {mg.mg_select_config(M, N, K, dt, 0, nb) for nb, M, N, K, _, dt, *_ in BATCHED_CASES}
+    assert len(rows) >= 3 and rows <= {0, 1, 2, 3, 4, 6, 8, 9}, sorted(rows)
+    assert {c[4] for c in BATCHED_CASES} == {"none", "a", "b"}
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", BATCHED_CASES, ids=lambda c: "b%d_%dx%dx%d_share%s_%s_%s" % (
+    c[0], c[1], c[2], c[3], c[4], "bf16" if c[5] else "f16", "int" if c[6] else "float"))
+def test_random_batched_auto_row(orc, _gpu, case):
+    import torch
+
+    nb, M, N, K, share, dtype, integer, seed = case
+    gen = inputs.integer_dense if integer else inputs.random_dense
+    entries = [gen(M, N, K, dtype, seed + b, name="random batched") for b in range(nb)]
+    # a shared operand is entry 0's
+    A_bits = [entries[0].A if share == "a" else e.A for e in entries]
+    B_bits = [entries[0].B if share == "b" else e.B for e in entries]
+    announce("batched b=%d %dx%dx%d share=%s dt=%d int=%s" % (nb, M, N, K, share, dtype, integer))
+    up8 = lambda n: (n + 7) // 8 * 8
+
+    def stack(bits, rows, cols, one):
+        n = 1 if one else nb
+        buf = np.zeros((n, rows, up8(cols)), dtype=np.uint16)
+        for i in range(n):
+            buf[i, :, :cols] = bits[i]
+        t = to_dev(buf, dtype)[:, :, :cols]
+        return t.expand(nb, -1, -1) if one else t
+
+    A = stack(A_bits, M, K, share == "a")
+    B = stack(B_bits, K, N, share == "b")
+    out = Guarded(nb * M, N, dtype, ld=up8(N))
+    mg.mg_gemm_batched(A, B, out=out.mat.view(nb, M, N))
+    torch.cuda.synchronize()
+    assert out.guards_intact(), "write outside the output"
+    got = out.result().reshape(nb, M, N)
+    for b in range(nb):
+        ref, ref_q = orc.gemm(A_bits[b], B_bits[b], dtype)
+        if integer:
+            assert_bitexact(got[b], ref_q, dtype, "batched entry %d" % b)
+        else:
+            assert_tolerance(got[b], ref, dtype, "batched entry %d" % b)
