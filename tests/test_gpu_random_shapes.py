@@ -13,8 +13,9 @@ Grouped launches get the same treatment: 1 to about 160 experts, up to
 about 23000 tokens split by a Dirichlet-multinomial draw (concentration
 0.2, 1 or 20: from a few experts holding almost every token, with many
 empty ones, to near-equal counts), N and K log-uniform.  Split-K takes the
-library's own split count and workspace, and batched products share A or B
-across entries (batch stride 0) in some of the cases.
+library's own split count and workspace, batched products share A or B
+across entries (batch stride 0) in some of the cases, and convolutions
+reach each of the three ways the library runs one.
 """
 import numpy as np
 import pytest
@@ -276,3 +277,86 @@ def test_random_batched_auto_row(orc, _gpu, case):
             assert_bitexact(got[b], ref_q, dtype, "batched entry %d" % b)
         else:
             assert_tolerance(got[b], ref, dtype, "batched entry %d" % b)
+
+
+# ---- convolutions --------------------------------------------------------------
+CONV_SEED = 2
+CONV_COUNT = 20
+F32 = 2
+
+
+def draw_conv_cases(seed=CONV_SEED, count=CONV_COUNT):
+    """NHWC convolutions with kernels of 1 to 7 taps a side, strides 1 to 3,
+    padding 0 to 3 and dilation 1 or 2; in_channels a multiple of 64 in about
+    half the cases (the implicit GEMM), any count otherwise (im2col, or the
+    input itself for an unstrided, unpadded 1x1 kernel); HWIO or OHWI
+    weights; fp16, bf16 and, now and then, fp32 (with K = KH KW C a multiple
+    of 16, which the fp32 GEMM requires)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < count:
+        Nb = int(rng.integers(1, 5))
+        H, W = (int(rng.integers(1, 41)) for _ in range(2))
+        C = int(rng.choice([64, 128, 192])) if rng.integers(0, 2) else int(rng.integers(1, 97))
+        KH, KW = (int(rng.integers(1, 8)) for _ in range(2))
+        if rng.integers(0, 4) == 0:
+            KH = KW = 1
+        stride = tuple(int(v) for v in rng.integers(1, 4, size=2))
+        pad = tuple(int(v) for v in rng.integers(0, 4, size=2))
+        dil = tuple(int(v) for v in rng.integers(1, 3, size=2))
+        if rng.integers(0, 4) == 0:
+            stride, pad, dil = (1, 1), (0, 0), (1, 1)
+        dt = F32 if rng.integers(0, 6) == 0 else int(rng.integers(0, 2))
+        OC = int(rng.integers(1, 33)) * (4 if dt == F32 else 8)
+        oh = (H + 2 * pad[0] - dil[0] * (KH - 1) - 1) // stride[0] + 1
+        ow = (W + 2 * pad[1] - dil[1] * (KW - 1) - 1) // stride[1] + 1
+        if oh < 1 or ow < 1 or Nb * oh * ow * OC * KH * KW * C > 5e8:
+            continue
+        K = KH * KW * C
+        if dt == F32 and K % 16 != 0:  # the fp32 GEMM takes whole 16-element K slices
+            continue
+        weights = "ohwi" if dt != F32 and K % 8 == 0 and rng.integers(0, 3) == 0 else "hwio"
+        cases.append((Nb, H, W, C, OC, KH, KW, stride, pad, dil, dt, weights, bool(rng.integers(0, 2)),
+                      bool(rng.integers(0, 2)), int(rng.integers(0, 2**31))))
+    return cases
+
+
+CONV_CASES = draw_conv_cases()
+
+
+def conv_path(case):
+    Nb, H, W, C, OC, KH, KW, stride, pad, dil, dt, *_ = case
+    s = mg.Conv2dShape(Nb, H, W, C, OC, KH, KW, stride[0], stride[1], pad[0], pad[1], dil[0], dil[1])
+    if mg.mg_conv2d_workspace_bytes(s, dt) > 0:
+        return "im2col"
+    return "input" if KH == KW == 1 and stride == (1, 1) and pad == (0, 0) else "implicit"
+
+
+def test_conv_draws_reach_every_path():
+    paths = {conv_path(c) for c in CONV_CASES}
+    assert paths == {"im2col", "input", "implicit"}, paths
+    assert {c[11] for c in CONV_CASES} == {"hwio", "ohwi"}
+    assert F32 in {c[10] for c in CONV_CASES}
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", CONV_CASES, ids=lambda c: "n%d_%dx%dx%d_oc%d_k%dx%d_s%d%d_p%d%d_d%d%d_%s_%s%s%s" % (
+    c[0], c[1], c[2], c[3], c[4], c[5], c[6], *c[7], *c[8], *c[9], ("f16", "bf16", "f32")[c[10]], c[11],
+    "_int" if c[12] else "", "_bias" if c[13] else ""))
+def test_random_conv2d(orc, _gpu, case):
+    from tests.test_gpu_consumers import check, run_conv
+
+    Nb, H, W, C, OC, KH, KW, stride, pad, dil, dt, weights, integer, with_bias, seed = case
+    label = "random conv %s (%s)" % (case, conv_path(case))
+    announce(label)
+    c = inputs.conv_case(Nb, H, W, C, OC, KH, KW, dt, seed=seed, stride=stride, pad=pad, dil=dil, integer=integer,
+                         bias=with_bias)
+    got, guards = run_conv(c, OC, weights, c.bias)
+    assert guards, label + ": write outside the output"
+    ref, ref_q = orc.conv2d(c.x, c.w, dt, stride, pad, dil, bias=c.bias, relu=with_bias)
+    absref = None
+    if dt == F32 and not integer:
+        xa = np.abs(orc.decode32(c.x)).astype(np.float32).view(np.uint32)
+        wa = np.abs(orc.decode32(c.w)).astype(np.float32).view(np.uint32)
+        absref, _ = orc.conv2d(xa, wa, F32, stride, pad, dil)
+    check(got, ref, ref_q, dt, integer, label, absref, KH * KW * C)
