@@ -14,8 +14,10 @@ about 23000 tokens split by a Dirichlet-multinomial draw (concentration
 0.2, 1 or 20: from a few experts holding almost every token, with many
 empty ones, to near-equal counts), N and K log-uniform.  Split-K takes the
 library's own split count and workspace, batched products share A or B
-across entries (batch stride 0) in some of the cases, and convolutions
-reach each of the three ways the library runs one.
+across entries (batch stride 0) in some of the cases, convolutions reach
+each of the three ways the library runs one, dense products also take
+transposed operands, and attention scores span head counts, lengths and
+head dimensions.
 """
 import numpy as np
 import pytest
@@ -360,3 +362,106 @@ def test_random_conv2d(orc, _gpu, case):
         wa = np.abs(orc.decode32(c.w)).astype(np.float32).view(np.uint32)
         absref, _ = orc.conv2d(xa, wa, F32, stride, pad, dil)
     check(got, ref, ref_q, dt, integer, label, absref, KH * KW * C)
+
+
+# ---- transposed operands and attention scores ----------------------------------
+TRANSPOSED_SEED = 11
+TRANSPOSED_COUNT = 16
+
+
+def draw_transposed_cases(seed=TRANSPOSED_SEED, count=TRANSPOSED_COUNT):
+    """Dense shapes as above with A, B or both handed over as transposed views."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < count:
+        M = int(np.exp2(rng.uniform(4, 14)))
+        N = int(np.exp2(rng.uniform(4, 13)))
+        K = int(np.exp2(rng.uniform(5, 12)))
+        if M * N * K > 3e9 or M * N * K < 5e7 or M * K > 2e7 or K * N > 2e7:
+            continue
+        ta, tb = [(1, 0), (0, 1), (1, 1)][int(rng.integers(0, 3))]
+        cases.append((M, N, K, ta, tb, int(rng.integers(0, 2)), bool(rng.integers(0, 2)), bool(rng.integers(0, 2)),
+                      int(rng.integers(0, 2**31))))
+    return cases
+
+
+TRANSPOSED_CASES = draw_transposed_cases()
+
+
+def test_transposed_draws_spread_over_rows_and_layouts():
+    rows = {mg.mg_select_config(M, N, K, dt) for M, N, K, _, _, dt, *_ in TRANSPOSED_CASES}
+    assert len(rows) >= 4 and rows <= {0, 1, 2, 3, 4, 6, 8, 9}, sorted(rows)
+    assert {(c[3], c[4]) for c in TRANSPOSED_CASES} == {(1, 0), (0, 1), (1, 1)}
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", TRANSPOSED_CASES, ids=lambda c: "%dx%dx%d_ta%d_tb%d_%s_%s%s" % (
+    c[0], c[1], c[2], c[3], c[4], "bf16" if c[5] else "f16", "int" if c[6] else "float", "_epi" if c[7] else ""))
+def test_random_transposed_auto_row(orc, _gpu, case):
+    import torch
+    from tests.test_gpu_parity import stored_row_major, stored_transposed
+
+    M, N, K, ta, tb, dtype, integer, epi, seed = case
+    gen = inputs.integer_dense if integer else inputs.random_dense
+    c = gen(M, N, K, dtype, seed, epilogue=epi, name="random transposed")
+    announce("transposed %dx%dx%d ta=%d tb=%d dt=%d int=%s epi=%s" % (M, N, K, ta, tb, dtype, integer, epi))
+    A = stored_transposed(c.A, dtype) if ta else stored_row_major(c.A, dtype)
+    B = stored_transposed(c.B, dtype) if tb else stored_row_major(c.B, dtype)
+    out = Guarded(M, N, dtype, ld=(N + 7) // 8 * 8)
+    if epi:
+        mg.mg_gemm_bias_relu(A, B, to_dev(c.bias, dtype), out=out.mat)
+    else:
+        mg.mg_gemm(A, B, out=out.mat)
+    torch.cuda.synchronize()
+    assert out.guards_intact(), "write outside the output"
+    ref, ref_q = orc.gemm(c.A, c.B, dtype, bias=c.bias, relu=c.relu)
+    if integer:
+        assert_bitexact(out.result(), ref_q, dtype, c.name)
+    else:
+        assert_tolerance(out.result(), ref, dtype, c.name)
+    assert mg.mg_last_kernel() == "gemm_dlds_kernel"
+
+
+ATTENTION_SEED = 4
+ATTENTION_COUNT = 12
+
+
+def draw_attention_cases(seed=ATTENTION_SEED, count=ATTENTION_COUNT):
+    """1 to 64 heads, query lengths of 4 to 2048, key lengths a multiple of 8
+    up to 2048 (the score rows' stride rule), head dimensions a multiple of 8
+    from 8 to 256."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < count:
+        H = int(np.exp2(rng.uniform(0, 6)))
+        Lq = int(np.exp2(rng.uniform(2, 11)))
+        Lk = max(8, int(np.exp2(rng.uniform(4, 11))) // 8 * 8)
+        d = 8 * int(rng.integers(1, 33))
+        if H * Lq * Lk * d > 3e9 or H * Lq * Lk > 3e7:
+            continue
+        cases.append((H, Lq, Lk, d, int(rng.integers(0, 2)), bool(rng.integers(0, 2)), int(rng.integers(0, 2**31))))
+    return cases
+
+
+ATTENTION_CASES = draw_attention_cases()
+
+
+def test_attention_draws_spread_over_rows():
+    rows = {mg.mg_select_config(Lq, Lk, d, dt, 0, H) for H, Lq, Lk, d, dt, *_ in ATTENTION_CASES}
+    assert len(rows) >= 3 and rows <= {0, 1, 2, 3, 4, 6, 8, 9}, sorted(rows)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", ATTENTION_CASES, ids=lambda c: "h%d_lq%d_lk%d_d%d_%s_%s" % (
+    c[0], c[1], c[2], c[3], "bf16" if c[4] else "f16", "int" if c[5] else "float"))
+def test_random_attention_scores(orc, _gpu, case):
+    from tests.test_gpu_consumers import check, run_attention
+
+    H, Lq, Lk, d, dtype, integer, seed = case
+    label = "random attention %s" % (case,)
+    announce(label)
+    a = inputs.attention_case(H, Lq, Lk, d, dtype, seed=seed, integer=integer)
+    got, guards = run_attention(a)
+    assert guards, label + ": write outside the output"
+    ref, ref_q = orc.attention_scores(a.Q, a.K, dtype)
+    check(got, ref, ref_q, dtype, integer, label)
